@@ -1,0 +1,276 @@
+// C ABI of epx (declared in include/epx.h): host-side validation, sizing and
+// kernel launches.  No call allocates, frees or synchronizes; every kernel
+// goes onto the caller's stream.
+#include <string.h>
+
+#include <mutex>
+
+#include "epx_device.h"
+
+namespace {
+
+using namespace epx;
+
+struct Shape {
+    int32_t T, H, E, S, K, Kp, A, C, shared, src, E_loc, G, NG;
+    int64_t R, min_rows, ws_bytes, tiles;
+    uint32_t flags;
+};
+
+bool misaligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) != 0; }
+
+// A buffer of `bytes` bytes must be present and aligned unless it is empty.
+bool bad_buffer(const void* p, int64_t bytes, uintptr_t align) {
+    if (bytes == 0) return false;
+    return p == nullptr || misaligned(p, align);
+}
+
+// Validate `c` and derive the sizes every call needs.
+int derive(const ep_cfg_t* c, Shape* d) {
+    if (c == nullptr) return EP_EINVAL;
+    if (c->num_tokens < 0 || c->hidden < 8 || c->hidden % 8 != 0) return EP_EINVAL;
+    if (c->num_experts < 1 || c->num_segments < 1 || c->num_experts % c->num_segments != 0) return EP_EINVAL;
+    if (c->top_k < 1 || c->top_k > c->num_experts) return EP_EINVAL;
+    if (c->align < 1 || c->align > (1 << 30) || c->seg_capacity < 0) return EP_EINVAL;
+    if (c->shared_expert != 0 && c->shared_expert != 1) return EP_EINVAL;
+    if (c->shared_expert && (c->src_segment < 0 || c->src_segment >= c->num_segments)) return EP_EINVAL;
+    if (c->reserved0 != 0 || c->reserved1 != 0) return EP_EINVAL;
+    if (c->flags & ~EP_ZERO_PAD_ROWS) return EP_EINVAL;
+    d->T = c->num_tokens;
+    d->H = c->hidden;
+    d->E = c->num_experts;
+    d->S = c->num_segments;
+    d->K = c->top_k;
+    d->shared = c->shared_expert;
+    d->Kp = d->K + d->shared;
+    d->A = c->align;
+    d->C = c->seg_capacity;
+    d->src = d->shared ? c->src_segment : 0;
+    d->E_loc = d->E / d->S;
+    d->G = d->E_loc + d->shared;
+    const int64_t ng = (int64_t)d->S * d->G;
+    if (ng > EP_MAX_GROUPS) return EP_EINVAL;
+    d->NG = (int32_t)ng;
+    const int64_t slots = (int64_t)d->T * d->Kp;
+    if (slots >= (int64_t(1) << 30)) return EP_EINVAL;  // look-back descriptors hold 30-bit counts
+    if (d->C > 0) {
+        d->min_rows = (int64_t)d->S * d->C;
+    } else {
+        const int64_t groups = (int64_t)d->E + d->shared;
+        d->min_rows = slots + (slots < groups ? slots : groups) * (int64_t)(d->A - 1);
+    }
+    if (d->min_rows >= (int64_t(1) << 31)) return EP_EINVAL;  // rows are int32
+    d->tiles = layout_tiles((int64_t)d->T * d->K);
+    d->ws_bytes = kWorkspaceHeader + d->tiles * (int64_t)d->NG * 4;
+    d->R = c->recv_rows;
+    d->flags = c->flags;
+    return EP_OK;
+}
+
+int check_rows(const Shape& d) {
+    if (d.R < d.min_rows || d.R >= (int64_t(1) << 31)) return EP_EINVAL;
+    return EP_OK;
+}
+
+// The current device must be a gfx950; the answer is cached per device.
+int check_device() {
+    static std::mutex mu;
+    static int verdict[64];  // 0 unknown, 1 ok, 2 not supported
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return EP_ELAUNCH;
+    if (dev < 0 || dev >= 64) return EP_ENOTSUP;
+    std::lock_guard<std::mutex> lock(mu);
+    if (verdict[dev] == 0) {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return EP_ELAUNCH;
+        verdict[dev] = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+    }
+    return verdict[dev] == 1 ? EP_OK : EP_ENOTSUP;
+}
+
+int status_of(hipError_t e) { return e == hipSuccess ? EP_OK : EP_ELAUNCH; }
+
+// Layout arrays read by the payload calls.
+int check_layout_for_payload(const Shape& d, const ep_layout_t* L) {
+    if (L == nullptr) return EP_EINVAL;
+    if (bad_buffer(L->token_row, (int64_t)d.T * d.Kp * 4, 4)) return EP_EINVAL;
+    if (d.flags & EP_ZERO_PAD_ROWS) {
+        if (bad_buffer(L->counts, (int64_t)d.NG * 4, 4) ||
+            bad_buffer(L->row_offsets, (int64_t)d.S * (d.G + 1) * 4, 4) ||
+            bad_buffer(L->seg_base, (int64_t)(d.S + 1) * 4, 4))
+            return EP_EINVAL;
+    }
+    return EP_OK;
+}
+
+MoveArgs move_args(const Shape& d, const ep_layout_t* L, const void* src, void* dst, const float* probs) {
+    MoveArgs m;
+    m.src = src;
+    m.dst = dst;
+    m.token_row = L->token_row;
+    m.probs = probs;
+    m.T = d.T;
+    m.K = d.K;
+    m.Kp = d.Kp;
+    m.H = d.H;
+    m.R = d.R;
+    return m;
+}
+
+int zero_pad(const Shape& d, const ep_layout_t* L, void* base, int64_t row_bytes, hipStream_t st) {
+    if (!(d.flags & EP_ZERO_PAD_ROWS) || d.A == 1) return EP_OK;
+    return status_of(launch_zero_pad_rows(base, row_bytes, *L, d.S, d.G, d.A, d.C, d.R, st));
+}
+
+}  // namespace
+
+extern "C" {
+
+int ep_abi_version(void) { return EPX_ABI_VERSION; }
+
+const char* ep_strerror(int status) {
+    switch (status) {
+        case EP_OK: return "ok";
+        case EP_EINVAL: return "invalid argument";
+        case EP_ELAUNCH: return "HIP runtime error while enqueueing work";
+        case EP_ENOTSUP: return "device is not gfx950 (MI355X)";
+        default: return "unknown status";
+    }
+}
+
+int ep_query(const ep_cfg_t* cfg, int64_t* min_recv_rows, int64_t* workspace_bytes, int32_t* groups_per_seg) {
+    Shape d;
+    const int rc = derive(cfg, &d);
+    if (rc != EP_OK) return rc;
+    if (min_recv_rows) *min_recv_rows = d.min_rows;
+    if (workspace_bytes) *workspace_bytes = d.ws_bytes;
+    if (groups_per_seg) *groups_per_seg = d.G;
+    return EP_OK;
+}
+
+int ep_dispatch_layout(const ep_cfg_t* cfg, const int32_t* topk_ids, void* workspace, int64_t workspace_bytes,
+                       const ep_layout_t* layout, void* stream) {
+    Shape d;
+    int rc = derive(cfg, &d);
+    if (rc != EP_OK) return rc;
+    if ((rc = check_rows(d)) != EP_OK) return rc;
+    if (layout == nullptr) return EP_EINVAL;
+    if (bad_buffer(topk_ids, (int64_t)d.T * d.K * 4, 4)) return EP_EINVAL;
+    if (workspace == nullptr || misaligned(workspace, 16) || workspace_bytes < d.ws_bytes) return EP_EINVAL;
+    const ep_layout_t* L = layout;
+    if (bad_buffer(L->counts, (int64_t)d.NG * 4, 4) || bad_buffer(L->seg_base, (int64_t)(d.S + 1) * 4, 4) ||
+        bad_buffer(L->row_offsets, (int64_t)d.S * (d.G + 1) * 4, 4) ||
+        bad_buffer(L->scales_offsets, (int64_t)d.S * (d.G + 1) * 4, 4) ||
+        bad_buffer(L->token_row, (int64_t)d.T * d.Kp * 4, 4) || bad_buffer(L->expert_ids, d.R * 4, 4) ||
+        bad_buffer(L->src_info, d.R * 8, 4) || bad_buffer(L->flags, 4, 4))
+        return EP_EINVAL;
+    if ((rc = check_device()) != EP_OK) return rc;
+
+    LayoutArgs a;
+    a.topk_ids = topk_ids;
+    a.ticket = static_cast<uint32_t*>(workspace);
+    a.desc = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(workspace) + kWorkspaceHeader);
+    a.out = *L;
+    a.T = d.T;
+    a.K = d.K;
+    a.Kp = d.Kp;
+    a.E = d.E;
+    a.S = d.S;
+    a.G = d.G;
+    a.NG = d.NG;
+    a.E_loc = d.E_loc;
+    a.A = d.A;
+    a.C = d.C;
+    a.shared = d.shared;
+    a.src_seg = d.src;
+    a.recv_rows = d.R;
+    a.tiles = (int32_t)d.tiles;
+    return status_of(launch_layout(a, static_cast<hipStream_t>(stream)));
+}
+
+int ep_dispatch(const ep_cfg_t* cfg, const ep_layout_t* layout, const uint16_t* x, uint16_t* recv, void* stream) {
+    Shape d;
+    int rc = derive(cfg, &d);
+    if (rc != EP_OK) return rc;
+    if ((rc = check_rows(d)) != EP_OK) return rc;
+    if ((rc = check_layout_for_payload(d, layout)) != EP_OK) return rc;
+    if (bad_buffer(x, (int64_t)d.T * d.H * 2, 16) || bad_buffer(recv, d.R * d.H * 2, 16)) return EP_EINVAL;
+    if ((rc = check_device()) != EP_OK) return rc;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if ((rc = status_of(launch_scatter(move_args(d, layout, x, recv, nullptr), st))) != EP_OK) return rc;
+    return zero_pad(d, layout, recv, (int64_t)d.H * 2, st);
+}
+
+int ep_dispatch_nvfp4(const ep_cfg_t* cfg, const ep_layout_t* layout, const uint16_t* x, uint8_t* codes,
+                      uint8_t* scales, uint16_t* rowscale, void* stream) {
+    Shape d;
+    int rc = derive(cfg, &d);
+    if (rc != EP_OK) return rc;
+    if ((rc = check_rows(d)) != EP_OK) return rc;
+    if (d.H % 16 != 0 || d.H > nvfp4_max_hidden()) return EP_EINVAL;
+    if ((rc = check_layout_for_payload(d, layout)) != EP_OK) return rc;
+    if (bad_buffer(x, (int64_t)d.T * d.H * 2, 16) || bad_buffer(codes, d.R * (d.H / 2), 16) ||
+        bad_buffer(scales, d.R * (d.H / 16), 1) || bad_buffer(rowscale, d.R * 2, 2))
+        return EP_EINVAL;
+    if ((rc = check_device()) != EP_OK) return rc;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    Nvfp4Args a;
+    a.x = x;
+    a.codes = codes;
+    a.scales = scales;
+    a.rowscale = rowscale;
+    a.token_row = layout->token_row;
+    a.T = d.T;
+    a.Kp = d.Kp;
+    a.H = d.H;
+    a.R = d.R;
+    if ((rc = status_of(launch_nvfp4(a, st))) != EP_OK) return rc;
+    if ((rc = zero_pad(d, layout, codes, d.H / 2, st)) != EP_OK) return rc;
+    if ((rc = zero_pad(d, layout, scales, d.H / 16, st)) != EP_OK) return rc;
+    return zero_pad(d, layout, rowscale, 2, st);
+}
+
+int ep_combine(const ep_cfg_t* cfg, const ep_layout_t* layout, const uint16_t* expert_out, const float* probs,
+               uint16_t* y, void* stream) {
+    Shape d;
+    int rc = derive(cfg, &d);
+    if (rc != EP_OK) return rc;
+    if ((rc = check_rows(d)) != EP_OK) return rc;
+    if (layout == nullptr || bad_buffer(layout->token_row, (int64_t)d.T * d.Kp * 4, 4)) return EP_EINVAL;
+    if (bad_buffer(expert_out, d.R * d.H * 2, 16) || bad_buffer(y, (int64_t)d.T * d.H * 2, 16)) return EP_EINVAL;
+    if (probs != nullptr && misaligned(probs, 4)) return EP_EINVAL;
+    if ((rc = check_device()) != EP_OK) return rc;
+    return status_of(launch_gather_reduce(move_args(d, layout, expert_out, y, probs), static_cast<hipStream_t>(stream)));
+}
+
+int ep_dispatch_bwd(const ep_cfg_t* cfg, const ep_layout_t* layout, const uint16_t* grad_recv, uint16_t* grad_x,
+                    void* stream) {
+    Shape d;
+    int rc = derive(cfg, &d);
+    if (rc != EP_OK) return rc;
+    if ((rc = check_rows(d)) != EP_OK) return rc;
+    if (layout == nullptr || bad_buffer(layout->token_row, (int64_t)d.T * d.Kp * 4, 4)) return EP_EINVAL;
+    if (bad_buffer(grad_recv, d.R * d.H * 2, 16) || bad_buffer(grad_x, (int64_t)d.T * d.H * 2, 16)) return EP_EINVAL;
+    if ((rc = check_device()) != EP_OK) return rc;
+    return status_of(launch_gather_reduce(move_args(d, layout, grad_recv, grad_x, nullptr), static_cast<hipStream_t>(stream)));
+}
+
+int ep_combine_bwd(const ep_cfg_t* cfg, const ep_layout_t* layout, const uint16_t* grad_y, const float* probs,
+                   uint16_t* grad_expert_out, void* stream) {
+    Shape d;
+    int rc = derive(cfg, &d);
+    if (rc != EP_OK) return rc;
+    if ((rc = check_rows(d)) != EP_OK) return rc;
+    if ((rc = check_layout_for_payload(d, layout)) != EP_OK) return rc;
+    if (bad_buffer(grad_y, (int64_t)d.T * d.H * 2, 16) || bad_buffer(grad_expert_out, d.R * d.H * 2, 16))
+        return EP_EINVAL;
+    if (probs != nullptr && misaligned(probs, 4)) return EP_EINVAL;
+    if ((rc = check_device()) != EP_OK) return rc;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const MoveArgs m = move_args(d, layout, grad_y, grad_expert_out, probs);
+    rc = status_of(probs != nullptr ? launch_scatter_scaled(m, st) : launch_scatter(m, st));
+    if (rc != EP_OK) return rc;
+    return zero_pad(d, layout, grad_expert_out, (int64_t)d.H * 2, st);
+}
+
+}  // extern "C"

@@ -1,0 +1,120 @@
+// Device-side helpers and kernel launchers shared by the epx HIP sources.
+// gfx950 (CDNA4) only: wave64, 64 KiB of LDS per workgroup used at most.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "epx.h"
+
+namespace epx {
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------------------
+// Layout pass geometry.
+// ---------------------------------------------------------------------------
+constexpr int kLayoutThreads = 256;                      // 4 waves
+constexpr int kLayoutWaves = kLayoutThreads / kWave;
+constexpr int kSlotsPerThread = 8;
+constexpr int kTileSlots = kLayoutThreads * kSlotsPerThread;  // routed slots per tile
+constexpr int kSlotsPerWave = kTileSlots / kLayoutWaves;      // contiguous per wave
+constexpr int kWorkspaceHeader = 256;                    // ticket + padding
+
+// Look-back descriptor: 2 status bits over a 30-bit count.
+constexpr uint32_t kDescAgg = 1u << 30;   // tile aggregate only
+constexpr uint32_t kDescInc = 2u << 30;   // inclusive prefix through this tile
+constexpr uint32_t kDescValue = (1u << 30) - 1;
+
+inline int64_t layout_tiles(int64_t routed_slots) {
+    int64_t nt = (routed_slots + kTileSlots - 1) / kTileSlots;
+    return nt < 1 ? 1 : nt;
+}
+
+// ---------------------------------------------------------------------------
+// Number helpers (bit-exact definitions, no fused multiply-add anywhere: the
+// library is built with -ffp-contract=off).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// float -> bf16 bits, round to nearest-even; NaN keeps sign and payload top
+// bits and is made quiet.
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (u >> 16) | 0x40u;
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+}
+
+// Count of set bits of `m` in lanes below this one (the in-wave rank).
+__device__ __forceinline__ uint32_t lanes_below(uint64_t m) {
+    return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                     __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
+// Lanes of the wave holding the same key as this lane.  Every lane of the
+// wave must be active; keys are < 2^nbits.
+__device__ __forceinline__ uint64_t match_any(uint32_t key, int nbits) {
+    uint64_t m = ~0ull;
+    for (int b = 0; b < nbits; ++b) {
+        const bool bit = (key >> b) & 1u;
+        const uint64_t on = __builtin_amdgcn_ballot_w64(bit);
+        m &= bit ? on : ~on;
+    }
+    return m;
+}
+
+template <typename T>
+__device__ __forceinline__ T uniform(T v) {
+    return __builtin_amdgcn_readfirstlane(v);
+}
+
+// ---------------------------------------------------------------------------
+// Launchers (defined in the .hip files).  All return a hipError_t of the
+// launch; shapes are validated by the caller (api.hip).
+// ---------------------------------------------------------------------------
+struct LayoutArgs {
+    const int32_t* topk_ids;
+    uint32_t* ticket;
+    uint32_t* desc;
+    ep_layout_t out;
+    int32_t T, K, Kp, E, S, G, NG, E_loc, A, C, shared, src_seg;
+    int64_t recv_rows;
+    int32_t tiles;
+};
+hipError_t launch_layout(const LayoutArgs& a, hipStream_t stream);
+
+struct MoveArgs {
+    const void* src;
+    void* dst;
+    const int32_t* token_row;
+    const float* probs;  // nullptr: weight 1
+    int32_t T, K, Kp, H;
+    int64_t R;           // receive rows; a token_row entry outside [0, R) is skipped
+};
+hipError_t launch_scatter(const MoveArgs& a, hipStream_t stream);         // dispatch: bit copy
+hipError_t launch_scatter_scaled(const MoveArgs& a, hipStream_t stream);  // combine-bwd: w_k * row
+hipError_t launch_gather_reduce(const MoveArgs& a, hipStream_t stream);   // combine / dispatch-bwd
+
+struct Nvfp4Args {
+    const uint16_t* x;
+    uint8_t* codes;
+    uint8_t* scales;
+    uint16_t* rowscale;
+    const int32_t* token_row;
+    int32_t T, Kp, H;
+    int64_t R;           // receive rows; a token_row entry outside [0, R) is skipped
+};
+hipError_t launch_nvfp4(const Nvfp4Args& a, hipStream_t stream);
+int nvfp4_max_hidden();
+
+// Zero the payload bytes of every pad row ([count, align_up(count)) of each
+// group, below capacity).  row_bytes = bytes of one row of `base`.
+hipError_t launch_zero_pad_rows(void* base, int64_t row_bytes, const ep_layout_t& L, int32_t S,
+                                int32_t G, int32_t A, int32_t C, int64_t R, hipStream_t stream);
+
+}  // namespace epx

@@ -1,0 +1,377 @@
+// Dispatch layout for one GPU's share of MoE expert-parallel dispatch:
+// per-group counts, aligned row offsets, stable in-group ranks, token_row,
+// expert_ids and src_info, plus the capacity-overflow flag.
+//
+// Semantics (page title, API item):
+//  - NeMo AutoModel token_dispatcher page: dispatch_postprocess counts the
+//    tokens per expert; _align_up / moe_router_expert_pad_multiple pad each
+//    expert's rows to a multiple; _assert_no_hybridep_overflow: truncation
+//    at capacity raises a one-element device overflow flag.
+//  - NeMo AutoModel fused_a2a page, HybridEPDispatch.forward: -1 marks an
+//    unused top-k slot; rows are grouped by local expert.
+//  - MAX DistributedEPDispatchBlockScaledNVDynGlobalScales page, execute:
+//    row_offsets, expert_ids per received token, src_info, atomic counters
+//    coordinating work across thread blocks.
+//
+// Three launches on the caller's stream:
+//  1. k_layout_clear  zero the counts (the shared group gets T), the flags
+//                     word, the tile ticket and the look-back descriptors.
+//  2. k_layout_hist   per tile of 2048 routed slots, a wave64 match-any over
+//                     the group key (one ballot per key bit); the lowest lane
+//                     of each match set adds the set's popcount into an LDS
+//                     counter, so a hot expert costs one LDS atomic per wave
+//                     instead of one per slot.  Tiles add their nonzero
+//                     counters into `counts`.
+//  3. k_layout_rank   single pass: every workgroup scans the aligned group
+//                     sizes (from the finished counts) into group start
+//                     rows, takes a tile from an atomic ticket (so it only
+//                     ever waits on tiles that already started), ranks its
+//                     slots inside their groups (per-wave running counters in
+//                     LDS + match-any), publishes its per-group aggregate,
+//                     then resolves its per-group prefix over earlier tiles
+//                     by decoupled look-back and writes token_row,
+//                     expert_ids and src_info.  Pad-row metadata and the
+//                     fused shared-expert rows are spread over the tiles.
+#include "epx_device.h"
+
+namespace epx {
+namespace {
+
+constexpr int kMaxSpins = 1 << 22;  // look-back gives up (EP_FLAG_INTERNAL) after this
+
+__device__ __forceinline__ int32_t align_up(int32_t count, int32_t multiple) {
+    return ((count + multiple - 1) / multiple) * multiple;
+}
+
+__global__ __launch_bounds__(256) void k_layout_clear(LayoutArgs a) {
+    const int64_t ndesc = (int64_t)a.tiles * a.NG;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    const int64_t i0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    for (int64_t i = i0; i < ndesc; i += stride) a.desc[i] = 0u;
+    const int32_t shared_group = a.shared ? a.src_seg * a.G : -1;
+    for (int64_t g = i0; g < a.NG; g += stride)
+        a.out.counts[g] = (g == shared_group) ? a.T : 0;
+    if (i0 == 0) {
+        a.out.flags[0] = 0;
+        a.ticket[0] = 0u;
+    }
+}
+
+__global__ __launch_bounds__(kLayoutThreads) void k_layout_hist(LayoutArgs a) {
+    __shared__ int32_t s_hist[EP_MAX_GROUPS];
+    __shared__ int32_t s_gof[EP_MAX_GROUPS];  // group of each routed expert
+    __shared__ int32_t s_bad;
+    const int tid = threadIdx.x;
+    for (int g = tid; g < a.NG; g += kLayoutThreads) s_hist[g] = 0;
+    for (int e = tid; e < a.E; e += kLayoutThreads)
+        s_gof[e] = (e / a.E_loc) * a.G + a.shared + (e % a.E_loc);
+    if (tid == 0) s_bad = 0;
+    __syncthreads();
+
+    const int64_t routed = (int64_t)a.T * a.K;
+    const int nbits = 32 - __clz(a.NG);  // keys live in [0, NG]; NG = "no group"
+    const int64_t base = (int64_t)blockIdx.x * kTileSlots;
+    bool bad = false;
+#pragma unroll
+    for (int it = 0; it < kSlotsPerThread; ++it) {
+        const int64_t f = base + it * kLayoutThreads + tid;
+        uint32_t key = (uint32_t)a.NG;
+        if (f < routed) {
+            const int32_t e = a.topk_ids[f];
+            if ((uint32_t)e < (uint32_t)a.E) key = (uint32_t)s_gof[e];
+            else if (e != -1) bad = true;
+        }
+        const uint64_t m = match_any(key, nbits);
+        if (key != (uint32_t)a.NG && lanes_below(m) == 0)
+            atomicAdd(&s_hist[key], (int32_t)__popcll(m));
+    }
+    if (bad) s_bad = 1;
+    __syncthreads();
+    for (int g = tid; g < a.NG; g += kLayoutThreads) {
+        const int32_t c = s_hist[g];
+        if (c) atomicAdd(&a.out.counts[g], c);
+    }
+    if (tid == 0 && s_bad) atomicOr(a.out.flags, EP_FLAG_BAD_ID);
+}
+
+__device__ __forceinline__ uint32_t desc_load(const uint32_t* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void desc_store(uint32_t* p, uint32_t v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__global__ __launch_bounds__(kLayoutThreads) void k_layout_rank(LayoutArgs a) {
+    __shared__ int32_t s_cnt[EP_MAX_GROUPS];    // group totals
+    __shared__ int32_t s_start[EP_MAX_GROUPS];  // first row of the group (clamped at capacity)
+    __shared__ int32_t s_lim[EP_MAX_GROUPS];    // first row past the segment's capacity
+    __shared__ int32_t s_pref[EP_MAX_GROUPS];   // slots of the group in earlier tiles
+    __shared__ int32_t s_gof[EP_MAX_GROUPS];    // group of each routed expert
+    __shared__ uint16_t s_wcnt[kLayoutWaves][EP_MAX_GROUPS];  // per-wave counts / prefixes
+    __shared__ int32_t s_wsum[kLayoutWaves];
+    __shared__ uint32_t s_tile;
+    __shared__ int32_t s_flag;
+
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), w = tid / kWave;
+    const int NG = a.NG, G = a.G;
+    if (tid == 0) {
+        s_tile = atomicAdd(a.ticket, 1u);
+        s_flag = 0;
+    }
+    for (int g = tid; g < NG; g += kLayoutThreads) s_cnt[g] = a.out.counts[g];
+    for (int e = tid; e < a.E; e += kLayoutThreads)
+        s_gof[e] = (e / a.E_loc) * G + a.shared + (e % a.E_loc);
+    for (int i = tid; i < kLayoutWaves * EP_MAX_GROUPS; i += kLayoutThreads)
+        (&s_wcnt[0][0])[i] = 0;
+    __syncthreads();
+    const uint32_t tile = s_tile;
+
+    // ---- aligned exclusive prefix P over all groups (segment-major) ----
+    // Thread i covers groups [8i, 8i + 8); NG <= 2048 = 256 * 8.
+    int32_t al[8];
+    int32_t tsum = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const int g = tid * 8 + j;
+        al[j] = g < NG ? align_up(s_cnt[g], a.A) : 0;
+        tsum += al[j];
+    }
+    int32_t incl = tsum;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+        const int32_t n = __shfl_up(incl, o, kWave);
+        if (lane >= o) incl += n;
+    }
+    if (lane == kWave - 1) s_wsum[w] = incl;
+    __syncthreads();
+    int32_t wbase = 0, total = 0;
+#pragma unroll
+    for (int w2 = 0; w2 < kLayoutWaves; ++w2) {
+        if (w2 < w) wbase += s_wsum[w2];
+        total += s_wsum[w2];
+    }
+    {
+        int32_t run = wbase + incl - tsum;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int g = tid * 8 + j;
+            if (g < NG) s_start[g] = run;
+            run += al[j];
+        }
+    }
+    __syncthreads();
+
+    // Offsets and segment bases (one tile writes them).
+    if (tile == 0) {
+        const int n = a.S * (G + 1);
+        for (int idx = tid; idx < n; idx += kLayoutThreads) {
+            const int s = idx / (G + 1), gl = idx - s * (G + 1);
+            const int gi = s * G + gl;
+            int32_t off = (gi < NG ? s_start[gi] : total) - s_start[s * G];
+            if (a.C > 0 && off > a.C) off = a.C;
+            a.out.row_offsets[idx] = off;
+            a.out.scales_offsets[idx] = off;
+        }
+        for (int s = tid; s <= a.S; s += kLayoutThreads)
+            a.out.seg_base[s] = a.C > 0 ? s * a.C : (s < a.S ? s_start[s * G] : total);
+    }
+    // P -> absolute first row (clamped at capacity) and capacity limit.
+    int32_t st[8], li[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const int g = tid * 8 + j;
+        st[j] = 0;
+        li[j] = 0;
+        if (g < NG) {
+            const int s = g / G;
+            const int32_t segp = s_start[s * G];
+            int32_t off = s_start[g] - segp;
+            if (a.C > 0) {
+                if (off > a.C) off = a.C;
+                st[j] = s * a.C + off;
+                li[j] = (s + 1) * a.C;
+            } else {
+                st[j] = segp + off;
+                li[j] = 0x7FFFFFFF;
+            }
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const int g = tid * 8 + j;
+        if (g < NG) {
+            s_start[g] = st[j];
+            s_lim[g] = li[j];
+        }
+    }
+
+    // ---- in-tile ranks: wave w owns slots [w*512, w*512 + 512) of the tile ----
+    const int64_t routed = (int64_t)a.T * a.K;
+    const int nbits = 32 - __clz(NG);
+    const int64_t wslot0 = (int64_t)tile * kTileSlots + (int64_t)w * kSlotsPerWave;
+    uint32_t key[kSlotsPerThread], rnk[kSlotsPerThread];
+    int32_t eid[kSlotsPerThread];
+#pragma unroll
+    for (int it = 0; it < kSlotsPerThread; ++it) {
+        const int64_t f = wslot0 + it * kWave + lane;
+        uint32_t k = (uint32_t)NG;
+        int32_t e = -1;
+        if (f < routed) {
+            e = a.topk_ids[f];
+            if ((uint32_t)e < (uint32_t)a.E) k = (uint32_t)s_gof[e];
+        }
+        const uint64_t m = match_any(k, nbits);
+        const uint32_t r = lanes_below(m);
+        rnk[it] = 0;
+        if (k != (uint32_t)NG) {
+            const uint32_t before = s_wcnt[w][k];
+            rnk[it] = before + r;
+            if (r == 0) s_wcnt[w][k] = (uint16_t)(before + (uint32_t)__popcll(m));
+        }
+        key[it] = k;
+        eid[it] = e;
+    }
+    __syncthreads();
+
+    // ---- per-wave exclusive prefixes and the tile aggregate per group ----
+    int32_t agg[EP_MAX_GROUPS / kLayoutThreads];
+    const int32_t shared_group = a.shared ? a.src_seg * G : -1;
+#pragma unroll
+    for (int j = 0; j < EP_MAX_GROUPS / kLayoutThreads; ++j) {
+        const int g = tid + j * kLayoutThreads;
+        agg[j] = 0;
+        if (g < NG) {
+            int32_t run = 0;
+#pragma unroll
+            for (int w2 = 0; w2 < kLayoutWaves; ++w2) {
+                const int32_t c = s_wcnt[w2][g];
+                s_wcnt[w2][g] = (uint16_t)run;
+                run += c;
+            }
+            agg[j] = run;
+            if (s_cnt[g] > 0 && g != shared_group)
+                desc_store(&a.desc[(int64_t)tile * NG + g], (tile == 0 ? kDescInc : kDescAgg) | (uint32_t)run);
+        }
+    }
+    // ---- decoupled look-back over earlier tiles ----
+    int32_t lost = 0;
+#pragma unroll
+    for (int j = 0; j < EP_MAX_GROUPS / kLayoutThreads; ++j) {
+        const int g = tid + j * kLayoutThreads;
+        if (g >= NG) continue;
+        uint32_t pref = 0;
+        if (tile > 0 && s_cnt[g] > 0 && g != shared_group) {
+            for (int64_t p = (int64_t)tile - 1; p >= 0; --p) {
+                const uint32_t* dp = &a.desc[p * NG + g];
+                uint32_t d = desc_load(dp);
+                int spins = 0;
+                while ((d & ~kDescValue) == 0u) {
+                    if (++spins > kMaxSpins) {
+                        lost = EP_FLAG_INTERNAL;
+                        d = kDescInc;
+                        break;
+                    }
+                    __builtin_amdgcn_s_sleep(1);
+                    d = desc_load(dp);
+                }
+                pref += d & kDescValue;
+                if (d & kDescInc) break;
+            }
+            desc_store(&a.desc[(int64_t)tile * NG + g], kDescInc | (pref + (uint32_t)agg[j]));
+        }
+        s_pref[g] = (int32_t)pref;
+    }
+    __syncthreads();
+
+    // ---- write the routed slots of this tile ----
+    int32_t flag = lost;
+    const uint32_t R = (uint32_t)a.recv_rows;
+#pragma unroll
+    for (int it = 0; it < kSlotsPerThread; ++it) {
+        const int64_t f = wslot0 + it * kWave + lane;
+        if (f >= routed) continue;
+        const uint32_t t = (uint32_t)f / (uint32_t)a.K, k = (uint32_t)f - t * (uint32_t)a.K;
+        int32_t* tr = &a.out.token_row[(int64_t)t * a.Kp + k];
+        const uint32_t g = key[it];
+        if (g == (uint32_t)NG) {
+            *tr = -1;
+            continue;
+        }
+        const uint32_t row = (uint32_t)s_start[g] + (uint32_t)s_pref[g] + (uint32_t)s_wcnt[w][g] + rnk[it];
+        if (row >= (uint32_t)s_lim[g]) {
+            *tr = -1;
+            flag |= EP_FLAG_DROPPED;
+            continue;
+        }
+        if (row >= R) {
+            *tr = -1;
+            flag |= EP_FLAG_INTERNAL;
+            continue;
+        }
+        *tr = (int32_t)row;
+        a.out.expert_ids[row] = eid[it];
+        a.out.src_info[2 * (int64_t)row] = (int32_t)t;
+        a.out.src_info[2 * (int64_t)row + 1] = (int32_t)k;
+    }
+
+    // ---- the fused shared expert: token t is rank t of group 0 of src_seg ----
+    if (a.shared) {
+        const int32_t per_tile = (a.T + a.tiles - 1) / a.tiles;
+        const int32_t t0 = (int32_t)tile * per_tile;
+        const int32_t t1 = min(a.T, t0 + per_tile);
+        const uint32_t st0 = (uint32_t)s_start[shared_group], lim0 = (uint32_t)s_lim[shared_group];
+        for (int32_t t = t0 + tid; t < t1; t += kLayoutThreads) {
+            int32_t* tr = &a.out.token_row[(int64_t)t * a.Kp + a.K];
+            const uint32_t row = st0 + (uint32_t)t;
+            if (row >= lim0) {
+                *tr = -1;
+                flag |= EP_FLAG_DROPPED;
+            } else if (row >= R) {
+                *tr = -1;
+                flag |= EP_FLAG_INTERNAL;
+            } else {
+                *tr = (int32_t)row;
+                a.out.expert_ids[row] = a.E;
+                a.out.src_info[2 * (int64_t)row] = t;
+                a.out.src_info[2 * (int64_t)row + 1] = a.K;
+            }
+        }
+    }
+
+    // ---- pad-row metadata of groups g = tile (mod tiles) ----
+    for (int g = (int)tile; g < NG; g += a.tiles) {
+        const int32_t c = s_cnt[g];
+        const int32_t npad = align_up(c, a.A) - c;
+        for (int32_t r = tid; r < npad; r += kLayoutThreads) {
+            const uint32_t row = (uint32_t)s_start[g] + (uint32_t)c + (uint32_t)r;
+            if (row >= (uint32_t)s_lim[g]) break;
+            if (row >= R) {
+                flag |= EP_FLAG_INTERNAL;
+                break;
+            }
+            a.out.expert_ids[row] = -1;
+            a.out.src_info[2 * (int64_t)row] = -1;
+            a.out.src_info[2 * (int64_t)row + 1] = -1;
+        }
+    }
+
+    if (flag) atomicOr(&s_flag, flag);
+    __syncthreads();
+    if (tid == 0 && s_flag) atomicOr(a.out.flags, s_flag);
+}
+
+}  // namespace
+
+hipError_t launch_layout(const LayoutArgs& a, hipStream_t stream) {
+    const int64_t nclear = (int64_t)a.tiles * a.NG > a.NG ? (int64_t)a.tiles * a.NG : a.NG;
+    int64_t cblocks = (nclear + 255) / 256;
+    if (cblocks > 1024) cblocks = 1024;
+    if (cblocks < 1) cblocks = 1;
+    hipLaunchKernelGGL(k_layout_clear, dim3((unsigned)cblocks), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(k_layout_hist, dim3((unsigned)a.tiles), dim3(kLayoutThreads), 0, stream, a);
+    hipLaunchKernelGGL(k_layout_rank, dim3((unsigned)a.tiles), dim3(kLayoutThreads), 0, stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace epx

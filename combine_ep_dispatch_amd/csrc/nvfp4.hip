@@ -1,0 +1,189 @@
+// NVFP4 dispatch with a per-token dynamic global scale (MAX
+// DistributedEPDispatchBlockScaledNVDynGlobalScales page, execute): every
+// token is quantized against its own global scale g = 2688 / rowmax, block
+// scales go to `scales`, the BF16 inverse of g to `rowscale`, and the packed
+// E2M1 codes to `codes`, once per kept (token, slot) row.
+//
+// 2688 = 448 * 6: the largest finite E4M3 block scale times the largest
+// E2M1 magnitude, so the block that holds rowmax gets scale 448.
+//
+// One wave64 per token.  Lane l holds 16-element blocks l, l+64, ... of the
+// row in registers (two 16-byte loads per block), so a block's amax is
+// lane-local and the row max is one wave reduction.  The token is quantized
+// once (VALU only: there is no contraction here for MFMA), then its bytes
+// are written to each of the token's K' rows: 8 code bytes per block per
+// lane (512 contiguous bytes per wave store), one scale byte per block.
+//
+// Arithmetic is IEEE binary32 with round-to-nearest-even everywhere; the
+// library is built with correctly rounded division and without FMA
+// contraction, so the results are bit-identical to the plain definition:
+//   s = (bmax / 6) * g            -> E4M3, RNE, saturating to 448
+//   v = x * (g / e4m3(s))         -> E2M1, RNE (ties to even), saturating
+//                                   at 6, sign bit of v kept
+//   rowscale = bf16(1 / g)
+// Formats: OCP OFP8 E4M3 ("fn": bias 7, max finite 448), OCP MX E2M1.
+#include "epx_device.h"
+
+namespace epx {
+namespace {
+
+constexpr int kQuantThreads = 256;
+constexpr int kQuantWaves = kQuantThreads / kWave;
+constexpr int kMaxBlocksPerLane = 16;  // H <= 16 * 64 * 16 = 16384
+
+// Non-negative finite s -> E4M3 code, RNE, saturating to 448 (0x7E).
+__device__ __forceinline__ uint32_t e4m3_encode(float s) {
+    if (!(s > 0.0f)) return 0u;
+    if (s >= 448.0f) return 0x7Eu;
+    if (s < 0.015625f) {                 // below 2^-6: subnormal step 2^-9
+        return (uint32_t)__builtin_rintf(s * 512.0f);  // exact scaling, RNE; 8 -> 0x08 = 2^-6
+    }
+    uint32_t u = __float_as_uint(s);
+    u += 0x7FFFFu + ((u >> 20) & 1u);    // round the mantissa to 3 bits, ties to even
+    const uint32_t c = (((u >> 23) - 120u) << 3) | ((u >> 20) & 7u);  // rebias 127 -> 7
+    return c > 0x7Eu ? 0x7Eu : c;
+}
+
+__device__ __forceinline__ float e4m3_decode(uint32_t c) {
+    const uint32_t e = c >> 3, m = c & 7u;
+    if (e == 0u) return (float)m * 0.001953125f;  // m * 2^-9, exact
+    return __uint_as_float(((e + 120u) << 23) | (m << 20));
+}
+
+// v -> E2M1 code.  Thresholds are the midpoints between the magnitudes
+// {0, .5, 1, 1.5, 2, 3, 4, 6}; at a midpoint the even code wins (the
+// comparison is strict toward the odd neighbour).
+__device__ __forceinline__ uint32_t e2m1_encode(float v) {
+    const float a = __builtin_fabsf(v);
+    uint32_t c = (a > 0.25f) + (a >= 0.75f) + (a > 1.25f) + (a >= 1.75f) + (a > 2.5f) + (a >= 3.5f) +
+                 (a > 5.0f);
+    return c | ((__float_as_uint(v) >> 28) & 8u);
+}
+
+__device__ __forceinline__ uint32_t absmax_bf16x2(uint32_t acc, uint32_t w) {
+    const uint32_t lo = w & 0x7FFFu, hi = (w >> 16) & 0x7FFFu;
+    return max(acc, max(lo, hi));
+}
+
+// Two E2M1 codes per byte, element 2j in the low nibble.
+__device__ __forceinline__ uint32_t codes_of_word(uint32_t w, float inv) {
+    const uint32_t c0 = e2m1_encode(bf16_lo(w) * inv);
+    const uint32_t c1 = e2m1_encode(bf16_hi(w) * inv);
+    return c0 | (c1 << 4);
+}
+
+template <int NBL>
+__global__ __launch_bounds__(kQuantThreads) void k_nvfp4(Nvfp4Args a) {
+    const int32_t t = uniform((int32_t)(blockIdx.x * kQuantWaves + threadIdx.x / kWave));
+    if (t >= a.T) return;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int32_t nblk = a.H / 16;
+    const uint4* xr = reinterpret_cast<const uint4*>(a.x + (int64_t)t * a.H);
+
+    uint4 q[NBL][2];
+    uint32_t bmax[NBL];
+    uint32_t lmax = 0;
+#pragma unroll
+    for (int i = 0; i < NBL; ++i) {
+        const int32_t b = lane + i * kWave;
+        if (b < nblk) {
+            q[i][0] = xr[2 * b];
+            q[i][1] = xr[2 * b + 1];
+        } else {
+            q[i][0] = make_uint4(0, 0, 0, 0);
+            q[i][1] = make_uint4(0, 0, 0, 0);
+        }
+        uint32_t m = 0;
+        m = absmax_bf16x2(m, q[i][0].x);
+        m = absmax_bf16x2(m, q[i][0].y);
+        m = absmax_bf16x2(m, q[i][0].z);
+        m = absmax_bf16x2(m, q[i][0].w);
+        m = absmax_bf16x2(m, q[i][1].x);
+        m = absmax_bf16x2(m, q[i][1].y);
+        m = absmax_bf16x2(m, q[i][1].z);
+        m = absmax_bf16x2(m, q[i][1].w);
+        bmax[i] = m;  // |x| as bf16 bits: integer order = magnitude order for finite x
+        lmax = max(lmax, m);
+    }
+#pragma unroll
+    for (int o = kWave / 2; o > 0; o >>= 1) lmax = max(lmax, (uint32_t)__shfl_xor((int)lmax, o, kWave));
+    const float rowmax = __uint_as_float(lmax << 16);
+
+    uint2 code[NBL];
+    uint32_t sc[NBL];
+    uint32_t rs = 0u;
+    if (rowmax == 0.0f) {
+#pragma unroll
+        for (int i = 0; i < NBL; ++i) {
+            code[i] = make_uint2(0, 0);
+            sc[i] = 0u;
+        }
+    } else {
+        const float g = 2688.0f / rowmax;
+#pragma unroll
+        for (int i = 0; i < NBL; ++i) {
+            const float d = __uint_as_float(bmax[i] << 16) / 6.0f;
+            const float s = d * g;
+            const uint32_t c = e4m3_encode(s);
+            const float sq = e4m3_decode(c);
+            sc[i] = c;
+            if (sq == 0.0f) {
+                code[i] = make_uint2(0, 0);
+            } else {
+                const float inv = g / sq;
+                code[i].x = codes_of_word(q[i][0].x, inv) | (codes_of_word(q[i][0].y, inv) << 8) |
+                            (codes_of_word(q[i][0].z, inv) << 16) | (codes_of_word(q[i][0].w, inv) << 24);
+                code[i].y = codes_of_word(q[i][1].x, inv) | (codes_of_word(q[i][1].y, inv) << 8) |
+                            (codes_of_word(q[i][1].z, inv) << 16) | (codes_of_word(q[i][1].w, inv) << 24);
+            }
+        }
+        rs = f32_to_bf16(1.0f / g);
+    }
+
+    const int64_t cstride = a.H / 2, sstride = nblk;
+    const int32_t* tr = a.token_row + (int64_t)t * a.Kp;
+    for (int32_t k = 0; k < a.Kp; ++k) {
+        const int32_t row = tr[k];
+        if (row < 0 || row >= a.R) continue;
+        uint8_t* crow = a.codes + (int64_t)row * cstride;
+        uint8_t* srow = a.scales + (int64_t)row * sstride;
+#pragma unroll
+        for (int i = 0; i < NBL; ++i) {
+            const int32_t b = lane + i * kWave;
+            if (b < nblk) {
+                *reinterpret_cast<uint2*>(crow + 8 * (int64_t)b) = code[i];
+                srow[b] = (uint8_t)sc[i];
+            }
+        }
+        if (lane == 0) a.rowscale[row] = (uint16_t)rs;
+    }
+}
+
+template <int NBL>
+hipError_t launch_nbl(const Nvfp4Args& a, hipStream_t stream) {
+    const unsigned blocks = (unsigned)((a.T + kQuantWaves - 1) / kQuantWaves);
+    hipLaunchKernelGGL(k_nvfp4<NBL>, dim3(blocks), dim3(kQuantThreads), 0, stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+int nvfp4_max_hidden() { return 16 * kWave * kMaxBlocksPerLane; }
+
+hipError_t launch_nvfp4(const Nvfp4Args& a, hipStream_t stream) {
+    if (a.T == 0) return hipSuccess;
+    const int nbl = (a.H / 16 + kWave - 1) / kWave;
+    switch (nbl) {
+        case 1: return launch_nbl<1>(a, stream);
+        case 2: return launch_nbl<2>(a, stream);
+        case 3: return launch_nbl<3>(a, stream);
+        case 4: return launch_nbl<4>(a, stream);
+        case 5: case 6: return launch_nbl<6>(a, stream);
+        case 7: return launch_nbl<7>(a, stream);
+        case 8: return launch_nbl<8>(a, stream);
+        case 9: case 10: case 11: case 12: return launch_nbl<12>(a, stream);
+        default: return launch_nbl<kMaxBlocksPerLane>(a, stream);
+    }
+}
+
+}  // namespace epx

@@ -1,0 +1,235 @@
+/*
+ * epx: MoE expert-parallel token dispatch and combine for one GPU's share of
+ * the work, on AMD Instinct MI355X (gfx950).
+ *
+ * Destination ranks are modelled as segments of one receive buffer in HBM:
+ * segment s holds the rows for experts [s*E/S, (s+1)*E/S).  Nothing here
+ * moves data between GPUs.
+ *
+ * Conventions for every call below:
+ *  - All buffers are caller-owned device memory (e.g. torch tensors).  The
+ *    library never allocates, frees or synchronizes; every call enqueues its
+ *    kernels on `stream` (a hipStream_t, NULL = the null stream) and returns.
+ *  - Calls are stateless and reentrant.  Two calls that share an output
+ *    buffer or a workspace must be ordered by the caller (same stream).
+ *  - bf16 values travel as uint16_t bit patterns; float is IEEE binary32.
+ *  - Payload pointers (x, recv, expert_out, y, grads, codes) must be 16-byte
+ *    aligned; index buffers 4-byte aligned.
+ *  - Return value: EP_OK, or a negative status (see ep_strerror).  Argument
+ *    errors are found on the host before anything is enqueued.  Data errors
+ *    (dropped slots, ids out of range) are reported on the device, in the
+ *    layout's flags word, and never make a call fail.
+ *
+ * Sources for the semantics (page title, API item):
+ *  [FA] NeMo AutoModel fused_a2a page: HybridEPDispatch.forward (tokens
+ *       [tokens, hidden] -> [dispatched_tokens, hidden] grouped by local
+ *       expert; topk_idx with -1 for unused slots; pad_multiple;
+ *       num_permuted_tokens as a static, host-known output extent),
+ *       HybridEPDispatch.backward (combine the gradients),
+ *       HybridEPCombine.forward / backward (restore token order;
+ *       redispatch the gradients).
+ *  [TD] NeMo AutoModel token_dispatcher page: _align_up,
+ *       TokenDispatcherConfig.moe_router_expert_pad_multiple,
+ *       TokenDispatcherConfig.moe_router_dtype (fp32 weighted averaging),
+ *       _assert_no_hybridep_overflow (device overflow flag, truncation at
+ *       capacity), _HybridEPManager._calibrate_hybridep_capacity,
+ *       _DeepepManager reversed_mapping_for_combine.
+ *  [MX] MAX DistributedEPDispatchBlockScaledNVDynGlobalScales page, execute:
+ *       NVFP4 with a per-token global scale 2688/rowmax, output_scales,
+ *       output_rowwise_scales (BF16 inverse global scale), row_offsets,
+ *       scales_offsets, expert_ids, src_info, atomic_counters,
+ *       fused_shared_expert.
+ */
+#ifndef EPX_H
+#define EPX_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define EPX_ABI_VERSION 1
+
+/* Status codes. */
+#define EP_OK 0
+#define EP_EINVAL (-1)   /* an argument fails a host-side check                */
+#define EP_ELAUNCH (-2)  /* the HIP runtime reported an error enqueueing work  */
+#define EP_ENOTSUP (-3)  /* the current device is not gfx950                   */
+
+/* Bits of ep_cfg_t.flags. */
+#define EP_ZERO_PAD_ROWS 1u  /* also write zeros into the payload of pad rows */
+
+/* Bits of the device flags word (ep_layout_t.flags[0]). */
+#define EP_FLAG_DROPPED 1      /* a slot was dropped at segment capacity [TD]  */
+#define EP_FLAG_BAD_ID 2       /* an expert id outside [-1, E) (slot masked)   */
+#define EP_FLAG_INTERNAL 4     /* the layout scan gave up waiting (never seen) */
+
+/* Largest number of groups S * (E/S + shared_expert) a layout may have. */
+#define EP_MAX_GROUPS 2048
+
+/*
+ * Problem description.  Field names follow the pages' statement of the
+ * problem ([MX] hidden_size, top_k, n_experts; [FA] num_local_experts,
+ * pad_multiple, num_permuted_tokens).
+ *
+ * Groups: segment s has G = E/S + shared_expert groups.  With a fused
+ * shared expert ([MX] fused_shared_expert) group 0 of every segment is the
+ * shared group; only segment src_segment receives rows in it (every token
+ * once, as top-k slot index `top_k`, expert id `num_experts`, weight 1 in
+ * combine).  Routed expert e goes to segment e/(E/S), group shared+e%(E/S).
+ */
+typedef struct ep_cfg_t {
+    int32_t num_tokens;    /* T >= 0 tokens of this GPU's share                   */
+    int32_t hidden;        /* H >= 8, multiple of 8 (bf16 calls) or 16 (NVFP4)     */
+    int32_t num_experts;   /* E >= 1 routed experts                               */
+    int32_t num_segments;  /* S >= 1 destination segments, E % S == 0             */
+    int32_t top_k;         /* K, 1 <= K <= E                                      */
+    int32_t align;         /* A >= 1: each group's rows are padded to a multiple  */
+    int32_t seg_capacity;  /* C >= 0: 0 = packed segments; > 0 = C rows per
+                              segment, slots past it are dropped and flagged      */
+    int32_t shared_expert; /* 0 or 1                                              */
+    int32_t src_segment;   /* 0 <= src_segment < S (ignored without shared)       */
+    int32_t reserved0;     /* must be 0                                           */
+    int64_t recv_rows;     /* R: rows of every receive-side buffer (expert_ids,
+                              src_info, recv, codes, ...); R >= ep_query's
+                              min_recv_rows and R < 2^31.  A host integer, so no
+                              call ever reads a count back from the device [FA]. */
+    uint32_t flags;        /* EP_ZERO_PAD_ROWS or 0                               */
+    uint32_t reserved1;    /* must be 0                                           */
+} ep_cfg_t;
+
+/*
+ * The dispatch "handle" ([FA] handle; [TD] overflow flag kept last): device
+ * arrays written by ep_dispatch_layout and read by every later call.  K' =
+ * K + shared_expert, G = groups per segment, R = recv_rows.
+ *   counts         int32 [S*G]      valid slots per group ([TD] tokens per expert)
+ *   seg_base       int32 [S+1]      first row of each segment (packed: running
+ *                                   sum of used rows; capacity: s*C)
+ *   row_offsets    int32 [S*(G+1)]  per segment, exclusive prefix of the
+ *                                   aligned group sizes, clamped to C ([MX])
+ *   scales_offsets int32 [S*(G+1)]  offsets into the block-scale rows; scales
+ *                                   are row-major, so equal to row_offsets ([MX])
+ *   token_row      int32 [T*K']     receive row of slot (t,k); -1 if the slot
+ *                                   is masked, invalid or dropped ([TD] the
+ *                                   reversed mapping used by combine)
+ *   expert_ids     int32 [R]        expert of every used row, -1 on pad rows;
+ *                                   shared rows carry E ([MX])
+ *   src_info       int32 [R*2]      (token t, slot k) of every used row,
+ *                                   (-1,-1) on pad rows ([MX])
+ *   flags          int32 [1]        EP_FLAG_* bits for this dispatch ([TD])
+ * Rows of a segment past its used rows are not written.  Within a group,
+ * rows follow ascending slot index t*K'+k (stable, deterministic).
+ */
+typedef struct ep_layout_t {
+    int32_t* counts;
+    int32_t* seg_base;
+    int32_t* row_offsets;
+    int32_t* scales_offsets;
+    int32_t* token_row;
+    int32_t* expert_ids;
+    int32_t* src_info;
+    int32_t* flags;
+} ep_layout_t;
+
+/*
+ * Sizes the caller must allocate for `cfg` (host only, no device work).
+ *   min_recv_rows   packed: T*K' + min(T*K', E+shared)*(A-1) (every group
+ *                   padded by at most A-1 rows, [TD] _align_up); capacity:
+ *                   S*C.
+ *   workspace_bytes scratch device memory for ep_dispatch_layout.
+ *   groups_per_seg  G = E/S + shared_expert.
+ * Any output pointer may be NULL.  Returns EP_OK or EP_EINVAL; recv_rows is
+ * not checked here.
+ */
+int ep_query(const ep_cfg_t* cfg, int64_t* min_recv_rows, int64_t* workspace_bytes,
+             int32_t* groups_per_seg);
+
+/*
+ * Build the receive layout from top-k expert ids ([FA] HybridEPDispatch
+ * routing-metadata preprocessing; [TD] dispatch_postprocess counts;
+ * [MX] row_offsets, expert_ids, src_info).
+ *   topk_ids   int32 [T*K], row-major; -1 = unused slot ([FA] topk_idx)
+ *   workspace  >= workspace_bytes from ep_query, 16-byte aligned; its
+ *              contents on entry do not matter and are clobbered
+ *   layout     the arrays above, all written here
+ * Steps (three kernels): clear the counters; per-tile wavefront
+ * ballot/popcount histogram into counts; one pass that scans the aligned
+ * group sizes, ranks every slot inside its group with a decoupled look-back
+ * over tiles, and writes token_row, expert_ids and src_info.
+ */
+int ep_dispatch_layout(const ep_cfg_t* cfg, const int32_t* topk_ids, void* workspace,
+                       int64_t workspace_bytes, const ep_layout_t* layout, void* stream);
+
+/*
+ * bf16 dispatch ([FA] HybridEPDispatch.forward with fuse_permute):
+ *   recv[token_row[t,k], :] = x[t, :] bit for bit, for every kept slot.
+ *   x     bf16 [T, H];  recv  bf16 [R, H].
+ * Uses layout->token_row (and counts/row_offsets/seg_base when
+ * EP_ZERO_PAD_ROWS is set).  Unused rows of recv are not written.
+ */
+int ep_dispatch(const ep_cfg_t* cfg, const ep_layout_t* layout, const uint16_t* x,
+                uint16_t* recv, void* stream);
+
+/*
+ * NVFP4 dispatch with a per-token dynamic global scale ([MX] execute):
+ * every token is quantized once and its bytes written to each kept row.
+ *   x         bf16 [T, H] (H % 16 == 0)
+ *   codes     uint8 [R, H/2]   E2M1 element codes, element 2j in the low
+ *                              nibble of byte j, 2j+1 in the high nibble
+ *   scales    uint8 [R, H/16]  E4M3 block scale of each 16-element block
+ *   rowscale  bf16  [R]        bf16(1/g), the inverse global scale
+ * Per token, in IEEE fp32 with round-to-nearest-even:
+ *   rowmax = max|x|;  g = 2688 / rowmax;
+ *   per block: s = (bmax / 6) * g -> E4M3 (RNE, saturating to 448);
+ *              v = x * (g / e4m3(s)) -> E2M1 (RNE, ties to even, saturating
+ *              at 6, sign bit of v kept); zero scale -> zero codes.
+ *   An all-zero token gives zero codes, zero scales and rowscale +0.
+ * Tokens must be finite; a token with 0 < rowmax < 2688/FLT_MAX (where g
+ * overflows) is outside the contract.
+ */
+int ep_dispatch_nvfp4(const ep_cfg_t* cfg, const ep_layout_t* layout, const uint16_t* x,
+                      uint8_t* codes, uint8_t* scales, uint16_t* rowscale, void* stream);
+
+/*
+ * Combine ([FA] HybridEPCombine.forward; [TD] moe_router_dtype fp32):
+ *   y[t, :] = bf16_rne( sum_{k=0..K'-1, token_row[t,k] >= 0}
+ *                       w_k * float(expert_out[token_row[t,k], :]) )
+ * accumulated in fp32 in ascending k, one rounding per multiply and per add
+ * (no fused multiply-add), starting from +0.  w_k = probs[t,k] for routed
+ * slots (1 when probs is NULL) and 1 for the shared slot.
+ *   expert_out bf16 [R, H];  probs float [T, K] or NULL;  y bf16 [T, H].
+ * Pad and dropped rows are never read.
+ */
+int ep_combine(const ep_cfg_t* cfg, const ep_layout_t* layout, const uint16_t* expert_out,
+               const float* probs, uint16_t* y, void* stream);
+
+/*
+ * Dispatch backward ([FA] HybridEPDispatch.backward: combine the
+ * gradients): grad_x[t] = bf16_rne( sum_k float(grad_recv[token_row[t,k]]) ),
+ * fp32, ascending k, unweighted (dispatch is a copy); 0 if no slot is kept.
+ *   grad_recv bf16 [R, H];  grad_x bf16 [T, H].
+ */
+int ep_dispatch_bwd(const ep_cfg_t* cfg, const ep_layout_t* layout, const uint16_t* grad_recv,
+                    uint16_t* grad_x, void* stream);
+
+/*
+ * Combine backward ([FA] HybridEPCombine.backward: redispatch through the
+ * saved layout): grad_expert_out[token_row[t,k]] = bf16_rne(w_k * float(grad_y[t]))
+ * for every kept slot, w_k as in ep_combine.
+ *   grad_y bf16 [T, H];  probs float [T, K] or NULL;  grad_expert_out bf16 [R, H].
+ */
+int ep_combine_bwd(const ep_cfg_t* cfg, const ep_layout_t* layout, const uint16_t* grad_y,
+                   const float* probs, uint16_t* grad_expert_out, void* stream);
+
+/* Static description of a status code. */
+const char* ep_strerror(int status);
+
+/* EPX_ABI_VERSION of the built library. */
+int ep_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EPX_H */

@@ -1,0 +1,188 @@
+"""The C ABI on the host (no GPU needed): the library loads, exports every
+symbol include/epx.h declares, sizes buffers as documented and rejects every
+host-checkable invalid argument with EP_EINVAL before touching the device.
+
+No call here reaches a kernel launch: each one fails validation first.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    from combine_ep_dispatch_amd import _lib
+
+    if not os.path.exists(_lib.LIB_PATH):
+        from combine_ep_dispatch_amd import build
+
+        build.build()
+    return _lib.lib()
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "epx.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ep_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(L):
+    from combine_ep_dispatch_amd import _lib
+
+    names = declared_functions()
+    assert set(names) == set(_lib.SYMBOLS), names
+    for n in names:
+        assert hasattr(L, n), n
+    assert L.ep_abi_version() == 1
+    assert L.ep_strerror(-1) == b"invalid argument"
+    assert L.ep_strerror(0) == b"ok"
+
+
+def test_header_and_binding_structs_agree():
+    from combine_ep_dispatch_amd._lib import EpCfg, EpLayout
+
+    assert ctypes.sizeof(EpCfg) == 10 * 4 + 8 + 2 * 4
+    assert EpCfg.recv_rows.offset == 40
+    assert ctypes.sizeof(EpLayout) == 8 * 8
+
+
+def cfg(**kw):
+    from combine_ep_dispatch_amd import EpConfig
+
+    base = dict(num_tokens=128, hidden=256, num_experts=8, num_segments=2, top_k=2, align=16)
+    base.update(kw)
+    return EpConfig(**base)
+
+
+def query(L, c):
+    from combine_ep_dispatch_amd._lib import EpCfg  # noqa: F401
+
+    rows, ws, g = ctypes.c_int64(-1), ctypes.c_int64(-1), ctypes.c_int32(-1)
+    cc = c.to_c()
+    st = L.ep_query(ctypes.byref(cc), ctypes.byref(rows), ctypes.byref(ws), ctypes.byref(g))
+    return st, rows.value, ws.value, g.value
+
+
+def test_query_sizes(L, orc):
+    import numpy as np
+
+    for kw in [dict(), dict(align=1), dict(shared_expert=1, src_segment=1),
+               dict(seg_capacity=100), dict(num_tokens=0), dict(num_tokens=4096, hidden=7168,
+               num_experts=256, num_segments=8, top_k=8, align=128)]:
+        c = cfg(**kw)
+        st, rows, ws, g = query(L, c)
+        assert st == 0
+        oc = orc.Cfg(T=c.num_tokens, H=c.hidden, E=c.num_experts, S=c.num_segments, K=c.top_k,
+                     A=c.align, C=c.seg_capacity, shared=c.shared_expert, src_seg=c.src_segment)
+        assert rows == orc.min_recv_rows(oc)
+        assert g == c.num_experts // c.num_segments + c.shared_expert
+        tiles = max(1, -(-c.num_tokens * c.top_k // 2048))
+        assert ws == 256 + tiles * c.num_segments * g * 4
+    # the bound is reached by some routing and never exceeded (oracle layout)
+    rng = np.random.default_rng(0)
+    c = cfg(num_tokens=9, num_experts=12, num_segments=3, top_k=3, align=5, shared_expert=1)
+    _, rows, _, _ = query(L, c)
+    oc = orc.Cfg(T=9, H=8, E=12, S=3, K=3, A=5, shared=1, recv_rows=rows)
+    for _ in range(50):
+        ids = np.stack([rng.permutation(12)[:3] for _ in range(9)]).astype(np.int32)
+        assert orc.layout(oc, ids)["seg_base"][-1] <= rows
+
+
+INVALID = [
+    dict(num_tokens=-1), dict(hidden=0), dict(hidden=12), dict(num_experts=0), dict(num_segments=0),
+    dict(num_experts=9), dict(top_k=0), dict(top_k=9), dict(align=0), dict(seg_capacity=-1),
+    dict(shared_expert=2), dict(shared_expert=1, src_segment=2), dict(shared_expert=1, src_segment=-1),
+    dict(flags=8), dict(num_experts=4096, num_segments=2),  # > EP_MAX_GROUPS groups
+    dict(num_tokens=1 << 28, top_k=4),  # 2^30 slots
+]
+
+
+@pytest.mark.parametrize("kw", INVALID, ids=[str(k) for k in INVALID])
+def test_query_rejects_invalid_config(L, kw):
+    assert query(L, cfg(**kw))[0] == -1
+
+
+def test_null_config_and_reserved_fields(L):
+    assert L.ep_query(None, None, None, None) == -1
+    c = cfg().to_c()
+    c.reserved0 = 1
+    assert L.ep_query(ctypes.byref(c), None, None, None) == -1
+    c = cfg().to_c()
+    c.reserved1 = 7
+    assert L.ep_query(ctypes.byref(c), None, None, None) == -1
+
+
+def test_calls_reject_bad_arguments_before_any_launch(L):
+    from combine_ep_dispatch_amd._lib import EpLayout
+
+    c = cfg()
+    st, rows, ws, g = query(L, c)
+    fake = 0x10000  # never dereferenced: every call below fails validation first
+    lay = EpLayout(*([fake] * 8))
+    # recv_rows below the bound
+    c.recv_rows = rows - 1
+    cc = c.to_c()
+    assert L.ep_dispatch_layout(ctypes.byref(cc), fake, fake, ws, ctypes.byref(lay), None) == -1
+    assert L.ep_dispatch(ctypes.byref(cc), ctypes.byref(lay), fake, fake, None) == -1
+    assert L.ep_combine(ctypes.byref(cc), ctypes.byref(lay), fake, None, fake, None) == -1
+    assert L.ep_dispatch_bwd(ctypes.byref(cc), ctypes.byref(lay), fake, fake, None) == -1
+    assert L.ep_combine_bwd(ctypes.byref(cc), ctypes.byref(lay), fake, None, fake, None) == -1
+    assert L.ep_dispatch_nvfp4(ctypes.byref(cc), ctypes.byref(lay), fake, fake, fake, fake, None) == -1
+    c.recv_rows = rows
+    cc = c.to_c()
+    # workspace too small / misaligned / missing
+    assert L.ep_dispatch_layout(ctypes.byref(cc), fake, fake, ws - 1, ctypes.byref(lay), None) == -1
+    assert L.ep_dispatch_layout(ctypes.byref(cc), fake, fake + 4, ws, ctypes.byref(lay), None) == -1
+    assert L.ep_dispatch_layout(ctypes.byref(cc), fake, None, ws, ctypes.byref(lay), None) == -1
+    # missing or misaligned buffers
+    assert L.ep_dispatch_layout(ctypes.byref(cc), None, fake, ws, ctypes.byref(lay), None) == -1
+    assert L.ep_dispatch_layout(ctypes.byref(cc), fake, fake, ws, None, None) == -1
+    for field in ("counts", "seg_base", "row_offsets", "scales_offsets", "token_row", "expert_ids",
+                  "src_info", "flags"):
+        bad = EpLayout(*([fake] * 8))
+        setattr(bad, field, None)
+        assert L.ep_dispatch_layout(ctypes.byref(cc), fake, fake, ws, ctypes.byref(bad), None) == -1, field
+        setattr(bad, field, fake + 2)
+        assert L.ep_dispatch_layout(ctypes.byref(cc), fake, fake, ws, ctypes.byref(bad), None) == -1, field
+    assert L.ep_dispatch(ctypes.byref(cc), ctypes.byref(lay), fake + 8, fake, None) == -1
+    assert L.ep_dispatch(ctypes.byref(cc), ctypes.byref(lay), fake, None, None) == -1
+    assert L.ep_dispatch(ctypes.byref(cc), None, fake, fake, None) == -1
+    assert L.ep_combine(ctypes.byref(cc), ctypes.byref(lay), fake, fake + 2, fake, None) == -1
+    assert L.ep_combine_bwd(ctypes.byref(cc), ctypes.byref(lay), fake, fake + 1, fake, None) == -1
+    assert L.ep_dispatch_bwd(ctypes.byref(cc), ctypes.byref(lay), None, fake, None) == -1
+    # NVFP4 needs H % 16 == 0 and H <= 16384
+    c24 = cfg(hidden=24)
+    c24.recv_rows = rows
+    cc = c24.to_c()
+    assert L.ep_dispatch_nvfp4(ctypes.byref(cc), ctypes.byref(lay), fake, fake, fake, fake, None) == -1
+    cbig = cfg(hidden=16384 + 16)
+    cbig.recv_rows = rows
+    cc = cbig.to_c()
+    assert L.ep_dispatch_nvfp4(ctypes.byref(cc), ctypes.byref(lay), fake, fake, fake, fake, None) == -1
+
+
+def test_binding_rejects_cpu_tensors():
+    import torch
+
+    import combine_ep_dispatch_amd as epx
+
+    c = cfg()
+    c.recv_rows = epx.ep_query(c).min_recv_rows
+    with pytest.raises(ValueError):
+        epx.ep_dispatch_layout(c, torch.zeros(c.num_tokens * c.top_k, dtype=torch.int32),
+                               torch.zeros(64, dtype=torch.uint8), None)
+
+
+def test_product_package_does_not_touch_the_oracle():
+    pkg = os.path.join(ROOT, "combine_ep_dispatch_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert "import oracle" not in text and "from oracle" not in text, f
+                assert "liboracle" not in text, f

@@ -1,0 +1,208 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle on the
+same seeded inputs.
+
+Bar: bit-exact for counts, offsets, token_row, expert_ids, src_info, flags,
+the bf16 dispatch copy, NVFP4 codes / scales / rowscales and the combine
+backward; the combine and dispatch backward reductions must be within
+|gpu - oracle| <= 1e-2 + 2e-2 |oracle| and, since both sides add in the same
+order without contraction, are also checked bit for bit.
+
+Cases: the five named workloads at full size, the launch configuration the
+benchmark times included; seeded random shapes (ragged tiles, partial hidden
+pieces, masked / invalid / duplicate ids, shared expert, capacity); edge
+cases (no tokens, everything masked, the largest group count, tile
+boundaries, K = 1, one expert per segment, tiny capacities).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def G():
+    import gpu_cases as gc
+
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    torch.cuda.init()
+    return gc
+
+
+NAMED = ["tiny", "dsv3", "skewed", "nvfp4", "capacity"]
+
+
+@pytest.mark.parametrize("name", NAMED)
+def test_named_workload_full_size(G, name):
+    c = G.workload_case(name)
+    lay = G.check_layout(c, name)
+    f = int(lay.flags.item())
+    assert f & 4 == 0
+    if name == "nvfp4":
+        G.check_nvfp4(c, lay, name)
+    G.check_dispatch(c, lay, name)
+    G.check_combine(c, lay, name, weighted=True)
+    G.check_dispatch_bwd(c, lay, name)
+    G.check_combine_bwd(c, lay, name, weighted=True)
+    if name == "capacity":
+        assert f == 1  # overflow flag raised, nothing else
+    else:
+        assert f == 0
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_random_shapes(G, seed):
+    rng = np.random.default_rng(seed)
+    kw = {}
+    if seed % 4 == 1:
+        kw["distinct"] = False
+    if seed % 6 == 2:
+        kw["bad_p"] = 0.05
+    c = G.random_case(100 + seed, **kw)
+    if seed % 5 == 3:
+        load = max(1, c.cfg.num_tokens * c.cfg.kp // c.cfg.num_segments)
+        c.cfg.seg_capacity = int(rng.integers(1, load + 2))
+        c.cfg.recv_rows = G.epx.ep_query(c.cfg).min_recv_rows
+        c = G.Case(c.cfg, c.ids, c.probs, c.x, c.seed)
+    name = f"random{seed}"
+    lay = G.check_layout(c, name)
+    G.check_dispatch(c, lay, name)
+    if c.cfg.hidden % 16 == 0:
+        G.check_nvfp4(c, lay, name)
+    G.check_combine(c, lay, name, weighted=seed % 2 == 0)
+    G.check_dispatch_bwd(c, lay, name)
+    G.check_combine_bwd(c, lay, name, weighted=seed % 3 != 0)
+
+
+EDGE = {
+    "no_tokens": dict(T=0),
+    "all_masked": dict(T=300, mask_p=1.0),
+    "one_token": dict(T=1, K=3, E_loc=4, S=2),
+    "max_groups": dict(T=600, S=8, E_loc=255, K=8, shared=1, A=4),
+    "max_groups_flat": dict(T=400, S=1, E_loc=2048, K=6, shared=0, A=2),
+    "tile_exact": dict(T=2048, K=2, S=2, E_loc=8),
+    "tile_plus_one": dict(T=2049, K=2, S=2, E_loc=8),
+    "tile_minus_one_slot": dict(T=683, K=3, S=4, E_loc=5),
+    "k1": dict(T=500, K=1),
+    "one_expert_per_segment": dict(T=700, S=8, E_loc=1, K=4),
+    "align_one": dict(T=700, A=1),
+    "big_align": dict(T=300, A=256, S=3, E_loc=3, K=2),
+    "many_tiles": dict(T=9000, S=4, E_loc=16, K=8, A=16, H=16),
+    "hot_expert": dict(T=4000, S=2, E_loc=1, K=1, H=32, A=8),
+}
+
+
+@pytest.mark.parametrize("edge", sorted(EDGE))
+def test_edge_cases(G, edge):
+    c = G.random_case(7, **dict(EDGE[edge]))
+    lay = G.check_layout(c, edge)
+    G.check_dispatch(c, lay, edge)
+    if c.cfg.hidden % 16 == 0:
+        G.check_nvfp4(c, lay, edge)
+    G.check_combine(c, lay, edge)
+    G.check_dispatch_bwd(c, lay, edge)
+    G.check_combine_bwd(c, lay, edge)
+
+
+@pytest.mark.parametrize("C", [1, 2, 7, 64])
+def test_tiny_capacities(G, C):
+    c = G.random_case(55, T=400, S=4, E_loc=4, K=4, A=4, shared=1, src=2, C=C)
+    c.cfg.recv_rows = G.epx.ep_query(c.cfg).min_recv_rows
+    c = G.Case(c.cfg, c.ids, c.probs, c.x, c.seed)
+    lay = G.check_layout(c, f"cap{C}")
+    assert int(lay.flags.item()) & 1
+    G.check_dispatch(c, lay, f"cap{C}")
+    G.check_nvfp4(c, lay, f"cap{C}")
+    G.check_combine(c, lay, f"cap{C}")
+    G.check_combine_bwd(c, lay, f"cap{C}")
+
+
+def test_nvfp4_special_rows(G):
+    """Zero tokens, negative zeros, subnormal bf16 values, huge outliers,
+    tiny blocks next to a large one (E4M3-subnormal and zero block scales)."""
+    rng = np.random.default_rng(3)
+    T, H = 64, 1040  # H/16 = 65 blocks: the second block column of a lane is ragged
+    x = rng.standard_normal((T, H)).astype(np.float32)
+    x[0] = 0
+    x[1] = -0.0
+    x[2] = 1e-39                                   # bf16 subnormals
+    x[3, :] = 1e-5 * rng.standard_normal(H)
+    x[3, 17] = 250.0                               # tiny blocks beside a big one
+    x[4] *= 3e4
+    x[5] = rng.uniform(-6, 6, H)
+    x[6, ::2] = 0.0
+    x[7] = 10.0 ** rng.uniform(-30, 30, H) * np.sign(rng.standard_normal(H))
+    xb = G.wl.bf16_bits(x)
+    c = G.random_case(9, T=T, H=H, S=2, E_loc=4, K=2, A=4, shared=1, src=0, mask_p=0.0)
+    c = G.Case(c.cfg, c.ids, c.probs, xb, c.seed)
+    lay = G.check_layout(c, "nvfp4_special")
+    G.check_nvfp4(c, lay, "nvfp4_special")
+
+
+def test_determinism_and_garbage_workspace(G):
+    c = G.workload_case("skewed", T=3000)
+    a = G.layout_np(G.gpu_layout(c.cfg, c.ids, garbage_ws=True))
+    b = G.layout_np(G.gpu_layout(c.cfg, c.ids, garbage_ws=False))
+    for k in a:
+        assert np.array_equal(a[k], b[k]), k
+    G.assert_layout_equal(a, c.L, "skewed3000")
+
+
+def test_zero_pad_rows_flag(G):
+    c = G.random_case(21, T=333, S=3, E_loc=5, K=3, A=16, H=64, shared=1, src=1)
+    c.cfg.flags = G.epx.EP_ZERO_PAD_ROWS
+    lay = G.check_layout(c, "zero_pad")
+    cfg = c.cfg
+    tr = c.L["token_row"]
+    used = np.zeros(cfg.recv_rows, bool)
+    for s in range(cfg.num_segments):
+        used[c.L["seg_base"][s]: c.L["seg_base"][s] + c.L["row_offsets"][s, -1]] = True
+    pad = used.copy()
+    pad[tr[tr >= 0]] = False
+    assert pad.any()
+    recv = G.bf16_filled(cfg.recv_rows, cfg.hidden, 0x7FA5)
+    G.epx.ep_dispatch(cfg, lay, G.u16_tensor(c.x), recv)
+    codes = torch.full((cfg.recv_rows * cfg.hidden // 2,), 0xA5, dtype=torch.uint8, device=G.DEV)
+    scales = torch.full((cfg.recv_rows * cfg.hidden // 16,), 0xA5, dtype=torch.uint8, device=G.DEV)
+    rowscale = G.bf16_filled(cfg.recv_rows, 1, 0x7FA5)
+    G.epx.ep_dispatch_nvfp4(cfg, lay, G.u16_tensor(c.x), codes, scales, rowscale)
+    gy = G.wl.make_tensor_like_rows(cfg.num_tokens, cfg.hidden, 5)
+    go = G.bf16_filled(cfg.recv_rows, cfg.hidden, 0x7FA5)
+    G.epx.ep_combine_bwd(cfg, lay, G.u16_tensor(gy), torch.from_numpy(c.probs.reshape(-1)).to(G.DEV), go)
+    torch.cuda.synchronize()
+    r = G.bits_of(recv).reshape(cfg.recv_rows, cfg.hidden)
+    assert np.all(r[pad] == 0) and np.all(r[~used] == 0x7FA5)
+    assert np.array_equal(r[tr[tr >= 0]], G.orc.dispatch(c.oc, tr, c.x)[tr[tr >= 0]])
+    cd = codes.cpu().numpy().reshape(cfg.recv_rows, -1)
+    sc = scales.cpu().numpy().reshape(cfg.recv_rows, -1)
+    rs = G.bits_of(rowscale)
+    assert np.all(cd[pad] == 0) and np.all(sc[pad] == 0) and np.all(rs[pad] == 0)
+    assert np.all(cd[~used] == 0xA5) and np.all(rs[~used] == 0x7FA5)
+    g = G.bits_of(go).reshape(cfg.recv_rows, cfg.hidden)
+    assert np.all(g[pad] == 0) and np.all(g[~used] == 0x7FA5)
+
+
+def test_assert_no_overflow(G):
+    c = G.workload_case("capacity", T=2000)
+    lay = G.gpu_layout(c.cfg, c.ids)
+    with pytest.raises(G.epx.EpError):
+        G.epx.assert_no_overflow(lay, capacity=c.cfg.seg_capacity)
+    c2 = G.workload_case("tiny")
+    G.epx.assert_no_overflow(G.gpu_layout(c2.cfg, c2.ids))
+
+
+def test_combine_of_dispatch_is_identity_on_gpu(G):
+    """combine(dispatch(x)) with identity experts and probabilities summing
+    to 1 returns x exactly (the shared expert, weight 1, doubles it)."""
+    for name in ("dsv3", "nvfp4"):
+        c = G.workload_case(name, T=512)
+        cfg = c.cfg
+        lay = G.gpu_layout(cfg, c.ids)
+        recv = G.bf16_filled(cfg.recv_rows, cfg.hidden, 0x7FC1)  # pad rows stay NaN
+        G.epx.ep_dispatch(cfg, lay, G.u16_tensor(c.x), recv)
+        y = G.bf16_filled(cfg.num_tokens, cfg.hidden, 0)
+        G.epx.ep_combine(cfg, lay, recv, torch.from_numpy(c.probs.reshape(-1)).to(G.DEV), y)
+        torch.cuda.synchronize()
+        want = c.x if not cfg.shared_expert else G.wl.bf16_bits(2.0 * G.f32(c.x))
+        assert np.array_equal(G.bits_of(y).reshape(cfg.num_tokens, -1), want), name
