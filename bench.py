@@ -1,0 +1,345 @@
+"""Benchmark of the MoE expert-parallel dispatch/combine hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload dsv3]
+
+One step is one pass of the whole hot path over one batch of the
+DeepSeek-V3-shaped share (T=4096 tokens, H=7168 bf16, 256 experts over 8
+segments, top-8, alignment 128), inputs resident in HBM:
+
+    ep_dispatch_layout  -> ep_dispatch (bf16) -> ep_dispatch_nvfp4
+    -> ep_combine -> ep_combine_bwd -> ep_dispatch_bwd
+
+The step is captured once into a HIP graph; K replays are timed between two
+device synchronizations (the same step launched op by op from Python is
+reported as eager_ms_per_step).  Each op is also captured as a graph of 8
+back-to-back launches and bracketed by HIP events on the stream it runs on,
+which gives each kernel's average duration.  Prints ONE JSON line on stdout:
+tokens/s of the whole step (`value`), the roofline of the dominant kernel
+(algorithmic bytes of one launch / its average duration, against the 8 TB/s
+HBM peak), and the CPU oracle's tokens/s on the same batch (`cpu_baseline`).
+
+--copy-calibration runs only a plain row copy of known size through the
+dispatch kernel (identity routing, K=1): the reference for scaling the
+rocprofv3 FETCH_SIZE / WRITE_SIZE counters to bytes.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import platform
+import statistics
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, published
+METRIC = "dispatch+combine tokens/s and effective HBM GB/s (% of peak), 1 MI355X"
+KERNEL_SOURCES = ("combine_ep_dispatch_amd/csrc/move.hip", "combine_ep_dispatch_amd/csrc/nvfp4.hip",
+                  "combine_ep_dispatch_amd/csrc/layout.hip", "combine_ep_dispatch_amd/csrc/epx_device.h")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def source_digest() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(op: str):
+    """HBM bytes per launch of `op` measured with rocprofv3 counters (see
+    profiles/), or None when missing or taken on different kernel sources."""
+    path = os.path.join(ROOT, "profiles", "traffic_dsv3.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        doc = json.load(f)
+    if doc.get("source_digest") != source_digest():
+        return None
+    entry = doc.get("ops", {}).get(op)
+    return None if entry is None else entry.get("bytes_per_launch")
+
+
+def algorithmic_bytes(w, kept: int, used_rows: int) -> dict:
+    """Bytes each op must move at minimum: valid rows only, x read once,
+    pad rows never touched (layout metadata: 12 bytes per used row)."""
+    T, H, K, Kp = w.T, w.H, w.K, w.Kp
+    row = 2 * H
+    return {
+        "layout": 4 * T * K + 4 * T * Kp + 12 * used_rows,
+        "dispatch": row * T + row * kept + 4 * T * Kp,
+        "dispatch_nvfp4": row * T + kept * (H // 2 + H // 16 + 2) + 4 * T * Kp,
+        "combine": row * kept + row * T + 4 * T * K + 4 * T * Kp,
+        "combine_bwd": row * T + row * kept + 4 * T * K + 4 * T * Kp,
+        "dispatch_bwd": row * kept + row * T + 4 * T * Kp,
+    }
+
+
+def cpu_baseline(w, host) -> dict:
+    """Time the CPU oracle (single-threaded C) over the whole step on the same
+    batch; tokens/s = T / seconds."""
+    import oracle as orc
+
+    orc.build(force=False)
+    oc = orc.Cfg(T=w.T, H=w.H, E=w.E, S=w.S, K=w.K, A=w.align, C=w.capacity, shared=w.shared_expert,
+                 src_seg=w.src_segment, recv_rows=host["R"])
+    t0 = time.perf_counter()
+    L = orc.layout(oc, host["ids"])
+    tr = L["token_row"]
+    orc.dispatch(oc, tr, host["x"])
+    orc.dispatch_nvfp4(oc, tr, host["x"])
+    orc.combine(oc, tr, host["out"], host["probs"])
+    orc.combine_bwd(oc, tr, host["gy"], host["probs"])
+    orc.dispatch_bwd(oc, tr, host["grad_recv"])
+    dt = time.perf_counter() - t0
+    cpu = platform.processor() or platform.machine()
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"value": round(w.T / dt, 1), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"one full step (layout, bf16 + NVFP4 dispatch, combine, both backward passes) "
+                      f"over the whole {w.T}-token batch, single-threaded C oracle, {dt:.2f} s; "
+                      f"host {cpu}, os.cpu_count()={os.cpu_count()}"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="dsv3")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU's share of the work; --gpus {args.gpus} is not supported "
+              "(destination ranks are modelled as segments of one receive buffer, no inter-GPU traffic)",
+              file=sys.stderr)
+        return 2
+
+    import torch
+
+    import combine_ep_dispatch_amd as epx
+    from combine_ep_dispatch_amd import workload as wl
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+
+    if args.copy_calibration:
+        return copy_calibration(torch, epx, dev)
+
+    w = wl.CONFIGS[args.workload]
+    log(f"[bench] workload {wl.describe(w)}")
+    d = wl.make_workload(w)
+    cfg = epx.EpConfig(num_tokens=w.T, hidden=w.H, num_experts=w.E, num_segments=w.S, top_k=w.K,
+                       align=w.align, seg_capacity=w.capacity, shared_expert=w.shared_expert,
+                       src_segment=w.src_segment)
+    q = epx.ep_query(cfg)
+    cfg.recv_rows = q.min_recv_rows
+    R, T, H = cfg.recv_rows, w.T, w.H
+
+    # inputs resident in HBM
+    x = torch.from_numpy(d["x"].view(np.int16)).to(dev).view(torch.bfloat16)
+    ids = torch.from_numpy(d["topk_ids"].reshape(-1)).to(dev)
+    probs = torch.from_numpy(d["probs"].reshape(-1)).to(dev)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(1)
+    out = torch.randn(R * H, generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    gy = torch.randn(T * H, generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    grad_recv = torch.randn(R * H, generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    # outputs
+    lay = epx.Layout.empty(cfg, dev)
+    ws = epx.workspace_for(cfg, dev)
+    recv = torch.empty(R * H, dtype=torch.bfloat16, device=dev)
+    codes = torch.empty(R * H // 2, dtype=torch.uint8, device=dev)
+    scales = torch.empty(R * H // 16, dtype=torch.uint8, device=dev)
+    rowscale = torch.empty(R, dtype=torch.bfloat16, device=dev)
+    y = torch.empty(T * H, dtype=torch.bfloat16, device=dev)
+    gout = torch.empty(R * H, dtype=torch.bfloat16, device=dev)
+    gx = torch.empty(T * H, dtype=torch.bfloat16, device=dev)
+
+    ops = [
+        ("layout", lambda: epx.ep_dispatch_layout(cfg, ids, ws, lay)),
+        ("dispatch", lambda: epx.ep_dispatch(cfg, lay, x, recv)),
+        ("dispatch_nvfp4", lambda: epx.ep_dispatch_nvfp4(cfg, lay, x, codes, scales, rowscale)),
+        ("combine", lambda: epx.ep_combine(cfg, lay, out, probs, y)),
+        ("combine_bwd", lambda: epx.ep_combine_bwd(cfg, lay, gy, probs, gout)),
+        ("dispatch_bwd", lambda: epx.ep_dispatch_bwd(cfg, lay, grad_recv, gx)),
+    ]
+    names = [n for n, _ in ops]
+
+    def step():
+        for _, fn in ops:
+            fn()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    eager_out = {k: v.clone() for k, v in (("recv", recv), ("codes", codes), ("y", y), ("gout", gout),
+                                           ("gx", gx), ("token_row", lay.token_row))}
+    # eager step time (host launch overhead included)
+    t0 = time.perf_counter()
+    for _ in range(max(3, args.steps // 5)):
+        step()
+    torch.cuda.synchronize()
+    eager_ms = (time.perf_counter() - t0) * 1e3 / max(3, args.steps // 5)
+
+    # the whole step as one HIP graph
+    g_step = capture(torch, step)
+    g_step.replay()
+    torch.cuda.synchronize()
+    for k, v in eager_out.items():
+        cur = {"recv": recv, "codes": codes, "y": y, "gout": gout, "gx": gx, "token_row": lay.token_row}[k]
+        if not torch.equal(cur.view(torch.uint8), v.view(torch.uint8)):  # bitwise: unused rows may hold NaNs
+            raise RuntimeError(f"graph replay of the step changed {k}")
+    log(f"[bench] warmup {args.warmup} done, graph checked; timing {args.steps} steps")
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record(stream)
+    for _ in range(args.steps):
+        g_step.replay()
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / args.steps
+    gpu_ms_step = start.elapsed_time(end) / args.steps
+
+    # per-op kernel durations: a graph of LAUNCHES back-to-back launches per op,
+    # bracketed by HIP events on the stream the kernels run on
+    LAUNCHES, REPS = 8, max(5, args.steps // 5)
+    op_us = {}
+    for n, fn in ops:
+        def many(fn=fn):
+            for _ in range(LAUNCHES):
+                fn()
+        g = capture(torch, many)
+        times = []
+        for _ in range(REPS):
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            g.replay()
+            b.record(stream)
+            times.append((a, b))
+        torch.cuda.synchronize()
+        op_us[n] = [a.elapsed_time(b) * 1e3 / LAUNCHES for a, b in times]
+        del g
+    flags = int(lay.flags.item())
+    tr = lay.token_row.cpu().numpy()
+    kept = int((tr >= 0).sum())
+    rowoff = lay.row_offsets.cpu().numpy()
+    used_rows = int(rowoff[:, -1].sum())
+    nbytes = algorithmic_bytes(w, kept, used_rows)
+    per_op = {}
+    for n in names:
+        us = statistics.mean(op_us[n])
+        med = statistics.median(op_us[n])
+        gbps = nbytes[n] / (us * 1e-6) / 1e9
+        per_op[n] = {"us": round(us, 2), "us_median": round(med, 2), "bytes": nbytes[n],
+                     "GBps": round(gbps, 1), "frac": round(gbps / HBM_PEAK_GBPS, 4)}
+        log(f"[bench] {n:15s} {us:9.2f} us  {nbytes[n] / 1e6:9.2f} MB  {gbps:8.1f} GB/s  "
+            f"{100 * gbps / HBM_PEAK_GBPS:5.1f}% of 8 TB/s")
+    step_bytes = sum(nbytes.values())
+    dom = max((n for n in names if n != "layout"), key=lambda n: per_op[n]["us"])
+    fwd_us = per_op["layout"]["us"] + per_op["dispatch"]["us"] + per_op["combine"]["us"]
+    roof = {"bound": "hbm", "kernel": dom, "achieved": per_op[dom]["GBps"], "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s", "frac": per_op[dom]["frac"], "traffic": traffic_for(dom),
+            "algorithmic_bytes_per_launch": nbytes[dom], "avg_launch_us": per_op[dom]["us"]}
+
+    result = {
+        "metric": METRIC,
+        "value": round(T / (ms_step * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "gpu_ms_per_step": round(gpu_ms_step, 4),
+        "eager_ms_per_step": round(eager_ms, 4),
+        "launch": "one HIP graph per step (eager_ms_per_step: the same step launched from Python)",
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"DeepSeek-V3-shaped share: {wl.describe(w)}",
+                   "step": "layout + bf16 dispatch + NVFP4 dispatch + combine + combine_bwd + dispatch_bwd",
+                   "tokens_per_step": T, "recv_rows": R, "kept_slots": kept, "used_rows": used_rows},
+        "effective_GBps": round(step_bytes / (ms_step * 1e-3) / 1e9, 1),
+        "hbm_frac": round(step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+        "fwd_dispatch_combine_tokens_per_s": round(T / (fwd_us * 1e-6), 1),
+        "ops": per_op,
+        "overflow_flags": flags,
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on the same batch")
+        host = {"R": R, "ids": d["topk_ids"], "x": d["x"], "probs": d["probs"],
+                "out": out.view(torch.int16).cpu().numpy().view(np.uint16).reshape(R, H),
+                "gy": gy.view(torch.int16).cpu().numpy().view(np.uint16).reshape(T, H),
+                "grad_recv": grad_recv.view(torch.int16).cpu().numpy().view(np.uint16).reshape(R, H)}
+        result["cpu_baseline"] = cpu_baseline(w, host)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+def capture(torch, fn):
+    """Capture fn's launches (all on the current stream) into a HIP graph."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    torch.cuda.synchronize()
+    return g
+
+
+def copy_calibration(torch, epx, dev) -> int:
+    """A plain copy of known size (1 GiB read + 1 GiB written) through the
+    dispatch kernel with identity routing: rocprofv3 FETCH_SIZE / WRITE_SIZE
+    of this launch give the counter-to-bytes scale."""
+    T, H = 65536, 8192  # 65536 rows x 16 KiB = 1 GiB
+    cfg = epx.EpConfig(num_tokens=T, hidden=H, num_experts=1, num_segments=1, top_k=1)
+    cfg.recv_rows = epx.ep_query(cfg).min_recv_rows
+    lay = epx.Layout.empty(cfg, dev)
+    ws = epx.workspace_for(cfg, dev)
+    ids = torch.zeros(T, dtype=torch.int32, device=dev)
+    x = torch.ones(T * H, dtype=torch.bfloat16, device=dev)
+    recv = torch.empty(T * H, dtype=torch.bfloat16, device=dev)
+    epx.ep_dispatch_layout(cfg, ids, ws, lay)
+    torch.cuda.synchronize()
+    assert int((lay.token_row.cpu() == torch.arange(T, dtype=torch.int32).view(T, 1)).all()) == 1
+    for _ in range(3):
+        epx.ep_dispatch(cfg, lay, x, recv)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration": {"bytes_read": T * H * 2 + T * 4, "bytes_written": T * H * 2,
+                                           "launches": 3}}), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -43,6 +43,7 @@ int derive(const ep_cfg_t* c, Shape* d) {
     d->K = c->top_k;
     d->shared = c->shared_expert;
     d->Kp = d->K + d->shared;
+    if (d->Kp > kMaxSlots) return EP_EINVAL;  // a token's slots are spread over one wave's lanes
     d->A = c->align;
     d->C = c->seg_capacity;
     d->src = d->shared ? c->src_segment : 0;

@@ -10,6 +10,7 @@
 namespace epx {
 
 constexpr int kWave = 64;
+constexpr int kMaxSlots = EP_MAX_SLOTS;  // K + shared_expert: one slot per lane
 
 // ---------------------------------------------------------------------------
 // Layout pass geometry.

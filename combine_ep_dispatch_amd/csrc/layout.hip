@@ -38,6 +38,7 @@ namespace epx {
 namespace {
 
 constexpr int kMaxSpins = 1 << 22;  // look-back gives up (EP_FLAG_INTERNAL) after this
+constexpr int kLookback = 8;        // predecessor descriptors read per round trip
 
 __device__ __forceinline__ int32_t align_up(int32_t count, int32_t multiple) {
     return ((count + multiple - 1) / multiple) * multiple;
@@ -262,21 +263,37 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout_rank(LayoutArgs a) {
         if (g >= NG) continue;
         uint32_t pref = 0;
         if (tile > 0 && s_cnt[g] > 0 && g != shared_group) {
-            for (int64_t p = (int64_t)tile - 1; p >= 0; --p) {
-                const uint32_t* dp = &a.desc[p * NG + g];
-                uint32_t d = desc_load(dp);
-                int spins = 0;
-                while ((d & ~kDescValue) == 0u) {
-                    if (++spins > kMaxSpins) {
-                        lost = EP_FLAG_INTERNAL;
-                        d = kDescInc;
-                        break;
+            // Read a window of kLookback predecessors at once (independent
+            // loads, one round trip), then fold them nearest-first until an
+            // inclusive prefix is found.  Tile 0 always publishes one, so the
+            // walk ends at or before it.
+            bool done = false;
+            for (int64_t p = (int64_t)tile - 1; !done && p >= 0; p -= kLookback) {
+                uint32_t d[kLookback];
+#pragma unroll
+                for (int i = 0; i < kLookback; ++i)
+                    d[i] = (p - i >= 0) ? desc_load(&a.desc[(p - i) * NG + g]) : kDescInc;
+#pragma unroll
+                for (int i = 0; i < kLookback; ++i) {
+                    if (done || p - i < 0) {
+                        done = true;
+                        continue;
                     }
-                    __builtin_amdgcn_s_sleep(1);
-                    d = desc_load(dp);
+                    const uint32_t* dp = &a.desc[(p - i) * NG + g];
+                    uint32_t di = d[i];
+                    int spins = 0;
+                    while ((di & ~kDescValue) == 0u) {  // not published yet
+                        if (++spins > kMaxSpins) {
+                            lost = EP_FLAG_INTERNAL;
+                            di = kDescInc;
+                            break;
+                        }
+                        __builtin_amdgcn_s_sleep(1);
+                        di = desc_load(dp);
+                    }
+                    pref += di & kDescValue;
+                    if (di & kDescInc) done = true;
                 }
-                pref += d & kDescValue;
-                if (d & kDescInc) break;
             }
             desc_store(&a.desc[(int64_t)tile * NG + g], kDescInc | (pref + (uint32_t)agg[j]));
         }

@@ -13,24 +13,56 @@
 //                    TokenDispatcherConfig.moe_router_dtype: fp32 weighting)
 //
 // All three are HBM-bound row movers.  One wave64 owns one (token, piece of
-// the hidden dimension): a piece is 64 lanes x VPL 16-byte vectors, so every
-// load and store instruction of the wave covers 1 KiB of one row,
-// contiguous.  The token index is wave-uniform, so token_row and probs come
-// in through scalar loads.  A token's x row is read once and written K'
-// times; combine issues the loads of up to 8 slots before reducing them in
-// slot order.
+// the hidden dimension): a piece is 64 lanes x VPL 16-byte vectors, so each
+// load or store instruction of the wave moves 1 KiB of one row, contiguous.
+// The token's K' receive rows (and weights) arrive with one vector load,
+// lane k holding slot k, and are broadcast to scalar registers with
+// v_readlane, so every row address is wave-uniform.  A token's x row is read
+// once and written K' times; the gather issues the loads of up to 8 slots
+// before reducing them in slot order.  When the pieces tile the row exactly
+// (H a multiple of 512 or 1024) the lane guards disappear.
 #include "epx_device.h"
+
+#ifndef EPX_SCATTER_VPL
+#define EPX_SCATTER_VPL 2
+#endif
+#ifndef EPX_GATHER_VPL
+#define EPX_GATHER_VPL 1
+#endif
+#ifndef EPX_NT_LOADS
+#define EPX_NT_LOADS 1
+#endif
+#ifndef EPX_NT_STORES
+#define EPX_NT_STORES 0
+#endif
 
 namespace epx {
 namespace {
 
 constexpr int kMoveThreads = 256;
 constexpr int kMoveWaves = kMoveThreads / kWave;
-constexpr int kVpl = 2;       // 16-byte vectors per lane per piece
 constexpr int kSlotBatch = 8;  // slots whose loads are in flight together in k_gather
 
-__device__ __forceinline__ uint4 scale_bf16x8(uint4 v, float w) {
-    uint4 o;
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ v4u load_stream(const v4u* p) {
+#if EPX_NT_LOADS
+    return __builtin_nontemporal_load(p);
+#else
+    return *p;
+#endif
+}
+
+__device__ __forceinline__ void store_stream(v4u* p, v4u v) {
+#if EPX_NT_STORES
+    __builtin_nontemporal_store(v, p);
+#else
+    *p = v;
+#endif
+}
+
+__device__ __forceinline__ v4u scale_bf16x8(v4u v, float w) {
+    v4u o;
     o.x = pack_bf16x2(w * bf16_lo(v.x), w * bf16_hi(v.x));
     o.y = pack_bf16x2(w * bf16_lo(v.y), w * bf16_hi(v.y));
     o.z = pack_bf16x2(w * bf16_lo(v.z), w * bf16_hi(v.z));
@@ -38,45 +70,64 @@ __device__ __forceinline__ uint4 scale_bf16x8(uint4 v, float w) {
     return o;
 }
 
-template <bool SCALED>
+// Slot rows of token t in lane k (k < Kp), -1 elsewhere; rows outside [0, R)
+// read as -1 so that no later address can leave the buffers.
+__device__ __forceinline__ int32_t slot_row_of_lane(const MoveArgs& a, int32_t t, int lane) {
+    int32_t r = -1;
+    if (lane < a.Kp) {
+        r = a.token_row[(int64_t)t * a.Kp + lane];
+        if (r >= a.R) r = -1;
+    }
+    return r;
+}
+
+__device__ __forceinline__ float slot_weight_of_lane(const MoveArgs& a, int32_t t, int lane) {
+    return (a.probs != nullptr && lane < a.K) ? a.probs[(int64_t)t * a.K + lane] : 1.0f;
+}
+
+template <bool SCALED, bool FULL>
 __global__ __launch_bounds__(kMoveThreads) void k_scatter(MoveArgs a, int32_t Hv, int32_t pieces) {
+    constexpr int VPL = EPX_SCATTER_VPL;
     const int32_t wave = uniform((int32_t)(blockIdx.x * kMoveWaves + threadIdx.x / kWave));
     const int32_t t = wave / pieces;
     if (t >= a.T) return;
     const int32_t piece = wave - t * pieces;
     const int lane = threadIdx.x & (kWave - 1);
-    const int32_t v0 = piece * (kWave * kVpl) + lane;
+    const int32_t v0 = piece * (kWave * VPL) + lane;
 
-    const uint4* src = static_cast<const uint4*>(a.src) + (int64_t)t * Hv;
-    uint4 buf[kVpl];
+    const int32_t my_row = slot_row_of_lane(a, t, lane);
+    const float my_w = SCALED ? slot_weight_of_lane(a, t, lane) : 1.0f;
+
+    const v4u* src = reinterpret_cast<const v4u*>(a.src) + (int64_t)t * Hv;
+    v4u buf[VPL];
 #pragma unroll
-    for (int i = 0; i < kVpl; ++i) {
+    for (int i = 0; i < VPL; ++i) {
         const int32_t v = v0 + i * kWave;
-        buf[i] = v < Hv ? src[v] : make_uint4(0, 0, 0, 0);
+        if (FULL || v < Hv) buf[i] = load_stream(src + v);
+        else buf[i] = v4u{0, 0, 0, 0};
     }
-    const int32_t* tr = a.token_row + (int64_t)t * a.Kp;
     for (int32_t k = 0; k < a.Kp; ++k) {
-        const int32_t row = tr[k];
-        if (row < 0 || row >= a.R) continue;
-        uint4* dst = static_cast<uint4*>(a.dst) + (int64_t)row * Hv;
+        const int32_t row = __builtin_amdgcn_readlane(my_row, k);
+        if (row < 0) continue;
+        v4u* dst = reinterpret_cast<v4u*>(a.dst) + (int64_t)row * Hv;
         if (SCALED) {
-            const float w = (a.probs != nullptr && k < a.K) ? a.probs[(int64_t)t * a.K + k] : 1.0f;
+            const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_w), k));
 #pragma unroll
-            for (int i = 0; i < kVpl; ++i) {
+            for (int i = 0; i < VPL; ++i) {
                 const int32_t v = v0 + i * kWave;
-                if (v < Hv) dst[v] = scale_bf16x8(buf[i], w);
+                if (FULL || v < Hv) store_stream(dst + v, scale_bf16x8(buf[i], w));
             }
         } else {
 #pragma unroll
-            for (int i = 0; i < kVpl; ++i) {
+            for (int i = 0; i < VPL; ++i) {
                 const int32_t v = v0 + i * kWave;
-                if (v < Hv) dst[v] = buf[i];
+                if (FULL || v < Hv) store_stream(dst + v, buf[i]);
             }
         }
     }
 }
 
-__device__ __forceinline__ void accumulate(float (&acc)[8], uint4 v, float w, bool weighted) {
+__device__ __forceinline__ void accumulate(float (&acc)[8], v4u v, float w, bool weighted) {
     const uint32_t q[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -92,77 +143,100 @@ __device__ __forceinline__ void accumulate(float (&acc)[8], uint4 v, float w, bo
     }
 }
 
-template <bool WEIGHTED>
+template <bool WEIGHTED, bool FULL>
 __global__ __launch_bounds__(kMoveThreads) void k_gather(MoveArgs a, int32_t Hv, int32_t pieces) {
+    constexpr int VPL = EPX_GATHER_VPL;
     const int32_t wave = uniform((int32_t)(blockIdx.x * kMoveWaves + threadIdx.x / kWave));
     const int32_t t = wave / pieces;
     if (t >= a.T) return;
     const int32_t piece = wave - t * pieces;
     const int lane = threadIdx.x & (kWave - 1);
-    const int32_t v0 = piece * (kWave * kVpl) + lane;
-    const int32_t* tr = a.token_row + (int64_t)t * a.Kp;
-    const uint4* src = static_cast<const uint4*>(a.src);
+    const int32_t v0 = piece * (kWave * VPL) + lane;
+    const v4u* src = reinterpret_cast<const v4u*>(a.src);
 
-    float acc[kVpl][8];
+    const int32_t my_row = slot_row_of_lane(a, t, lane);
+    const float my_w = WEIGHTED ? slot_weight_of_lane(a, t, lane) : 1.0f;
+
+    float acc[VPL][8];
 #pragma unroll
-    for (int i = 0; i < kVpl; ++i)
+    for (int i = 0; i < VPL; ++i)
 #pragma unroll
         for (int j = 0; j < 8; ++j) acc[i][j] = 0.0f;
 
     for (int32_t k0 = 0; k0 < a.Kp; k0 += kSlotBatch) {
         int32_t rows[kSlotBatch];
-        float wts[kSlotBatch];
-        uint4 buf[kSlotBatch][kVpl];
+        v4u buf[kSlotBatch][VPL];
 #pragma unroll
         for (int kk = 0; kk < kSlotBatch; ++kk) {
             const int32_t k = k0 + kk;
-            const int32_t r = k < a.Kp ? tr[k] : -1;
-            rows[kk] = r < a.R ? r : -1;
-            wts[kk] = (WEIGHTED && k < a.K) ? a.probs[(int64_t)t * a.K + (k < a.K ? k : 0)] : 1.0f;
-        }
+            rows[kk] = k < a.Kp ? __builtin_amdgcn_readlane(my_row, k) : -1;
+            const v4u* r = src + (int64_t)(rows[kk] < 0 ? 0 : rows[kk]) * Hv;
 #pragma unroll
-        for (int kk = 0; kk < kSlotBatch; ++kk) {
-            const uint4* r = src + (int64_t)(rows[kk] < 0 ? 0 : rows[kk]) * Hv;
-#pragma unroll
-            for (int i = 0; i < kVpl; ++i) {
+            for (int i = 0; i < VPL; ++i) {
                 const int32_t v = v0 + i * kWave;
-                buf[kk][i] = (rows[kk] >= 0 && v < Hv) ? r[v] : make_uint4(0, 0, 0, 0);
+                buf[kk][i] = (rows[kk] >= 0 && (FULL || v < Hv)) ? load_stream(r + v) : v4u{0, 0, 0, 0};
             }
         }
 #pragma unroll
         for (int kk = 0; kk < kSlotBatch; ++kk) {
             if (rows[kk] < 0) continue;  // masked or dropped: contributes nothing
+            const float w =
+                WEIGHTED ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_w), k0 + kk)) : 1.0f;
 #pragma unroll
-            for (int i = 0; i < kVpl; ++i) accumulate(acc[i], buf[kk][i], wts[kk], WEIGHTED);
+            for (int i = 0; i < VPL; ++i) accumulate(acc[i], buf[kk][i], w, WEIGHTED);
         }
     }
-    uint4* dst = static_cast<uint4*>(a.dst) + (int64_t)t * Hv;
+    v4u* dst = reinterpret_cast<v4u*>(a.dst) + (int64_t)t * Hv;
 #pragma unroll
-    for (int i = 0; i < kVpl; ++i) {
+    for (int i = 0; i < VPL; ++i) {
         const int32_t v = v0 + i * kWave;
-        if (v < Hv) {
-            uint4 o;
+        if (FULL || v < Hv) {
+            v4u o;
             o.x = pack_bf16x2(acc[i][0], acc[i][1]);
             o.y = pack_bf16x2(acc[i][2], acc[i][3]);
             o.z = pack_bf16x2(acc[i][4], acc[i][5]);
             o.w = pack_bf16x2(acc[i][6], acc[i][7]);
-            dst[v] = o;
+            store_stream(dst + v, o);
         }
     }
 }
 
 struct Grid {
     int32_t Hv, pieces;
+    bool full;
     dim3 blocks;
 };
 
-Grid move_grid(const MoveArgs& a) {
+Grid move_grid(const MoveArgs& a, int vpl) {
     Grid g;
     g.Hv = a.H / 8;
-    g.pieces = (g.Hv + kWave * kVpl - 1) / (kWave * kVpl);
+    const int per_piece = kWave * vpl;
+    g.pieces = (g.Hv + per_piece - 1) / per_piece;
+    g.full = g.Hv % per_piece == 0;
     const int64_t waves = (int64_t)a.T * g.pieces;
     g.blocks = dim3((unsigned)((waves + kMoveWaves - 1) / kMoveWaves));
     return g;
+}
+
+template <bool SCALED>
+hipError_t scatter(const MoveArgs& a, hipStream_t stream) {
+    if (a.T == 0) return hipSuccess;
+    const Grid g = move_grid(a, EPX_SCATTER_VPL);
+    if (g.full)
+        hipLaunchKernelGGL((k_scatter<SCALED, true>), g.blocks, dim3(kMoveThreads), 0, stream, a, g.Hv, g.pieces);
+    else
+        hipLaunchKernelGGL((k_scatter<SCALED, false>), g.blocks, dim3(kMoveThreads), 0, stream, a, g.Hv, g.pieces);
+    return hipGetLastError();
+}
+
+template <bool WEIGHTED>
+hipError_t gather(const MoveArgs& a, hipStream_t stream) {
+    const Grid g = move_grid(a, EPX_GATHER_VPL);
+    if (g.full)
+        hipLaunchKernelGGL((k_gather<WEIGHTED, true>), g.blocks, dim3(kMoveThreads), 0, stream, a, g.Hv, g.pieces);
+    else
+        hipLaunchKernelGGL((k_gather<WEIGHTED, false>), g.blocks, dim3(kMoveThreads), 0, stream, a, g.Hv, g.pieces);
+    return hipGetLastError();
 }
 
 // Zero the byte range [b0, b1) of `base` with 16-byte stores where aligned.
@@ -191,7 +265,6 @@ __global__ __launch_bounds__(256) void k_zero_pad_rows(uint8_t* base, int64_t ro
         if (first > C) first = C;
         if (last > C) last = C;
     }
-    if (first >= last) return;
     int64_t r0 = (int64_t)L.seg_base[s] + first, r1 = (int64_t)L.seg_base[s] + last;
     if (r0 < 0) r0 = 0;
     if (r1 > R) r1 = R;  // never past the buffer, whatever the layout holds
@@ -201,28 +274,13 @@ __global__ __launch_bounds__(256) void k_zero_pad_rows(uint8_t* base, int64_t ro
 
 }  // namespace
 
-hipError_t launch_scatter(const MoveArgs& a, hipStream_t stream) {
-    if (a.T == 0) return hipSuccess;
-    const Grid g = move_grid(a);
-    hipLaunchKernelGGL(k_scatter<false>, g.blocks, dim3(kMoveThreads), 0, stream, a, g.Hv, g.pieces);
-    return hipGetLastError();
-}
+hipError_t launch_scatter(const MoveArgs& a, hipStream_t stream) { return scatter<false>(a, stream); }
+
+hipError_t launch_scatter_scaled(const MoveArgs& a, hipStream_t stream) { return scatter<true>(a, stream); }
 
 hipError_t launch_gather_reduce(const MoveArgs& a, hipStream_t stream) {
     if (a.T == 0) return hipSuccess;
-    const Grid g = move_grid(a);
-    if (a.probs != nullptr)
-        hipLaunchKernelGGL(k_gather<true>, g.blocks, dim3(kMoveThreads), 0, stream, a, g.Hv, g.pieces);
-    else
-        hipLaunchKernelGGL(k_gather<false>, g.blocks, dim3(kMoveThreads), 0, stream, a, g.Hv, g.pieces);
-    return hipGetLastError();
-}
-
-hipError_t launch_scatter_scaled(const MoveArgs& a, hipStream_t stream) {
-    if (a.T == 0) return hipSuccess;
-    const Grid g = move_grid(a);
-    hipLaunchKernelGGL(k_scatter<true>, g.blocks, dim3(kMoveThreads), 0, stream, a, g.Hv, g.pieces);
-    return hipGetLastError();
+    return a.probs != nullptr ? gather<true>(a, stream) : gather<false>(a, stream);
 }
 
 hipError_t launch_zero_pad_rows(void* base, int64_t row_bytes, const ep_layout_t& L, int32_t S, int32_t G,

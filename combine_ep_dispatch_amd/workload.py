@@ -59,9 +59,18 @@ class Workload:
     outlier_scale: float = 1.0
     seed: int = 0
 
+    capacity_factor: float = 0.0  # > 0: capacity = factor x mean segment load (recomputed per T)
+
     @property
     def Kp(self) -> int:
         return self.K + self.shared_expert
+
+    def at_tokens(self, T: int) -> "Workload":
+        """The same recipe with T tokens (capacity recomputed from its factor)."""
+        cap = self.capacity
+        if self.capacity_factor > 0:
+            cap = _capacity_rows(T, self.K, self.S, self.capacity_factor, 4)
+        return dataclasses.replace(self, T=T, capacity=cap)
 
 
 def _capacity_rows(T: int, K: int, S: int, factor: float, multiple: int) -> int:
@@ -86,7 +95,7 @@ CONFIGS = {
                       shared_expert=1, src_segment=0,
                       outlier_frac=0.01, outlier_scale=50.0),
     "capacity": Workload("capacity", T=16384, H=2048, E=64, S=4, K=6, align=1,
-                         capacity=_capacity_rows(16384, 6, 4, 1.1, 4),
+                         capacity=_capacity_rows(16384, 6, 4, 1.1, 4), capacity_factor=1.1,
                          routing="zipf", zipf_s=1.5),
 }
 

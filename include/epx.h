@@ -67,6 +67,8 @@ extern "C" {
 
 /* Largest number of groups S * (E/S + shared_expert) a layout may have. */
 #define EP_MAX_GROUPS 2048
+/* Largest number of slots per token, K + shared_expert. */
+#define EP_MAX_SLOTS 64
 
 /*
  * Problem description.  Field names follow the pages' statement of the
@@ -84,7 +86,7 @@ typedef struct ep_cfg_t {
     int32_t hidden;        /* H >= 8, multiple of 8 (bf16 calls) or 16 (NVFP4)     */
     int32_t num_experts;   /* E >= 1 routed experts                               */
     int32_t num_segments;  /* S >= 1 destination segments, E % S == 0             */
-    int32_t top_k;         /* K, 1 <= K <= E                                      */
+    int32_t top_k;         /* K, 1 <= K <= E, K + shared_expert <= EP_MAX_SLOTS  */
     int32_t align;         /* A >= 1: each group's rows are padded to a multiple  */
     int32_t seg_capacity;  /* C >= 0: 0 = packed segments; > 0 = C rows per
                               segment, slots past it are dropped and flagged      */

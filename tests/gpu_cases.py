@@ -104,11 +104,12 @@ def assert_bits_equal(gpu: np.ndarray, ora: np.ndarray, name: str):
 
 def assert_close_bf16(gpu_bits: np.ndarray, ora_bits: np.ndarray, name: str):
     """The combine tolerance: |gpu - oracle| <= 1e-2 + 2e-2 |oracle| element-wise."""
-    g, o = f32(gpu_bits).astype(np.float64), f32(ora_bits).astype(np.float64)
+    g = f32(gpu_bits).astype(np.float64).reshape(-1)
+    o = f32(ora_bits).astype(np.float64).reshape(-1)
     err = np.abs(g - o)
     ok = err <= 1e-2 + 2e-2 * np.abs(o)
     if not ok.all():
-        bad = np.nonzero(~ok.reshape(-1))[0]
+        bad = np.nonzero(~ok)[0]
         raise AssertionError(f"{name}: {bad.size} elements outside tolerance, max err {err.max()}")
 
 
@@ -173,8 +174,10 @@ def random_case(seed: int, **over) -> Case:
 
 def workload_case(name: str, T=None) -> Case:
     w = wl.CONFIGS[name]
-    d = wl.make_workload(w, T=T)
-    cfg = cfg_of(w, T=T)
+    if T is not None:
+        w = w.at_tokens(T)
+    d = wl.make_workload(w)
+    cfg = cfg_of(w)
     return Case(cfg, d["topk_ids"], d["probs"], d["x"], seed=7)
 
 

@@ -206,3 +206,72 @@ def test_combine_of_dispatch_is_identity_on_gpu(G):
         torch.cuda.synchronize()
         want = c.x if not cfg.shared_expert else G.wl.bf16_bits(2.0 * G.f32(c.x))
         assert np.array_equal(G.bits_of(y).reshape(cfg.num_tokens, -1), want), name
+
+
+def test_graph_replays_match_eager(G):
+    """The whole step captured into a HIP graph: every replay (with eager
+    work and output clearing in between) reproduces the eager results and
+    the oracle's layout."""
+    c = G.workload_case("nvfp4", T=1024)
+    cfg = c.cfg
+    epx, DEV = G.epx, G.DEV
+    R, T, H = cfg.recv_rows, cfg.num_tokens, cfg.hidden
+    ids = torch.from_numpy(c.ids.reshape(-1)).to(DEV)
+    x = G.u16_tensor(c.x)
+    probs = torch.from_numpy(c.probs.reshape(-1)).to(DEV)
+    out = G.u16_tensor(c.rows(1))
+    lay = epx.Layout.empty(cfg, DEV)
+    ws = epx.workspace_for(cfg, DEV)
+    bufs = {"recv": torch.empty(R * H, dtype=torch.bfloat16, device=DEV),
+            "codes": torch.empty(R * H // 2, dtype=torch.uint8, device=DEV),
+            "scales": torch.empty(R * H // 16, dtype=torch.uint8, device=DEV),
+            "rowscale": torch.empty(R, dtype=torch.bfloat16, device=DEV),
+            "y": torch.empty(T * H, dtype=torch.bfloat16, device=DEV),
+            "gout": torch.empty(R * H, dtype=torch.bfloat16, device=DEV),
+            "gx": torch.empty(T * H, dtype=torch.bfloat16, device=DEV)}
+
+    def step():
+        epx.ep_dispatch_layout(cfg, ids, ws, lay)
+        epx.ep_dispatch(cfg, lay, x, bufs["recv"])
+        epx.ep_dispatch_nvfp4(cfg, lay, x, bufs["codes"], bufs["scales"], bufs["rowscale"])
+        epx.ep_combine(cfg, lay, out, probs, bufs["y"])
+        epx.ep_combine_bwd(cfg, lay, bufs["y"], probs, bufs["gout"])
+        epx.ep_dispatch_bwd(cfg, lay, out, bufs["gx"])
+
+    def clear():
+        for t in list(bufs.values()) + [lay.token_row, lay.expert_ids, lay.src_info, lay.counts, lay.flags]:
+            t.view(torch.uint8).fill_(0x5A)
+
+    clear()
+    step()
+    torch.cuda.synchronize()
+    ref = {k: v.clone() for k, v in bufs.items()}
+    ref_tr = lay.token_row.clone()
+    assert np.array_equal(ref_tr.cpu().numpy(), c.L["token_row"])
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    other = G.random_case(3, T=200, H=256)
+    for i in range(4):
+        clear()
+        torch.cuda.synchronize()
+        G.check_layout(other, f"eager between replays {i}")  # unrelated eager work
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(lay.token_row, ref_tr), i
+        for k, v in bufs.items():
+            if k in ("recv", "codes", "scales", "rowscale", "gout"):
+                # only the used rows are defined
+                used = torch.from_numpy(np.unique(c.L["token_row"][c.L["token_row"] >= 0])).to(DEV).long()
+                a, b = v.view(R, -1)[used], ref[k].view(R, -1)[used]
+            else:
+                a, b = v, ref[k]
+            assert torch.equal(a, b), (i, k)
