@@ -169,7 +169,6 @@ int ep_dispatch_layout(const ep_cfg_t* cfg, const int32_t* topk_ids, void* works
 
     LayoutArgs a;
     a.topk_ids = topk_ids;
-    a.ticket = static_cast<uint32_t*>(workspace);
     a.desc = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(workspace) + kWorkspaceHeader);
     a.out = *L;
     a.T = d.T;
@@ -186,6 +185,7 @@ int ep_dispatch_layout(const ep_cfg_t* cfg, const int32_t* topk_ids, void* works
     a.src_seg = d.src;
     a.recv_rows = d.R;
     a.tiles = (int32_t)d.tiles;
+    a.slots_per_thread = layout_slots_per_thread((int64_t)d.T * d.K);
     return status_of(launch_layout(a, static_cast<hipStream_t>(stream)));
 }
 

@@ -17,20 +17,27 @@ constexpr int kMaxSlots = EP_MAX_SLOTS;  // K + shared_expert: one slot per lane
 // ---------------------------------------------------------------------------
 constexpr int kLayoutThreads = 256;                      // 4 waves
 constexpr int kLayoutWaves = kLayoutThreads / kWave;
-constexpr int kSlotsPerThread = 8;
-constexpr int kTileSlots = kLayoutThreads * kSlotsPerThread;  // routed slots per tile
-constexpr int kSlotsPerWave = kTileSlots / kLayoutWaves;      // contiguous per wave
-constexpr int kWorkspaceHeader = 256;                    // ticket + padding
+constexpr int kWorkspaceHeader = 256;                    // reserved header before the descriptors
+constexpr int kTargetTiles = 64;                         // tiles aimed for by the tile-size choice
+
+// Routed slots per thread in one layout tile (2, 4 or 8): the smallest that
+// keeps the number of tiles near kTargetTiles, so that short inputs get more
+// workgroups and long ones a short look-back.
+inline int layout_slots_per_thread(int64_t routed_slots) {
+    const int64_t per = (routed_slots + (int64_t)kLayoutThreads * kTargetTiles - 1) /
+                        ((int64_t)kLayoutThreads * kTargetTiles);
+    return per <= 2 ? 2 : (per <= 4 ? 4 : 8);
+}
+inline int64_t layout_tiles(int64_t routed_slots) {
+    const int64_t tile = (int64_t)kLayoutThreads * layout_slots_per_thread(routed_slots);
+    const int64_t nt = (routed_slots + tile - 1) / tile;
+    return nt < 1 ? 1 : nt;
+}
 
 // Look-back descriptor: 2 status bits over a 30-bit count.
 constexpr uint32_t kDescAgg = 1u << 30;   // tile aggregate only
 constexpr uint32_t kDescInc = 2u << 30;   // inclusive prefix through this tile
 constexpr uint32_t kDescValue = (1u << 30) - 1;
-
-inline int64_t layout_tiles(int64_t routed_slots) {
-    int64_t nt = (routed_slots + kTileSlots - 1) / kTileSlots;
-    return nt < 1 ? 1 : nt;
-}
 
 // ---------------------------------------------------------------------------
 // Number helpers (bit-exact definitions, no fused multiply-add anywhere: the
@@ -80,12 +87,12 @@ __device__ __forceinline__ T uniform(T v) {
 // ---------------------------------------------------------------------------
 struct LayoutArgs {
     const int32_t* topk_ids;
-    uint32_t* ticket;
-    uint32_t* desc;
+    uint32_t* desc;  // [tiles][NG] look-back descriptors
     ep_layout_t out;
     int32_t T, K, Kp, E, S, G, NG, E_loc, A, C, shared, src_seg;
     int64_t recv_rows;
     int32_t tiles;
+    int32_t slots_per_thread;  // 2, 4 or 8 (layout_slots_per_thread)
 };
 hipError_t launch_layout(const LayoutArgs& a, hipStream_t stream);
 

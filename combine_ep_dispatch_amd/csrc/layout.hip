@@ -14,51 +14,59 @@
 //    coordinating work across thread blocks.
 //
 // Three launches on the caller's stream:
-//  1. k_layout_clear  zero the counts (the shared group gets T), the flags
-//                     word, the tile ticket and the look-back descriptors.
-//  2. k_layout_hist   per tile of 2048 routed slots, a wave64 match-any over
+//  1. k_layout_clear  zero the counts (the shared group gets T) and the flags
+//                     word.
+//  2. k_layout_hist   per tile of 256 x {2,4,8} routed slots (chosen so that
+//                     there are about 64 tiles), a wave64 match-any over
 //                     the group key (one ballot per key bit); the lowest lane
 //                     of each match set adds the set's popcount into an LDS
 //                     counter, so a hot expert costs one LDS atomic per wave
-//                     instead of one per slot.  Tiles add their nonzero
-//                     counters into `counts`.
+//                     instead of one per slot.  Each tile publishes its
+//                     per-group aggregate as a look-back descriptor (tile 0
+//                     publishes its inclusive prefix directly) and adds its
+//                     nonzero counters into `counts`.
 //  3. k_layout_rank   single pass: every workgroup scans the aligned group
 //                     sizes (from the finished counts) into group start
-//                     rows, takes a tile from an atomic ticket (so it only
-//                     ever waits on tiles that already started), ranks its
-//                     slots inside their groups (per-wave running counters in
-//                     LDS + match-any), publishes its per-group aggregate,
-//                     then resolves its per-group prefix over earlier tiles
-//                     by decoupled look-back and writes token_row,
-//                     expert_ids and src_info.  Pad-row metadata and the
-//                     fused shared-expert rows are spread over the tiles.
+//                     rows, ranks its tile's slots inside their groups
+//                     (per-wave running counters in LDS + match-any),
+//                     resolves its per-group prefix over earlier tiles by
+//                     decoupled look-back (16 predecessor descriptors per
+//                     round trip, folded nearest-first until an inclusive
+//                     prefix is met), upgrades its own descriptors to
+//                     inclusive prefixes for the tiles after it, and writes
+//                     token_row, expert_ids and src_info.  Pad-row metadata
+//                     and the fused shared-expert rows are spread over the
+//                     tiles.  Every aggregate is published by the previous
+//                     launch, so no workgroup ever waits on another one and
+//                     tiles need no ordering ticket.
 #include "epx_device.h"
 
 namespace epx {
 namespace {
 
 constexpr int kMaxSpins = 1 << 22;  // look-back gives up (EP_FLAG_INTERNAL) after this
-constexpr int kLookback = 8;        // predecessor descriptors read per round trip
+constexpr int kLookback = 16;       // predecessor descriptors read per round trip
 
 __device__ __forceinline__ int32_t align_up(int32_t count, int32_t multiple) {
     return ((count + multiple - 1) / multiple) * multiple;
 }
 
-__global__ __launch_bounds__(256) void k_layout_clear(LayoutArgs a) {
-    const int64_t ndesc = (int64_t)a.tiles * a.NG;
-    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    const int64_t i0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    for (int64_t i = i0; i < ndesc; i += stride) a.desc[i] = 0u;
-    const int32_t shared_group = a.shared ? a.src_seg * a.G : -1;
-    for (int64_t g = i0; g < a.NG; g += stride)
-        a.out.counts[g] = (g == shared_group) ? a.T : 0;
-    if (i0 == 0) {
-        a.out.flags[0] = 0;
-        a.ticket[0] = 0u;
-    }
+__device__ __forceinline__ uint32_t desc_load(const uint32_t* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void desc_store(uint32_t* p, uint32_t v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+__global__ __launch_bounds__(256) void k_layout_clear(LayoutArgs a) {
+    const int32_t shared_group = a.shared ? a.src_seg * a.G : -1;
+    for (int g = threadIdx.x; g < a.NG; g += blockDim.x) a.out.counts[g] = (g == shared_group) ? a.T : 0;
+    if (threadIdx.x == 0) a.out.flags[0] = 0;
+}
+
+template <int SPT>
 __global__ __launch_bounds__(kLayoutThreads) void k_layout_hist(LayoutArgs a) {
+    constexpr int kTileSlots = kLayoutThreads * SPT;
     __shared__ int32_t s_hist[EP_MAX_GROUPS];
     __shared__ int32_t s_gof[EP_MAX_GROUPS];  // group of each routed expert
     __shared__ int32_t s_bad;
@@ -74,7 +82,7 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout_hist(LayoutArgs a) {
     const int64_t base = (int64_t)blockIdx.x * kTileSlots;
     bool bad = false;
 #pragma unroll
-    for (int it = 0; it < kSlotsPerThread; ++it) {
+    for (int it = 0; it < SPT; ++it) {
         const int64_t f = base + it * kLayoutThreads + tid;
         uint32_t key = (uint32_t)a.NG;
         if (f < routed) {
@@ -88,21 +96,20 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout_hist(LayoutArgs a) {
     }
     if (bad) s_bad = 1;
     __syncthreads();
+    const uint32_t status = blockIdx.x == 0 ? kDescInc : kDescAgg;  // tile 0: prefix 0 + aggregate
+    uint32_t* desc = a.desc + (int64_t)blockIdx.x * a.NG;
     for (int g = tid; g < a.NG; g += kLayoutThreads) {
         const int32_t c = s_hist[g];
+        desc_store(&desc[g], status | (uint32_t)c);
         if (c) atomicAdd(&a.out.counts[g], c);
     }
     if (tid == 0 && s_bad) atomicOr(a.out.flags, EP_FLAG_BAD_ID);
 }
 
-__device__ __forceinline__ uint32_t desc_load(const uint32_t* p) {
-    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void desc_store(uint32_t* p, uint32_t v) {
-    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
+template <int SPT>
 __global__ __launch_bounds__(kLayoutThreads) void k_layout_rank(LayoutArgs a) {
+    constexpr int kTileSlots = kLayoutThreads * SPT;
+    constexpr int kSlotsPerWave = kWave * SPT;
     __shared__ int32_t s_cnt[EP_MAX_GROUPS];    // group totals
     __shared__ int32_t s_start[EP_MAX_GROUPS];  // first row of the group (clamped at capacity)
     __shared__ int32_t s_lim[EP_MAX_GROUPS];    // first row past the segment's capacity
@@ -110,22 +117,28 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout_rank(LayoutArgs a) {
     __shared__ int32_t s_gof[EP_MAX_GROUPS];    // group of each routed expert
     __shared__ uint16_t s_wcnt[kLayoutWaves][EP_MAX_GROUPS];  // per-wave counts / prefixes
     __shared__ int32_t s_wsum[kLayoutWaves];
-    __shared__ uint32_t s_tile;
     __shared__ int32_t s_flag;
 
     const int tid = threadIdx.x, lane = tid & (kWave - 1), w = tid / kWave;
     const int NG = a.NG, G = a.G;
-    if (tid == 0) {
-        s_tile = atomicAdd(a.ticket, 1u);
-        s_flag = 0;
+    const uint32_t tile = blockIdx.x;
+    // This tile's routed slots: wave w owns [w*64*SPT, (w+1)*64*SPT), in SPT
+    // rounds of 64.  The ids are fetched first so their latency hides behind the
+    // offset scan.
+    const int64_t routed = (int64_t)a.T * a.K;
+    const int64_t wslot0 = (int64_t)tile * kTileSlots + (int64_t)w * kSlotsPerWave;
+    int32_t eid[SPT];
+#pragma unroll
+    for (int it = 0; it < SPT; ++it) {
+        const int64_t f = wslot0 + it * kWave + lane;
+        eid[it] = f < routed ? a.topk_ids[f] : -1;
     }
+    if (tid == 0) s_flag = 0;
     for (int g = tid; g < NG; g += kLayoutThreads) s_cnt[g] = a.out.counts[g];
     for (int e = tid; e < a.E; e += kLayoutThreads)
         s_gof[e] = (e / a.E_loc) * G + a.shared + (e % a.E_loc);
-    for (int i = tid; i < kLayoutWaves * EP_MAX_GROUPS; i += kLayoutThreads)
-        (&s_wcnt[0][0])[i] = 0;
+    for (int i = tid; i < kLayoutWaves * NG; i += kLayoutThreads) s_wcnt[i / NG][i % NG] = 0;
     __syncthreads();
-    const uint32_t tile = s_tile;
 
     // ---- aligned exclusive prefix P over all groups (segment-major) ----
     // Thread i covers groups [8i, 8i + 8); NG <= 2048 = 256 * 8.
@@ -207,21 +220,13 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout_rank(LayoutArgs a) {
         }
     }
 
-    // ---- in-tile ranks: wave w owns slots [w*512, w*512 + 512) of the tile ----
-    const int64_t routed = (int64_t)a.T * a.K;
+    // ---- in-tile ranks (per-wave running counters + match-any) ----
     const int nbits = 32 - __clz(NG);
-    const int64_t wslot0 = (int64_t)tile * kTileSlots + (int64_t)w * kSlotsPerWave;
-    uint32_t key[kSlotsPerThread], rnk[kSlotsPerThread];
-    int32_t eid[kSlotsPerThread];
+    uint32_t key[SPT], rnk[SPT];
 #pragma unroll
-    for (int it = 0; it < kSlotsPerThread; ++it) {
-        const int64_t f = wslot0 + it * kWave + lane;
-        uint32_t k = (uint32_t)NG;
-        int32_t e = -1;
-        if (f < routed) {
-            e = a.topk_ids[f];
-            if ((uint32_t)e < (uint32_t)a.E) k = (uint32_t)s_gof[e];
-        }
+    for (int it = 0; it < SPT; ++it) {
+        const int32_t e = eid[it];
+        const uint32_t k = (uint32_t)e < (uint32_t)a.E ? (uint32_t)s_gof[e] : (uint32_t)NG;
         const uint64_t m = match_any(k, nbits);
         const uint32_t r = lanes_below(m);
         rnk[it] = 0;
@@ -231,7 +236,6 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout_rank(LayoutArgs a) {
             if (r == 0) s_wcnt[w][k] = (uint16_t)(before + (uint32_t)__popcll(m));
         }
         key[it] = k;
-        eid[it] = e;
     }
     __syncthreads();
 
@@ -251,8 +255,6 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout_rank(LayoutArgs a) {
                 run += c;
             }
             agg[j] = run;
-            if (s_cnt[g] > 0 && g != shared_group)
-                desc_store(&a.desc[(int64_t)tile * NG + g], (tile == 0 ? kDescInc : kDescAgg) | (uint32_t)run);
         }
     }
     // ---- decoupled look-back over earlier tiles ----
@@ -265,8 +267,10 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout_rank(LayoutArgs a) {
         if (tile > 0 && s_cnt[g] > 0 && g != shared_group) {
             // Read a window of kLookback predecessors at once (independent
             // loads, one round trip), then fold them nearest-first until an
-            // inclusive prefix is found.  Tile 0 always publishes one, so the
-            // walk ends at or before it.
+            // inclusive prefix is found.  Tile 0's descriptor is inclusive
+            // from the start, so the walk ends at or before it.  Every
+            // descriptor was published by the histogram launch; the wait
+            // below is only a guard and gives up after kMaxSpins polls.
             bool done = false;
             for (int64_t p = (int64_t)tile - 1; !done && p >= 0; p -= kLookback) {
                 uint32_t d[kLookback];
@@ -305,7 +309,7 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout_rank(LayoutArgs a) {
     int32_t flag = lost;
     const uint32_t R = (uint32_t)a.recv_rows;
 #pragma unroll
-    for (int it = 0; it < kSlotsPerThread; ++it) {
+    for (int it = 0; it < SPT; ++it) {
         const int64_t f = wslot0 + it * kWave + lane;
         if (f >= routed) continue;
         const uint32_t t = (uint32_t)f / (uint32_t)a.K, k = (uint32_t)f - t * (uint32_t)a.K;
@@ -381,13 +385,22 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout_rank(LayoutArgs a) {
 }  // namespace
 
 hipError_t launch_layout(const LayoutArgs& a, hipStream_t stream) {
-    const int64_t nclear = (int64_t)a.tiles * a.NG > a.NG ? (int64_t)a.tiles * a.NG : a.NG;
-    int64_t cblocks = (nclear + 255) / 256;
-    if (cblocks > 1024) cblocks = 1024;
-    if (cblocks < 1) cblocks = 1;
-    hipLaunchKernelGGL(k_layout_clear, dim3((unsigned)cblocks), dim3(256), 0, stream, a);
-    hipLaunchKernelGGL(k_layout_hist, dim3((unsigned)a.tiles), dim3(kLayoutThreads), 0, stream, a);
-    hipLaunchKernelGGL(k_layout_rank, dim3((unsigned)a.tiles), dim3(kLayoutThreads), 0, stream, a);
+    hipLaunchKernelGGL(k_layout_clear, dim3(1), dim3(256), 0, stream, a);
+    const dim3 grid((unsigned)a.tiles), block(kLayoutThreads);
+    switch (a.slots_per_thread) {
+        case 2:
+            hipLaunchKernelGGL(k_layout_hist<2>, grid, block, 0, stream, a);
+            hipLaunchKernelGGL(k_layout_rank<2>, grid, block, 0, stream, a);
+            break;
+        case 4:
+            hipLaunchKernelGGL(k_layout_hist<4>, grid, block, 0, stream, a);
+            hipLaunchKernelGGL(k_layout_rank<4>, grid, block, 0, stream, a);
+            break;
+        default:
+            hipLaunchKernelGGL(k_layout_hist<8>, grid, block, 0, stream, a);
+            hipLaunchKernelGGL(k_layout_rank<8>, grid, block, 0, stream, a);
+            break;
+    }
     return hipGetLastError();
 }
 

@@ -81,7 +81,10 @@ def test_query_sizes(L, orc):
                      A=c.align, C=c.seg_capacity, shared=c.shared_expert, src_seg=c.src_segment)
         assert rows == orc.min_recv_rows(oc)
         assert g == c.num_experts // c.num_segments + c.shared_expert
-        tiles = max(1, -(-c.num_tokens * c.top_k // 2048))
+        routed = c.num_tokens * c.top_k
+        per = -(-routed // (256 * 64))  # tiles of 256 x {2,4,8} slots, about 64 of them
+        spt = 2 if per <= 2 else (4 if per <= 4 else 8)
+        tiles = max(1, -(-routed // (256 * spt)))
         assert ws == 256 + tiles * c.num_segments * g * 4
     # the bound is reached by some routing and never exceeded (oracle layout)
     rng = np.random.default_rng(0)

@@ -90,6 +90,8 @@ EDGE = {
     "big_align": dict(T=300, A=256, S=3, E_loc=3, K=2),
     "many_tiles": dict(T=9000, S=4, E_loc=16, K=8, A=16, H=16),
     "hot_expert": dict(T=4000, S=2, E_loc=1, K=1, H=32, A=8),
+    "tile4_ragged": dict(T=5001, S=8, E_loc=8, K=8, H=16, A=4),          # 4 slots/thread tiles
+    "tile8_long_lookback": dict(T=20011, S=4, E_loc=16, K=8, H=16, A=2),  # 8 slots/thread, 79 tiles
 }
 
 
