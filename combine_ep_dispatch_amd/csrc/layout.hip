@@ -30,7 +30,7 @@
 //                     rows, ranks its tile's slots inside their groups
 //                     (per-wave running counters in LDS + match-any),
 //                     resolves its per-group prefix over earlier tiles by
-//                     decoupled look-back (16 predecessor descriptors per
+//                     decoupled look-back (64 predecessor descriptors per
 //                     round trip, folded nearest-first until an inclusive
 //                     prefix is met), upgrades its own descriptors to
 //                     inclusive prefixes for the tiles after it, and writes
@@ -45,9 +45,10 @@ namespace epx {
 namespace {
 
 constexpr int kMaxSpins = 1 << 22;  // look-back gives up (EP_FLAG_INTERNAL) after this
-constexpr int kLookback = 16;       // predecessor descriptors read per round trip
+constexpr int kLookback = 64;       // predecessor descriptors read per round trip
 
 __device__ __forceinline__ int32_t align_up(int32_t count, int32_t multiple) {
+    if ((multiple & (multiple - 1)) == 0) return (count + multiple - 1) & -multiple;  // power of two
     return ((count + multiple - 1) / multiple) * multiple;
 }
 
@@ -137,7 +138,9 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout_rank(LayoutArgs a) {
     for (int g = tid; g < NG; g += kLayoutThreads) s_cnt[g] = a.out.counts[g];
     for (int e = tid; e < a.E; e += kLayoutThreads)
         s_gof[e] = (e / a.E_loc) * G + a.shared + (e % a.E_loc);
-    for (int i = tid; i < kLayoutWaves * NG; i += kLayoutThreads) s_wcnt[i / NG][i % NG] = 0;
+#pragma unroll
+    for (int w2 = 0; w2 < kLayoutWaves; ++w2)
+        for (int g = tid; g < NG; g += kLayoutThreads) s_wcnt[w2][g] = 0;
     __syncthreads();
 
     // ---- aligned exclusive prefix P over all groups (segment-major) ----
@@ -189,15 +192,20 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout_rank(LayoutArgs a) {
         for (int s = tid; s <= a.S; s += kLayoutThreads)
             a.out.seg_base[s] = a.C > 0 ? s * a.C : (s < a.S ? s_start[s * G] : total);
     }
-    // P -> absolute first row (clamped at capacity) and capacity limit.
+    // P -> absolute first row (clamped at capacity) and capacity limit.  The
+    // segment index advances with g instead of being divided out each time.
     int32_t st[8], li[8];
+    int s = (tid * 8) / G, gl = tid * 8 - s * G;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
+    for (int j = 0; j < 8; ++j, ++gl) {
         const int g = tid * 8 + j;
+        if (gl == G) {
+            ++s;
+            gl = 0;
+        }
         st[j] = 0;
         li[j] = 0;
         if (g < NG) {
-            const int s = g / G;
             const int32_t segp = s_start[s * G];
             int32_t off = s_start[g] - segp;
             if (a.C > 0) {

@@ -74,6 +74,8 @@ def _load():
         for name in ("orc_combine", "orc_combine_bwd"):
             getattr(lib, name).restype = None
             getattr(lib, name).argtypes = [P] * 5
+        lib.orc_combine_bwd_probs.restype = None
+        lib.orc_combine_bwd_probs.argtypes = [P] * 5
         lib.orc_dispatch_nvfp4.restype = None
         lib.orc_dispatch_nvfp4.argtypes = [P] * 6
         lib.orc_nvfp4_row.restype = None
@@ -215,6 +217,18 @@ def combine_bwd(cfg: Cfg, token_row: np.ndarray, grad_y: np.ndarray,
     pp = None if probs is None else np.ascontiguousarray(probs, np.float32)
     lib.orc_combine_bwd(ctypes.byref(cfg._c()), _ptr(tr), _ptr(gy), _ptr(pp), _ptr(go))
     return go
+
+
+def combine_bwd_probs(cfg: Cfg, token_row: np.ndarray, grad_y: np.ndarray,
+                      out: np.ndarray) -> np.ndarray:
+    """d loss / d probs [T, K] in float64 (the definition)."""
+    lib = _load()
+    gp = np.full((cfg.T, cfg.K), np.nan, np.float64)
+    tr = np.ascontiguousarray(token_row, np.int32)
+    gy = np.ascontiguousarray(grad_y, np.uint16)
+    oo = np.ascontiguousarray(out, np.uint16)
+    lib.orc_combine_bwd_probs(ctypes.byref(cfg._c()), _ptr(tr), _ptr(gy), _ptr(oo), _ptr(gp))
+    return gp
 
 
 def e4m3_encode(s: float) -> int:

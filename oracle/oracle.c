@@ -339,6 +339,29 @@ void orc_combine_bwd(const orc_cfg* c, const int32_t* token_row, const uint16_t*
         }
 }
 
+/* Router-probability gradient (NeMo AutoModel fused_a2a page,
+ * HybridEPDispatch.backward returns a probability gradient next to the
+ * hidden-state gradient): combine is y[t] = sum_k p[t,k] * out[row(t,k)],
+ * so d loss / d p[t,k] = <grad_y[t], out[row(t,k)]>.  The dot product is
+ * taken in double (the definition, not a rounding order); masked, invalid
+ * and dropped slots get 0.  grad_probs is [T, K] (the shared slot carries
+ * no probability). */
+void orc_combine_bwd_probs(const orc_cfg* c, const int32_t* token_row, const uint16_t* grad_y,
+                           const uint16_t* out, double* grad_probs)
+{
+    const int32_t Kp = c->K + c->shared;
+    for (int32_t t = 0; t < c->T; ++t)
+        for (int32_t k = 0; k < c->K; ++k) {
+            int32_t row = token_row[(int64_t)t * Kp + k];
+            double dot = 0.0;
+            if (row >= 0)
+                for (int32_t h = 0; h < c->H; ++h)
+                    dot += (double)orc_bf16_to_f32(grad_y[(int64_t)t * c->H + h]) *
+                           (double)orc_bf16_to_f32(out[(int64_t)row * c->H + h]);
+            grad_probs[(int64_t)t * c->K + k] = dot;
+        }
+}
+
 /* ------------------------------------------------------------------ */
 /* NVFP4 quantization with a per-token dynamic global scale             */
 /* ------------------------------------------------------------------ */

@@ -55,6 +55,8 @@ MUTANTS = {
                            "float w = 1.0f;\n                float v"),
     "combine_bwd_weight_index": ("float w = slot_weight(c, probs, t, k);\n            for",
                                  "float w = slot_weight(c, probs, t, (k + 1) % (c->K));\n            for"),
+    "probs_grad_wrong_operand": ("dot += (double)orc_bf16_to_f32(grad_y[(int64_t)t * c->H + h]) *\n                           (double)orc_bf16_to_f32(out[(int64_t)row * c->H + h]);",
+                                 "dot += (double)orc_bf16_to_f32(grad_y[(int64_t)t * c->H + h]) *\n                           (double)orc_bf16_to_f32(out[(int64_t)t * c->H + h]);"),
     "bf16_truncates": ("if (rem > 0x8000u) return (uint16_t)(lo + 1);",
                        "if (rem > 0x8000u) return (uint16_t)(lo);"),
 }

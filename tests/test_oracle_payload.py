@@ -169,3 +169,27 @@ def test_dropped_slots_contribute_zero(orc):
     assert np.all(np.abs(f32(y) - y64) <= 2.0 ** -8 * np.abs(y64) + 4 * cfg.Kp * 2.0 ** -24 * mag + 1e-30)
     none = np.all(tr < 0, axis=1)
     assert none.any() and np.all(y[none] == 0)
+
+
+def test_probability_gradient_matches_torch_autograd(orc):
+    """grad_probs (NeMo AutoModel fused_a2a page, HybridEPDispatch.backward:
+    a probability gradient beside the hidden-state gradient) is the
+    derivative of combine's weighted sum with respect to the weights."""
+    cfg, ids, probs, x, L, rng = make_case(orc, 8, shared=1, A=4, mask_p=0.15)
+    T, H, K, R = cfg.T, cfg.H, cfg.K, cfg.recv_rows
+    tr = torch.from_numpy(L["token_row"].astype(np.int64))
+    out = wl.bf16_bits(rng.standard_normal((R, H), dtype=np.float32))
+    gy = wl.bf16_bits(rng.standard_normal((T, H), dtype=np.float32))
+    p = torch.from_numpy(probs.astype(np.float64)).requires_grad_(True)
+    ot = torch.from_numpy(f32(out).astype(np.float64))
+    y = torch.zeros(T, H, dtype=torch.float64)
+    for k in range(cfg.Kp):
+        ok = tr[:, k] >= 0
+        w = p[:, k] if k < K else torch.ones(T, dtype=torch.float64)
+        y = y + torch.where(ok[:, None], w[:, None] * ot[tr[:, k].clamp(min=0)], torch.zeros(()))
+    (y * torch.from_numpy(f32(gy).astype(np.float64))).sum().backward()
+    want = p.grad.numpy()
+    got = orc.combine_bwd_probs(cfg, L["token_row"], gy, out)
+    assert np.allclose(got, want, rtol=1e-12, atol=1e-12)
+    masked = L["token_row"][:, :K] < 0
+    assert masked.any() and np.all(got[masked] == 0)
