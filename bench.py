@@ -71,9 +71,10 @@ def traffic_for(op: str):
     return None if entry is None else entry.get("bytes_per_launch")
 
 
-def algorithmic_bytes(w, kept: int, used_rows: int) -> dict:
+def algorithmic_bytes(w, kept: int, used_rows: int, kept_routed: int = None) -> dict:
     """Bytes each op must move at minimum: valid rows only, x read once,
     pad rows never touched (layout metadata: 12 bytes per used row)."""
+    kept_routed = kept if kept_routed is None else kept_routed
     T, H, K, Kp = w.T, w.H, w.K, w.Kp
     row = 2 * H
     return {
@@ -83,6 +84,8 @@ def algorithmic_bytes(w, kept: int, used_rows: int) -> dict:
         "combine": row * kept + row * T + 4 * T * K + 4 * T * Kp,
         "combine_bwd": row * T + row * kept + 4 * T * K + 4 * T * Kp,
         "dispatch_bwd": row * kept + row * T + 4 * T * Kp,
+        # not part of the step: the router-probability gradient
+        "combine_bwd_probs": row * T + row * kept_routed + 4 * T * Kp + 4 * T * K,
     }
 
 
@@ -184,6 +187,8 @@ def main() -> int:
         ("dispatch_bwd", lambda: epx.ep_dispatch_bwd(cfg, lay, grad_recv, gx)),
     ]
     names = [n for n, _ in ops]
+    gprobs = torch.empty(T * w.K, dtype=torch.float32, device=dev)
+    extra_ops = [("combine_bwd_probs", lambda: epx.ep_combine_bwd_probs(cfg, lay, gy, out, gprobs))]
 
     def step():
         for _, fn in ops:
@@ -226,7 +231,7 @@ def main() -> int:
     # bracketed by HIP events on the stream the kernels run on
     LAUNCHES, REPS = 8, max(5, args.steps // 5)
     op_us = {}
-    for n, fn in ops:
+    for n, fn in ops + extra_ops:
         def many(fn=fn):
             for _ in range(LAUNCHES):
                 fn()
@@ -247,9 +252,10 @@ def main() -> int:
     kept = int((tr >= 0).sum())
     rowoff = lay.row_offsets.cpu().numpy()
     used_rows = int(rowoff[:, -1].sum())
-    nbytes = algorithmic_bytes(w, kept, used_rows)
+    kept_routed = int((tr[:, :w.K] >= 0).sum())
+    nbytes = algorithmic_bytes(w, kept, used_rows, kept_routed)
     per_op = {}
-    for n in names:
+    for n in names + [n for n, _ in extra_ops]:
         us = statistics.mean(op_us[n])
         med = statistics.median(op_us[n])
         gbps = nbytes[n] / (us * 1e-6) / 1e9
@@ -257,7 +263,7 @@ def main() -> int:
                      "GBps": round(gbps, 1), "frac": round(gbps / HBM_PEAK_GBPS, 4)}
         log(f"[bench] {n:15s} {us:9.2f} us  {nbytes[n] / 1e6:9.2f} MB  {gbps:8.1f} GB/s  "
             f"{100 * gbps / HBM_PEAK_GBPS:5.1f}% of 8 TB/s")
-    step_bytes = sum(nbytes.values())
+    step_bytes = sum(nbytes[n] for n in names)
     dom = max((n for n in names if n != "layout"), key=lambda n: per_op[n]["us"])
     fwd_us = per_op["layout"]["us"] + per_op["dispatch"]["us"] + per_op["combine"]["us"]
     roof = {"bound": "hbm", "kernel": dom, "achieved": per_op[dom]["GBps"], "peak": HBM_PEAK_GBPS,

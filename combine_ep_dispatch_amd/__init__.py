@@ -33,7 +33,7 @@ from ._lib import (EP_FLAG_BAD_ID, EP_FLAG_DROPPED, EP_FLAG_INTERNAL, EP_ZERO_PA
 __all__ = [
     "EpConfig", "Layout", "QueryResult", "ep_query", "workspace_for", "ep_dispatch_layout",
     "ep_dispatch", "ep_dispatch_nvfp4", "ep_combine", "ep_dispatch_bwd", "ep_combine_bwd",
-    "assert_no_overflow", "EpError", "abi_version", "EP_ZERO_PAD_ROWS", "EP_FLAG_DROPPED",
+    "ep_combine_bwd_probs", "assert_no_overflow", "EpError", "abi_version", "EP_ZERO_PAD_ROWS", "EP_FLAG_DROPPED",
     "EP_FLAG_BAD_ID", "EP_FLAG_INTERNAL",
 ]
 
@@ -238,6 +238,21 @@ def ep_combine_bwd(cfg: EpConfig, layout: Layout, grad_y: torch.Tensor, probs: O
     _check(_lib.lib().ep_combine_bwd(ctypes.byref(c), ctypes.byref(L), grad_y.data_ptr(),
                                      None if probs is None else probs.data_ptr(),
                                      grad_expert_out.data_ptr(), _stream(stream, dev)), "ep_combine_bwd")
+
+
+def ep_combine_bwd_probs(cfg: EpConfig, layout: Layout, grad_y: torch.Tensor, expert_out: torch.Tensor,
+                         grad_probs: torch.Tensor, stream=None) -> None:
+    """grad_probs[t, k] = <grad_y[t], expert_out[token_row[t, k]]> (fp32, [T, K])."""
+    dev = grad_y.device
+    T, H, R = cfg.num_tokens, cfg.hidden, cfg.recv_rows
+    _tensor(grad_y, "grad_y", torch.bfloat16, T * H)
+    _tensor(expert_out, "expert_out", torch.bfloat16, R * H, dev)
+    _tensor(grad_probs, "grad_probs", torch.float32, T * cfg.top_k, dev)
+    layout.check(cfg, dev)
+    c, L = cfg.to_c(), layout.to_c()
+    _check(_lib.lib().ep_combine_bwd_probs(ctypes.byref(c), ctypes.byref(L), grad_y.data_ptr(),
+                                           expert_out.data_ptr(), grad_probs.data_ptr(),
+                                           _stream(stream, dev)), "ep_combine_bwd_probs")
 
 
 def assert_no_overflow(layout: Layout, capacity: Optional[int] = None) -> None:

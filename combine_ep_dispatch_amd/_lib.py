@@ -23,7 +23,8 @@ EP_MAX_GROUPS = 2048
 
 # Every symbol include/epx.h declares.
 SYMBOLS = ("ep_query", "ep_dispatch_layout", "ep_dispatch", "ep_dispatch_nvfp4", "ep_combine",
-           "ep_dispatch_bwd", "ep_combine_bwd", "ep_strerror", "ep_abi_version")
+           "ep_dispatch_bwd", "ep_combine_bwd", "ep_combine_bwd_probs", "ep_strerror",
+           "ep_abi_version")
 
 
 class EpCfg(ctypes.Structure):
@@ -66,7 +67,8 @@ def lib():
         L.ep_combine.argtypes = [cfg_p, lay_p, P, P, P, P]
         L.ep_dispatch_bwd.argtypes = [cfg_p, lay_p, P, P, P]
         L.ep_combine_bwd.argtypes = [cfg_p, lay_p, P, P, P, P]
-        for name in SYMBOLS[:7]:
+        L.ep_combine_bwd_probs.argtypes = [cfg_p, lay_p, P, P, P, P]
+        for name in SYMBOLS[:8]:
             getattr(L, name).restype = I
         L.ep_strerror.argtypes = [I]
         L.ep_strerror.restype = ctypes.c_char_p

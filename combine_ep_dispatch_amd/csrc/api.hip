@@ -274,4 +274,19 @@ int ep_combine_bwd(const ep_cfg_t* cfg, const ep_layout_t* layout, const uint16_
     return zero_pad(d, layout, grad_expert_out, (int64_t)d.H * 2, st);
 }
 
+int ep_combine_bwd_probs(const ep_cfg_t* cfg, const ep_layout_t* layout, const uint16_t* grad_y,
+                         const uint16_t* expert_out, float* grad_probs, void* stream) {
+    Shape d;
+    int rc = derive(cfg, &d);
+    if (rc != EP_OK) return rc;
+    if ((rc = check_rows(d)) != EP_OK) return rc;
+    if (layout == nullptr || bad_buffer(layout->token_row, (int64_t)d.T * d.Kp * 4, 4)) return EP_EINVAL;
+    if (bad_buffer(grad_y, (int64_t)d.T * d.H * 2, 16) || bad_buffer(expert_out, d.R * d.H * 2, 16) ||
+        bad_buffer(grad_probs, (int64_t)d.T * d.K * 4, 4))
+        return EP_EINVAL;
+    if ((rc = check_device()) != EP_OK) return rc;
+    MoveArgs m = move_args(d, layout, grad_y, const_cast<uint16_t*>(expert_out), nullptr);
+    return status_of(launch_probs_grad(m, grad_probs, static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

@@ -107,6 +107,8 @@ struct MoveArgs {
 hipError_t launch_scatter(const MoveArgs& a, hipStream_t stream);         // dispatch: bit copy
 hipError_t launch_scatter_scaled(const MoveArgs& a, hipStream_t stream);  // combine-bwd: w_k * row
 hipError_t launch_gather_reduce(const MoveArgs& a, hipStream_t stream);   // combine / dispatch-bwd
+// grad_probs [T,K] = <grad_y[t] (a.src), expert_out[row(t,k)] (a.dst, read only)>
+hipError_t launch_probs_grad(const MoveArgs& a, float* grad_probs, hipStream_t stream);
 
 struct Nvfp4Args {
     const uint16_t* x;

@@ -30,7 +30,7 @@
 //                     rows, ranks its tile's slots inside their groups
 //                     (per-wave running counters in LDS + match-any),
 //                     resolves its per-group prefix over earlier tiles by
-//                     decoupled look-back (64 predecessor descriptors per
+//                     decoupled look-back (16 predecessor descriptors per
 //                     round trip, folded nearest-first until an inclusive
 //                     prefix is met), upgrades its own descriptors to
 //                     inclusive prefixes for the tiles after it, and writes
@@ -45,7 +45,7 @@ namespace epx {
 namespace {
 
 constexpr int kMaxSpins = 1 << 22;  // look-back gives up (EP_FLAG_INTERNAL) after this
-constexpr int kLookback = 64;       // predecessor descriptors read per round trip
+constexpr int kLookback = 16;       // predecessor descriptors read per round trip
 
 __device__ __forceinline__ int32_t align_up(int32_t count, int32_t multiple) {
     if ((multiple & (multiple - 1)) == 0) return (count + multiple - 1) & -multiple;  // power of two

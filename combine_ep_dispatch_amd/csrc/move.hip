@@ -201,6 +201,68 @@ __global__ __launch_bounds__(kMoveThreads) void k_gather(MoveArgs a, int32_t Hv,
     }
 }
 
+// Router-probability gradient: grad_probs[t,k] = <grad_y[t], expert_out[row(t,k)]>
+// (the derivative of combine's weighted sum with respect to its weights;
+// NeMo AutoModel fused_a2a page, HybridEPDispatch.backward returns a
+// probability gradient beside the hidden-state gradient).  One workgroup per
+// token; thread i takes 16-byte vectors i, i+256, ... of the row and keeps
+// one fp32 partial per slot (multiply, then add: no contraction), for up to
+// 8 slots per pass.  The partials are reduced by a fixed butterfly inside
+// each wave and then across the 4 waves in wave order, so the result is
+// deterministic.  Masked, invalid and dropped slots get 0.
+__global__ __launch_bounds__(kMoveThreads) void k_probs_grad(MoveArgs a, int32_t Hv, float* grad_probs) {
+    __shared__ float s_part[kMoveWaves][kSlotBatch];
+    const int32_t t = blockIdx.x;
+    const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
+    const int32_t my_row = slot_row_of_lane(a, t, lane);
+    const v4u* gy = reinterpret_cast<const v4u*>(a.src) + (int64_t)t * Hv;
+    const v4u* out = reinterpret_cast<const v4u*>(a.dst);
+    for (int32_t k0 = 0; k0 < a.K; k0 += kSlotBatch) {
+        int32_t rows[kSlotBatch];
+        float acc[kSlotBatch];
+#pragma unroll
+        for (int kk = 0; kk < kSlotBatch; ++kk) {
+            rows[kk] = k0 + kk < a.K ? __builtin_amdgcn_readlane(my_row, k0 + kk) : -1;
+            acc[kk] = 0.0f;
+        }
+        for (int32_t v = threadIdx.x; v < Hv; v += kMoveThreads) {
+            const v4u g = gy[v];
+            const uint32_t gq[4] = {g.x, g.y, g.z, g.w};
+#pragma unroll
+            for (int kk = 0; kk < kSlotBatch; ++kk) {
+                if (rows[kk] < 0) continue;
+                const v4u o = load_stream(out + (int64_t)rows[kk] * Hv + v);
+                const uint32_t oq[4] = {o.x, o.y, o.z, o.w};
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const float p0 = bf16_lo(gq[j]) * bf16_lo(oq[j]);
+                    acc[kk] = acc[kk] + p0;
+                    const float p1 = bf16_hi(gq[j]) * bf16_hi(oq[j]);
+                    acc[kk] = acc[kk] + p1;
+                }
+            }
+        }
+#pragma unroll
+        for (int kk = 0; kk < kSlotBatch; ++kk) {
+#pragma unroll
+            for (int o = kWave / 2; o > 0; o >>= 1) acc[kk] = acc[kk] + __shfl_xor(acc[kk], o, kWave);
+        }
+        if (lane == 0) {
+#pragma unroll
+            for (int kk = 0; kk < kSlotBatch; ++kk) s_part[w][kk] = acc[kk];
+        }
+        __syncthreads();
+        if (threadIdx.x < kSlotBatch && k0 + (int)threadIdx.x < a.K) {
+            const int kk = threadIdx.x;
+            float sum = 0.0f;
+#pragma unroll
+            for (int w2 = 0; w2 < kMoveWaves; ++w2) sum = sum + s_part[w2][kk];
+            grad_probs[(int64_t)t * a.K + k0 + kk] = sum;  // rows < 0 summed zeros: exactly 0
+        }
+        __syncthreads();
+    }
+}
+
 struct Grid {
     int32_t Hv, pieces;
     bool full;
@@ -281,6 +343,12 @@ hipError_t launch_scatter_scaled(const MoveArgs& a, hipStream_t stream) { return
 hipError_t launch_gather_reduce(const MoveArgs& a, hipStream_t stream) {
     if (a.T == 0) return hipSuccess;
     return a.probs != nullptr ? gather<true>(a, stream) : gather<false>(a, stream);
+}
+
+hipError_t launch_probs_grad(const MoveArgs& a, float* grad_probs, hipStream_t stream) {
+    if (a.T == 0) return hipSuccess;
+    hipLaunchKernelGGL(k_probs_grad, dim3((unsigned)a.T), dim3(kMoveThreads), 0, stream, a, a.H / 8, grad_probs);
+    return hipGetLastError();
 }
 
 hipError_t launch_zero_pad_rows(void* base, int64_t row_bytes, const ep_layout_t& L, int32_t S, int32_t G,

@@ -224,6 +224,21 @@ int ep_dispatch_bwd(const ep_cfg_t* cfg, const ep_layout_t* layout, const uint16
 int ep_combine_bwd(const ep_cfg_t* cfg, const ep_layout_t* layout, const uint16_t* grad_y,
                    const float* probs, uint16_t* grad_expert_out, void* stream);
 
+/*
+ * Router-probability gradient ([FA] HybridEPDispatch.backward returns a
+ * probability gradient beside the hidden-state gradient): with combine
+ * y[t] = sum_k p[t,k] * out[row(t,k)],
+ *   grad_probs[t,k] = <grad_y[t], expert_out[token_row[t,k]]>  (k < K)
+ * as an fp32 dot product over H; 0 for masked, invalid and dropped slots.
+ * The summation order is fixed (each of 256 threads sums its strided
+ * share of the row in order, then a fixed tree), so results are
+ * deterministic; they equal the exact dot product to within about
+ * (8*ceil(H/2048) + 10) * 2^-24 * sum_h |grad_y[t,h] * out[row,h]|.
+ *   grad_y bf16 [T, H];  expert_out bf16 [R, H];  grad_probs float [T, K].
+ */
+int ep_combine_bwd_probs(const ep_cfg_t* cfg, const ep_layout_t* layout, const uint16_t* grad_y,
+                         const uint16_t* expert_out, float* grad_probs, void* stream);
+
 /* Static description of a status code. */
 const char* ep_strerror(int status);
 

@@ -260,3 +260,38 @@ def check_combine_bwd(c: Case, lay: epx.Layout, name: str, weighted=True):
     torch.cuda.synchronize()
     want = orc.combine_bwd(c.oc, c.L["token_row"], gy, probs)
     assert_bits_equal(bits_of(go), want, f"{name}: combine_bwd")
+
+
+def check_probs_grad(c: Case, lay: epx.Layout, name: str):
+    """grad_probs against the oracle's float64 dot products, within the bound
+    of the kernel's fp32 summation: each thread adds 8*ceil(H/2048) products
+    in order, then 6 butterfly levels and 4 wave partials, one product
+    rounding each: (8*ceil(H/2048) + 10) * 2^-24 * sum |terms|."""
+    say(f"[gpu] combine_bwd_probs {name}")
+    cfg = c.cfg
+    T, H, K = cfg.num_tokens, cfg.hidden, cfg.top_k
+    gy = wl.make_tensor_like_rows(T, H, c.seed * 1000 + 3)
+    out = c.rows(1, nan_pad=True)
+    gp = torch.full((T * K,), float("nan"), dtype=torch.float32, device=DEV)
+    epx.ep_combine_bwd_probs(cfg, lay, u16_tensor(gy), u16_tensor(out), gp)
+    torch.cuda.synchronize()
+    got = gp.cpu().numpy().reshape(T, K).astype(np.float64)
+    gp2 = torch.full((T * K,), float("nan"), dtype=torch.float32, device=DEV)
+    epx.ep_combine_bwd_probs(cfg, lay, u16_tensor(gy), u16_tensor(out), gp2)
+    torch.cuda.synchronize()
+    assert torch.equal(gp.view(torch.int32), gp2.view(torch.int32)), f"{name}: not deterministic"
+    tr = c.L["token_row"]
+    want = orc.combine_bwd_probs(c.oc, tr, gy, out)
+    gyf = np.abs(f32(gy).reshape(T, H).astype(np.float64))
+    mag = np.zeros((T, K))
+    for k in range(K):
+        ok = tr[:, k] >= 0
+        if ok.any():
+            mag[ok, k] = (gyf[ok] * np.abs(f32(out[tr[ok, k]]).astype(np.float64))).sum(1)
+    bound = (8 * -(-H // 2048) + 10) * 2.0 ** -24 * mag + 1e-30
+    err = np.abs(got - want)
+    if not np.all(err <= bound):
+        i = np.argmax(err - bound)
+        raise AssertionError(f"{name}: grad_probs err {err.flat[i]} > bound {bound.flat[i]}")
+    masked = tr[:, :K] < 0
+    assert np.all(got[masked] == 0), f"{name}: masked slots not zero"

@@ -45,6 +45,7 @@ def test_named_workload_full_size(G, name):
     G.check_combine(c, lay, name, weighted=True)
     G.check_dispatch_bwd(c, lay, name)
     G.check_combine_bwd(c, lay, name, weighted=True)
+    G.check_probs_grad(c, lay, name)
     if name == "capacity":
         assert f == 1  # overflow flag raised, nothing else
     else:
@@ -73,6 +74,7 @@ def test_random_shapes(G, seed):
     G.check_combine(c, lay, name, weighted=seed % 2 == 0)
     G.check_dispatch_bwd(c, lay, name)
     G.check_combine_bwd(c, lay, name, weighted=seed % 3 != 0)
+    G.check_probs_grad(c, lay, name)
 
 
 EDGE = {
@@ -105,6 +107,7 @@ def test_edge_cases(G, edge):
     G.check_combine(c, lay, edge)
     G.check_dispatch_bwd(c, lay, edge)
     G.check_combine_bwd(c, lay, edge)
+    G.check_probs_grad(c, lay, edge)
 
 
 @pytest.mark.parametrize("C", [1, 2, 7, 64])
@@ -118,6 +121,7 @@ def test_tiny_capacities(G, C):
     G.check_nvfp4(c, lay, f"cap{C}")
     G.check_combine(c, lay, f"cap{C}")
     G.check_combine_bwd(c, lay, f"cap{C}")
+    G.check_probs_grad(c, lay, f"cap{C}")
 
 
 def test_nvfp4_special_rows(G):
