@@ -76,6 +76,12 @@ def _load():
             getattr(lib, name).argtypes = [P] * 5
         lib.orc_combine_bwd_probs.restype = None
         lib.orc_combine_bwd_probs.argtypes = [P] * 5
+        lib.orc_fp8_row.restype = None
+        lib.orc_fp8_row.argtypes = [ctypes.c_int32, P, P, P]
+        lib.orc_dispatch_fp8.restype = None
+        lib.orc_dispatch_fp8.argtypes = [P] * 5
+        lib.orc_e4m3_encode_signed.restype = ctypes.c_uint8
+        lib.orc_e4m3_encode_signed.argtypes = [ctypes.c_float]
         lib.orc_dispatch_nvfp4.restype = None
         lib.orc_dispatch_nvfp4.argtypes = [P] * 6
         lib.orc_nvfp4_row.restype = None
@@ -175,6 +181,30 @@ def dispatch_nvfp4(cfg: Cfg, token_row: np.ndarray, x: np.ndarray):
     lib.orc_dispatch_nvfp4(ctypes.byref(cfg._c()), _ptr(tr), _ptr(xx), _ptr(codes),
                            _ptr(scales), _ptr(rowscale))
     return codes, scales, rowscale
+
+
+SENTINEL_F32_BITS = np.uint32(0x7FA5A5A5)  # a NaN payload nothing computes
+
+
+def fp8_row(x_row: np.ndarray):
+    """FP8 dispatch of one token (bf16 bits [H]) -> (codes u8 [H], scales f32 [H/128])."""
+    lib = _load()
+    xx = np.ascontiguousarray(x_row, np.uint16)
+    H = xx.shape[0]
+    codes = np.zeros(H, np.uint8)
+    scales = np.zeros(H // 128, np.float32)
+    lib.orc_fp8_row(H, _ptr(xx), _ptr(codes), _ptr(scales))
+    return codes, scales
+
+
+def dispatch_fp8(cfg: Cfg, token_row: np.ndarray, x: np.ndarray):
+    lib = _load()
+    codes = np.full((cfg.recv_rows, cfg.H), SENTINEL_U8, np.uint8)
+    scales = np.full((cfg.recv_rows, cfg.H // 128), SENTINEL_F32_BITS, np.uint32).view(np.float32)
+    tr = np.ascontiguousarray(token_row, np.int32)
+    xx = np.ascontiguousarray(x, np.uint16)
+    lib.orc_dispatch_fp8(ctypes.byref(cfg._c()), _ptr(tr), _ptr(xx), _ptr(codes), _ptr(scales))
+    return codes, scales
 
 
 def nvfp4_row(x_row: np.ndarray):

@@ -363,6 +363,66 @@ void orc_combine_bwd_probs(const orc_cfg* c, const int32_t* token_row, const uin
 }
 
 /* ------------------------------------------------------------------ */
+/* FP8 (E4M3) dispatch                                                 */
+/* ------------------------------------------------------------------ */
+
+/* NeMo AutoModel fused_a2a page: init_hybrid_ep_buffer can use FP8 for the
+ * dispatch payload, and HybridEPDispatch.forward returns a scaling factor
+ * next to the dispatched hidden states.  Reading (the pages give no
+ * format): per token and 128-element block, amax = max|x|,
+ *   code  = E4M3(x * (448 / amax))  (RNE, saturating, sign bit of the product kept)
+ *   scale = amax / 448               (fp32, the dequantization factor)
+ * so that code * scale reproduces x; an all-zero block gives zero codes and
+ * scale 0. */
+uint8_t orc_e4m3_encode_signed(float v)
+{
+    uint8_t c = orc_e4m3_encode(fabsf(v));
+    return signbit(v) ? (uint8_t)(c | 0x80) : c;
+}
+
+void orc_fp8_row(int32_t H, const uint16_t* x, uint8_t* codes, float* scales)
+{
+    for (int32_t b = 0; b < H / 128; ++b) {
+        const uint16_t* xb = x + 128 * b;
+        float amax = 0.0f;
+        for (int i = 0; i < 128; ++i) {
+            float a = fabsf(orc_bf16_to_f32(xb[i]));
+            if (a > amax) amax = a;
+        }
+        if (amax == 0.0f) {
+            memset(codes + 128 * b, 0, 128);
+            scales[b] = 0.0f;
+            continue;
+        }
+        float inv = 448.0f / amax;
+        for (int i = 0; i < 128; ++i) {
+            float v = orc_bf16_to_f32(xb[i]) * inv;
+            codes[128 * b + i] = orc_e4m3_encode_signed(v);
+        }
+        scales[b] = amax / 448.0f;
+    }
+}
+
+void orc_dispatch_fp8(const orc_cfg* c, const int32_t* token_row, const uint16_t* x, uint8_t* codes,
+                      float* scales)
+{
+    const int32_t Kp = c->K + c->shared, H = c->H;
+    uint8_t* qc = (uint8_t*)malloc((size_t)H);
+    float* qs = (float*)malloc(sizeof(float) * (size_t)(H / 128));
+    for (int32_t t = 0; t < c->T; ++t) {
+        orc_fp8_row(H, x + (int64_t)t * H, qc, qs);
+        for (int32_t k = 0; k < Kp; ++k) {
+            int32_t row = token_row[(int64_t)t * Kp + k];
+            if (row < 0) continue;
+            memcpy(codes + (int64_t)row * H, qc, (size_t)H);
+            memcpy(scales + (int64_t)row * (H / 128), qs, sizeof(float) * (size_t)(H / 128));
+        }
+    }
+    free(qc);
+    free(qs);
+}
+
+/* ------------------------------------------------------------------ */
 /* NVFP4 quantization with a per-token dynamic global scale             */
 /* ------------------------------------------------------------------ */
 

@@ -19,7 +19,7 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 PINS = ["tests/test_oracle_formats.py", "tests/test_oracle_layout.py",
-        "tests/test_oracle_payload.py", "tests/test_oracle_nvfp4.py"]
+        "tests/test_oracle_payload.py", "tests/test_oracle_nvfp4.py", "tests/test_oracle_fp8.py"]
 
 MUTANTS = {
     "global_scale_448": ("2688.0f / rowmax", "448.0f / rowmax"),
@@ -57,6 +57,9 @@ MUTANTS = {
                                  "float w = slot_weight(c, probs, t, (k + 1) % (c->K));\n            for"),
     "probs_grad_wrong_operand": ("dot += (double)orc_bf16_to_f32(grad_y[(int64_t)t * c->H + h]) *\n                           (double)orc_bf16_to_f32(out[(int64_t)row * c->H + h]);",
                                  "dot += (double)orc_bf16_to_f32(grad_y[(int64_t)t * c->H + h]) *\n                           (double)orc_bf16_to_f32(out[(int64_t)t * c->H + h]);"),
+    "fp8_scale_formula": ("scales[b] = amax / 448.0f;", "scales[b] = amax / 447.0f;"),
+    "fp8_inverse_scale": ("float inv = 448.0f / amax;", "float inv = 480.0f / amax;"),
+    "fp8_sign_dropped": ("return signbit(v) ? (uint8_t)(c | 0x80) : c;", "return c;"),
     "bf16_truncates": ("if (rem > 0x8000u) return (uint16_t)(lo + 1);",
                        "if (rem > 0x8000u) return (uint16_t)(lo);"),
 }
