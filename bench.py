@@ -84,8 +84,9 @@ def algorithmic_bytes(w, kept: int, used_rows: int, kept_routed: int = None) -> 
         "combine": row * kept + row * T + 4 * T * K + 4 * T * Kp,
         "combine_bwd": row * T + row * kept + 4 * T * K + 4 * T * Kp,
         "dispatch_bwd": row * kept + row * T + 4 * T * Kp,
-        # not part of the step: the router-probability gradient
+        # not part of the step: the router-probability gradient and FP8 dispatch
         "combine_bwd_probs": row * T + row * kept_routed + 4 * T * Kp + 4 * T * K,
+        "dispatch_fp8": row * T + kept * (H + 4 * (H // 128)) + 4 * T * Kp,
     }
 
 
@@ -188,7 +189,10 @@ def main() -> int:
     ]
     names = [n for n, _ in ops]
     gprobs = torch.empty(T * w.K, dtype=torch.float32, device=dev)
-    extra_ops = [("combine_bwd_probs", lambda: epx.ep_combine_bwd_probs(cfg, lay, gy, out, gprobs))]
+    fp8_codes = torch.empty(R * H, dtype=torch.uint8, device=dev)
+    fp8_scales = torch.empty(R * (H // 128), dtype=torch.float32, device=dev)
+    extra_ops = [("combine_bwd_probs", lambda: epx.ep_combine_bwd_probs(cfg, lay, gy, out, gprobs)),
+                 ("dispatch_fp8", lambda: epx.ep_dispatch_fp8(cfg, lay, x, fp8_codes, fp8_scales))]
 
     def step():
         for _, fn in ops:

@@ -32,7 +32,7 @@ from ._lib import (EP_FLAG_BAD_ID, EP_FLAG_DROPPED, EP_FLAG_INTERNAL, EP_ZERO_PA
 
 __all__ = [
     "EpConfig", "Layout", "QueryResult", "ep_query", "workspace_for", "ep_dispatch_layout",
-    "ep_dispatch", "ep_dispatch_nvfp4", "ep_combine", "ep_dispatch_bwd", "ep_combine_bwd",
+    "ep_dispatch", "ep_dispatch_nvfp4", "ep_dispatch_fp8", "ep_combine", "ep_dispatch_bwd", "ep_combine_bwd",
     "ep_combine_bwd_probs", "assert_no_overflow", "EpError", "abi_version", "EP_ZERO_PAD_ROWS", "EP_FLAG_DROPPED",
     "EP_FLAG_BAD_ID", "EP_FLAG_INTERNAL",
 ]
@@ -196,6 +196,20 @@ def ep_dispatch_nvfp4(cfg: EpConfig, layout: Layout, x: torch.Tensor, codes: tor
     _check(_lib.lib().ep_dispatch_nvfp4(ctypes.byref(c), ctypes.byref(L), x.data_ptr(), codes.data_ptr(),
                                         scales.data_ptr(), rowscale.data_ptr(), _stream(stream, dev)),
            "ep_dispatch_nvfp4")
+
+
+def ep_dispatch_fp8(cfg: EpConfig, layout: Layout, x: torch.Tensor, codes: torch.Tensor,
+                    scales: torch.Tensor, stream=None) -> None:
+    """FP8 dispatch: codes uint8 [R, H] (E4M3), scales float32 [R, H/128]."""
+    dev = x.device
+    T, H, R = cfg.num_tokens, cfg.hidden, cfg.recv_rows
+    _tensor(x, "x", torch.bfloat16, T * H)
+    _tensor(codes, "codes", torch.uint8, R * H, dev)
+    _tensor(scales, "scales", torch.float32, R * (H // 128), dev)
+    layout.check(cfg, dev)
+    c, L = cfg.to_c(), layout.to_c()
+    _check(_lib.lib().ep_dispatch_fp8(ctypes.byref(c), ctypes.byref(L), x.data_ptr(), codes.data_ptr(),
+                                      scales.data_ptr(), _stream(stream, dev)), "ep_dispatch_fp8")
 
 
 def ep_combine(cfg: EpConfig, layout: Layout, expert_out: torch.Tensor, probs: Optional[torch.Tensor],

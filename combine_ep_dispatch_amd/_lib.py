@@ -22,8 +22,8 @@ EP_FLAG_INTERNAL = 4
 EP_MAX_GROUPS = 2048
 
 # Every symbol include/epx.h declares.
-SYMBOLS = ("ep_query", "ep_dispatch_layout", "ep_dispatch", "ep_dispatch_nvfp4", "ep_combine",
-           "ep_dispatch_bwd", "ep_combine_bwd", "ep_combine_bwd_probs", "ep_strerror",
+SYMBOLS = ("ep_query", "ep_dispatch_layout", "ep_dispatch", "ep_dispatch_nvfp4", "ep_dispatch_fp8",
+           "ep_combine", "ep_dispatch_bwd", "ep_combine_bwd", "ep_combine_bwd_probs", "ep_strerror",
            "ep_abi_version")
 
 
@@ -68,7 +68,8 @@ def lib():
         L.ep_dispatch_bwd.argtypes = [cfg_p, lay_p, P, P, P]
         L.ep_combine_bwd.argtypes = [cfg_p, lay_p, P, P, P, P]
         L.ep_combine_bwd_probs.argtypes = [cfg_p, lay_p, P, P, P, P]
-        for name in SYMBOLS[:8]:
+        L.ep_dispatch_fp8.argtypes = [cfg_p, lay_p, P, P, P, P]
+        for name in SYMBOLS[:9]:
             getattr(L, name).restype = I
         L.ep_strerror.argtypes = [I]
         L.ep_strerror.restype = ctypes.c_char_p

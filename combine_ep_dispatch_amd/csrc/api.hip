@@ -231,6 +231,33 @@ int ep_dispatch_nvfp4(const ep_cfg_t* cfg, const ep_layout_t* layout, const uint
     return zero_pad(d, layout, rowscale, 2, st);
 }
 
+int ep_dispatch_fp8(const ep_cfg_t* cfg, const ep_layout_t* layout, const uint16_t* x, uint8_t* codes,
+                    float* scales, void* stream) {
+    Shape d;
+    int rc = derive(cfg, &d);
+    if (rc != EP_OK) return rc;
+    if ((rc = check_rows(d)) != EP_OK) return rc;
+    if (d.H % 128 != 0 || d.H > fp8_max_hidden()) return EP_EINVAL;
+    if ((rc = check_layout_for_payload(d, layout)) != EP_OK) return rc;
+    if (bad_buffer(x, (int64_t)d.T * d.H * 2, 16) || bad_buffer(codes, d.R * d.H, 16) ||
+        bad_buffer(scales, d.R * (d.H / 128) * 4, 4))
+        return EP_EINVAL;
+    if ((rc = check_device()) != EP_OK) return rc;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    Fp8Args a;
+    a.x = x;
+    a.codes = codes;
+    a.scales = scales;
+    a.token_row = layout->token_row;
+    a.T = d.T;
+    a.Kp = d.Kp;
+    a.H = d.H;
+    a.R = d.R;
+    if ((rc = status_of(launch_fp8(a, st))) != EP_OK) return rc;
+    if ((rc = zero_pad(d, layout, codes, d.H, st)) != EP_OK) return rc;
+    return zero_pad(d, layout, scales, (int64_t)(d.H / 128) * 4, st);
+}
+
 int ep_combine(const ep_cfg_t* cfg, const ep_layout_t* layout, const uint16_t* expert_out, const float* probs,
                uint16_t* y, void* stream) {
     Shape d;

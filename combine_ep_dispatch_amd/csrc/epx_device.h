@@ -58,6 +58,27 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
 }
 
+// E4M3 ("fn" variant of OCP OFP8: bias 7, largest finite 448, exponent
+// field 0 subnormal with step 2^-9).
+// Non-negative finite s -> E4M3 code, RNE, saturating to 448 (0x7E).
+__device__ __forceinline__ uint32_t e4m3_encode(float s) {
+    if (!(s > 0.0f)) return 0u;
+    if (s >= 448.0f) return 0x7Eu;
+    if (s < 0.015625f) {                 // below 2^-6: subnormal step 2^-9
+        return (uint32_t)__builtin_rintf(s * 512.0f);  // exact scaling, RNE; 8 -> 0x08 = 2^-6
+    }
+    uint32_t u = __float_as_uint(s);
+    u += 0x7FFFFu + ((u >> 20) & 1u);    // round the mantissa to 3 bits, ties to even
+    const uint32_t c = (((u >> 23) - 120u) << 3) | ((u >> 20) & 7u);  // rebias 127 -> 7
+    return c > 0x7Eu ? 0x7Eu : c;
+}
+
+__device__ __forceinline__ float e4m3_decode(uint32_t c) {
+    const uint32_t e = c >> 3, m = c & 7u;
+    if (e == 0u) return (float)m * 0.001953125f;  // m * 2^-9, exact
+    return __uint_as_float(((e + 120u) << 23) | (m << 20));
+}
+
 // Count of set bits of `m` in lanes below this one (the in-wave rank).
 __device__ __forceinline__ uint32_t lanes_below(uint64_t m) {
     return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
@@ -121,6 +142,17 @@ struct Nvfp4Args {
 };
 hipError_t launch_nvfp4(const Nvfp4Args& a, hipStream_t stream);
 int nvfp4_max_hidden();
+
+struct Fp8Args {
+    const uint16_t* x;
+    uint8_t* codes;    // [R, H] E4M3
+    float* scales;     // [R, H/128]
+    const int32_t* token_row;
+    int32_t T, Kp, H;
+    int64_t R;
+};
+hipError_t launch_fp8(const Fp8Args& a, hipStream_t stream);
+int fp8_max_hidden();
 
 // Zero the payload bytes of every pad row ([count, align_up(count)) of each
 // group, below capacity).  row_bytes = bytes of one row of `base`.

@@ -1,0 +1,122 @@
+// FP8 (E4M3) dispatch (NeMo AutoModel fused_a2a page: init_hybrid_ep_buffer
+// can use FP8 for the dispatch payload, and HybridEPDispatch.forward returns
+// a scaling factor beside the dispatched hidden states).  Per token and
+// 128-element block, with amax = max|x|:
+//   code  = E4M3(x * (448 / amax))   RNE, saturating to 448, sign of the product kept
+//   scale = amax / 448               fp32, so that code * scale reproduces x
+// An all-zero block gives zero codes and scale 0.  Each token is quantized
+// once and its bytes written to every kept (token, slot) row.
+//
+// One wave64 per token.  Lanes form 8 groups of 8; group j owns block
+// 8*it + j of iteration it and each lane 16 of its elements, so one wave
+// load covers 2 KiB of the row and one wave store 1 KiB of codes, both
+// contiguous.  The block amax is three xor-shuffles inside the 8-lane group.
+// IEEE division and no contraction keep the result bit-identical to the
+// plain definition.
+#include "epx_device.h"
+
+namespace epx {
+namespace {
+
+constexpr int kFp8Threads = 256;
+constexpr int kFp8Waves = kFp8Threads / kWave;
+constexpr int kFp8MaxIters = 16;  // H <= 1024 * 16
+
+__device__ __forceinline__ uint32_t e4m3_signed(float v) {
+    return e4m3_encode(__builtin_fabsf(v)) | ((__float_as_uint(v) >> 24) & 0x80u);
+}
+
+__device__ __forceinline__ uint32_t absmax16(const uint4& p, const uint4& q) {
+    const uint32_t w[8] = {p.x, p.y, p.z, p.w, q.x, q.y, q.z, q.w};
+    uint32_t m = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) m = max(m, max(w[i] & 0x7FFFu, (w[i] >> 16) & 0x7FFFu));
+    return m;
+}
+
+// Four E4M3 codes (elements 2i, 2i+1 of words w0, w1) packed little-endian.
+__device__ __forceinline__ uint32_t codes4(uint32_t w0, uint32_t w1, float inv) {
+    return e4m3_signed(bf16_lo(w0) * inv) | (e4m3_signed(bf16_hi(w0) * inv) << 8) |
+           (e4m3_signed(bf16_lo(w1) * inv) << 16) | (e4m3_signed(bf16_hi(w1) * inv) << 24);
+}
+
+template <int NIT>
+__global__ __launch_bounds__(kFp8Threads) void k_fp8(Fp8Args a) {
+    const int32_t t = uniform((int32_t)(blockIdx.x * kFp8Waves + threadIdx.x / kWave));
+    if (t >= a.T) return;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int32_t nblk = a.H / 128;
+    const uint4* xr = reinterpret_cast<const uint4*>(a.x + (int64_t)t * a.H);
+
+    uint4 code[NIT];
+    float scale[NIT];
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+        const int32_t b = it * 8 + lane / 8;  // this lane's block
+        uint4 p = make_uint4(0, 0, 0, 0), q = make_uint4(0, 0, 0, 0);
+        if (b < nblk) {
+            p = xr[128 * it + 2 * lane];
+            q = xr[128 * it + 2 * lane + 1];
+        }
+        uint32_t m = absmax16(p, q);
+        m = max(m, (uint32_t)__shfl_xor((int)m, 4, kWave));
+        m = max(m, (uint32_t)__shfl_xor((int)m, 2, kWave));
+        m = max(m, (uint32_t)__shfl_xor((int)m, 1, kWave));
+        const float amax = __uint_as_float(m << 16);
+        if (amax == 0.0f) {
+            code[it] = make_uint4(0, 0, 0, 0);
+            scale[it] = 0.0f;
+        } else {
+            const float inv = 448.0f / amax;
+            code[it].x = codes4(p.x, p.y, inv);
+            code[it].y = codes4(p.z, p.w, inv);
+            code[it].z = codes4(q.x, q.y, inv);
+            code[it].w = codes4(q.z, q.w, inv);
+            scale[it] = amax / 448.0f;
+        }
+    }
+
+    const int32_t* tr = a.token_row + (int64_t)t * a.Kp;
+    for (int32_t k = 0; k < a.Kp; ++k) {
+        const int32_t row = tr[k];
+        if (row < 0 || row >= a.R) continue;
+        uint4* crow = reinterpret_cast<uint4*>(a.codes + (int64_t)row * a.H);
+        float* srow = a.scales + (int64_t)row * nblk;
+#pragma unroll
+        for (int it = 0; it < NIT; ++it) {
+            const int32_t b = it * 8 + lane / 8;
+            if (b < nblk) {
+                crow[64 * it + lane] = code[it];
+                if ((lane & 7) == 0) srow[b] = scale[it];
+            }
+        }
+    }
+}
+
+template <int NIT>
+hipError_t launch_nit(const Fp8Args& a, hipStream_t stream) {
+    const unsigned blocks = (unsigned)((a.T + kFp8Waves - 1) / kFp8Waves);
+    hipLaunchKernelGGL(k_fp8<NIT>, dim3(blocks), dim3(kFp8Threads), 0, stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+int fp8_max_hidden() { return 1024 * kFp8MaxIters; }
+
+hipError_t launch_fp8(const Fp8Args& a, hipStream_t stream) {
+    if (a.T == 0) return hipSuccess;
+    const int nit = (a.H + 1023) / 1024;
+    switch (nit) {
+        case 1: return launch_nit<1>(a, stream);
+        case 2: return launch_nit<2>(a, stream);
+        case 3: case 4: return launch_nit<4>(a, stream);
+        case 5: case 6: return launch_nit<6>(a, stream);
+        case 7: return launch_nit<7>(a, stream);
+        case 8: return launch_nit<8>(a, stream);
+        case 9: case 10: case 11: case 12: return launch_nit<12>(a, stream);
+        default: return launch_nit<kFp8MaxIters>(a, stream);
+    }
+}
+
+}  // namespace epx

@@ -31,25 +31,6 @@ constexpr int kQuantThreads = 256;
 constexpr int kQuantWaves = kQuantThreads / kWave;
 constexpr int kMaxBlocksPerLane = 16;  // H <= 16 * 64 * 16 = 16384
 
-// Non-negative finite s -> E4M3 code, RNE, saturating to 448 (0x7E).
-__device__ __forceinline__ uint32_t e4m3_encode(float s) {
-    if (!(s > 0.0f)) return 0u;
-    if (s >= 448.0f) return 0x7Eu;
-    if (s < 0.015625f) {                 // below 2^-6: subnormal step 2^-9
-        return (uint32_t)__builtin_rintf(s * 512.0f);  // exact scaling, RNE; 8 -> 0x08 = 2^-6
-    }
-    uint32_t u = __float_as_uint(s);
-    u += 0x7FFFFu + ((u >> 20) & 1u);    // round the mantissa to 3 bits, ties to even
-    const uint32_t c = (((u >> 23) - 120u) << 3) | ((u >> 20) & 7u);  // rebias 127 -> 7
-    return c > 0x7Eu ? 0x7Eu : c;
-}
-
-__device__ __forceinline__ float e4m3_decode(uint32_t c) {
-    const uint32_t e = c >> 3, m = c & 7u;
-    if (e == 0u) return (float)m * 0.001953125f;  // m * 2^-9, exact
-    return __uint_as_float(((e + 120u) << 23) | (m << 20));
-}
-
 // v -> E2M1 code.  Thresholds are the midpoints between the magnitudes
 // {0, .5, 1, 1.5, 2, 3, 4, 6}; at a midpoint the even code wins (the
 // comparison is strict toward the odd neighbour).

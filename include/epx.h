@@ -194,6 +194,24 @@ int ep_dispatch_nvfp4(const ep_cfg_t* cfg, const ep_layout_t* layout, const uint
                       uint8_t* codes, uint8_t* scales, uint16_t* rowscale, void* stream);
 
 /*
+ * FP8 dispatch ([FA] init_hybrid_ep_buffer: FP8 communication in the
+ * dispatch phase; HybridEPDispatch.forward returns a scaling factor beside
+ * the hidden states).  The pages give no format; this library reads it as
+ * E4M3 codes with one fp32 factor per token and 128-element block:
+ *   x       bf16 [T, H] (H % 128 == 0, H <= 16384)
+ *   codes   uint8 [R, H]       E4M3 ("fn") codes
+ *   scales  float [R, H/128]   dequantization factors
+ * Per block, in IEEE fp32 with round-to-nearest-even: amax = max|x|;
+ *   codes = E4M3(x * (448 / amax))  (saturating to 448, sign of the product kept)
+ *   scale = amax / 448
+ * An all-zero block gives zero codes and scale 0.  Every copy of a token
+ * carries the same bytes.  Blocks with 0 < amax < 448/FLT_MAX are outside
+ * the contract.
+ */
+int ep_dispatch_fp8(const ep_cfg_t* cfg, const ep_layout_t* layout, const uint16_t* x,
+                    uint8_t* codes, float* scales, void* stream);
+
+/*
  * Combine ([FA] HybridEPCombine.forward; [TD] moe_router_dtype fp32):
  *   y[t, :] = bf16_rne( sum_{k=0..K'-1, token_row[t,k] >= 0}
  *                       w_k * float(expert_out[token_row[t,k], :]) )

@@ -295,3 +295,18 @@ def check_probs_grad(c: Case, lay: epx.Layout, name: str):
         raise AssertionError(f"{name}: grad_probs err {err.flat[i]} > bound {bound.flat[i]}")
     masked = tr[:, :K] < 0
     assert np.all(got[masked] == 0), f"{name}: masked slots not zero"
+
+
+def check_fp8(c: Case, lay: epx.Layout, name: str, x=None):
+    say(f"[gpu] fp8 {name}: H={c.cfg.hidden}")
+    cfg = c.cfg
+    x = c.x if x is None else x
+    R, H = cfg.recv_rows, cfg.hidden
+    codes = torch.full((R * H,), int(orc.SENTINEL_U8), dtype=torch.uint8, device=DEV)
+    scales = torch.full((R * (H // 128),), int(np.int32(orc.SENTINEL_F32_BITS.view(np.int32))),
+                        dtype=torch.int32, device=DEV).view(torch.float32)
+    epx.ep_dispatch_fp8(cfg, lay, u16_tensor(x), codes, scales)
+    torch.cuda.synchronize()
+    wc, wsc = orc.dispatch_fp8(c.oc, c.L["token_row"], x)
+    assert_bits_equal(codes.cpu().numpy(), wc, f"{name}: fp8 codes")
+    assert_bits_equal(scales.view(torch.int32).cpu().numpy(), wsc.view(np.int32), f"{name}: fp8 scales")

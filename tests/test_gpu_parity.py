@@ -41,6 +41,8 @@ def test_named_workload_full_size(G, name):
     assert f & 4 == 0
     if name == "nvfp4":
         G.check_nvfp4(c, lay, name)
+    if c.cfg.hidden % 128 == 0:
+        G.check_fp8(c, lay, name)
     G.check_dispatch(c, lay, name)
     G.check_combine(c, lay, name, weighted=True)
     G.check_dispatch_bwd(c, lay, name)
@@ -71,6 +73,8 @@ def test_random_shapes(G, seed):
     G.check_dispatch(c, lay, name)
     if c.cfg.hidden % 16 == 0:
         G.check_nvfp4(c, lay, name)
+    if c.cfg.hidden % 128 == 0:
+        G.check_fp8(c, lay, name)
     G.check_combine(c, lay, name, weighted=seed % 2 == 0)
     G.check_dispatch_bwd(c, lay, name)
     G.check_combine_bwd(c, lay, name, weighted=seed % 3 != 0)
@@ -104,6 +108,8 @@ def test_edge_cases(G, edge):
     G.check_dispatch(c, lay, edge)
     if c.cfg.hidden % 16 == 0:
         G.check_nvfp4(c, lay, edge)
+    if c.cfg.hidden % 128 == 0:
+        G.check_fp8(c, lay, edge)
     G.check_combine(c, lay, edge)
     G.check_dispatch_bwd(c, lay, edge)
     G.check_combine_bwd(c, lay, edge)
@@ -112,13 +118,15 @@ def test_edge_cases(G, edge):
 
 @pytest.mark.parametrize("C", [1, 2, 7, 64])
 def test_tiny_capacities(G, C):
-    c = G.random_case(55, T=400, S=4, E_loc=4, K=4, A=4, shared=1, src=2, C=C)
+    c = G.random_case(55, T=400, S=4, E_loc=4, K=4, A=4, shared=1, src=2, C=C, H=256)
     c.cfg.recv_rows = G.epx.ep_query(c.cfg).min_recv_rows
     c = G.Case(c.cfg, c.ids, c.probs, c.x, c.seed)
     lay = G.check_layout(c, f"cap{C}")
     assert int(lay.flags.item()) & 1
     G.check_dispatch(c, lay, f"cap{C}")
     G.check_nvfp4(c, lay, f"cap{C}")
+    if c.cfg.hidden % 128 == 0:
+        G.check_fp8(c, lay, f"cap{C}")
     G.check_combine(c, lay, f"cap{C}")
     G.check_combine_bwd(c, lay, f"cap{C}")
     G.check_probs_grad(c, lay, f"cap{C}")
@@ -144,6 +152,27 @@ def test_nvfp4_special_rows(G):
     c = G.Case(c.cfg, c.ids, c.probs, xb, c.seed)
     lay = G.check_layout(c, "nvfp4_special")
     G.check_nvfp4(c, lay, "nvfp4_special")
+    if H % 128 == 0:
+        G.check_fp8(c, lay, "fp8_special")
+
+
+def test_fp8_special_rows(G):
+    """FP8 blocks with zeros, -0, bf16 subnormals, huge and tiny magnitudes,
+    ties at E4M3 midpoints, and a ragged last block group (H/128 = 9)."""
+    rng = np.random.default_rng(4)
+    T, H = 48, 1152
+    x = rng.standard_normal((T, H)).astype(np.float32)
+    x[0] = 0
+    x[1] = -0.0
+    x[2, :128] = 1e-39
+    x[3] = (rng.standard_normal(H) * 10.0 ** rng.uniform(-20, 20, H)).astype(np.float32)
+    x[4, :128] = 7.0 * rng.integers(-64, 65, 128) / 64  # values on the E4M3 grid and midpoints
+    x[5, ::3] = 0.0
+    xb = G.wl.bf16_bits(x)
+    c = G.random_case(11, T=T, H=H, S=2, E_loc=4, K=2, A=4, shared=1, src=1, mask_p=0.0)
+    c = G.Case(c.cfg, c.ids, c.probs, xb, c.seed)
+    lay = G.check_layout(c, "fp8_special")
+    G.check_fp8(c, lay, "fp8_special")
 
 
 def test_determinism_and_garbage_workspace(G):
