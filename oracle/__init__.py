@@ -76,6 +76,10 @@ def _load():
             getattr(lib, name).argtypes = [P] * 5
         lib.orc_combine_bwd_probs.restype = None
         lib.orc_combine_bwd_probs.argtypes = [P] * 5
+        lib.orc_indices_to_multihot.restype = None
+        lib.orc_indices_to_multihot.argtypes = [P] * 5
+        lib.orc_multihot_to_indices.restype = ctypes.c_int32
+        lib.orc_multihot_to_indices.argtypes = [P] * 5
         lib.orc_fp8_row.restype = None
         lib.orc_fp8_row.argtypes = [ctypes.c_int32, P, P, P]
         lib.orc_dispatch_fp8.restype = None
@@ -184,6 +188,29 @@ def dispatch_nvfp4(cfg: Cfg, token_row: np.ndarray, x: np.ndarray):
 
 
 SENTINEL_F32_BITS = np.uint32(0x7FA5A5A5)  # a NaN payload nothing computes
+FLAG_MAP_OVERFLOW = 8
+
+
+def indices_to_multihot(cfg: Cfg, topk_ids: np.ndarray, probs: Optional[np.ndarray]):
+    """(routing_map uint8 [T, E], dense_probs float32 [T, E] or None)."""
+    lib = _load()
+    ids = np.ascontiguousarray(topk_ids, np.int32).reshape(cfg.T, cfg.K)
+    rm = np.full((cfg.T, cfg.E), SENTINEL_U8, np.uint8)
+    dp = None if probs is None else np.full((cfg.T, cfg.E), np.nan, np.float32)
+    pp = None if probs is None else np.ascontiguousarray(probs, np.float32)
+    lib.orc_indices_to_multihot(ctypes.byref(cfg._c()), _ptr(ids), _ptr(pp), _ptr(rm), _ptr(dp))
+    return rm, dp
+
+
+def multihot_to_indices(cfg: Cfg, routing_map: np.ndarray, dense_probs: Optional[np.ndarray]):
+    """(topk_ids int32 [T, K], probs float32 [T, K], flags)."""
+    lib = _load()
+    rm = np.ascontiguousarray(routing_map, np.uint8).reshape(cfg.T, cfg.E)
+    dp = None if dense_probs is None else np.ascontiguousarray(dense_probs, np.float32)
+    ids = np.full((cfg.T, cfg.K), SENTINEL_I32, np.int32)
+    pr = np.full((cfg.T, cfg.K), np.nan, np.float32)
+    f = lib.orc_multihot_to_indices(ctypes.byref(cfg._c()), _ptr(rm), _ptr(dp), _ptr(ids), _ptr(pr))
+    return ids, pr, int(f)
 
 
 def fp8_row(x_row: np.ndarray):

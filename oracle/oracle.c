@@ -363,6 +363,64 @@ void orc_combine_bwd_probs(const orc_cfg* c, const int32_t* token_row, const uin
 }
 
 /* ------------------------------------------------------------------ */
+/* Compact top-k <-> dense routing map                                  */
+/* ------------------------------------------------------------------ */
+
+/* NeMo AutoModel token_dispatcher page, _HybridEPManager._indices_to_multihot:
+ * top-k indices (and their probabilities) become a multihot [T, E] map and
+ * a dense [T, E] probability matrix.  Readings: -1 and ids outside [0, E)
+ * set nothing; an expert named by two slots of one token is set once and
+ * its probabilities add, in slot order (so a combine over the dense form
+ * weights that expert's output by the same total). */
+void orc_indices_to_multihot(const orc_cfg* c, const int32_t* ids, const float* probs,
+                             uint8_t* routing_map, float* dense_probs)
+{
+    for (int32_t t = 0; t < c->T; ++t) {
+        for (int32_t e = 0; e < c->E; ++e) {
+            routing_map[(int64_t)t * c->E + e] = 0;
+            if (dense_probs) dense_probs[(int64_t)t * c->E + e] = 0.0f;
+        }
+        for (int32_t k = 0; k < c->K; ++k) {
+            int32_t e = ids[(int64_t)t * c->K + k];
+            if (e < 0 || e >= c->E) continue;
+            routing_map[(int64_t)t * c->E + e] = 1;
+            if (dense_probs && probs)
+                dense_probs[(int64_t)t * c->E + e] = dense_probs[(int64_t)t * c->E + e] + probs[(int64_t)t * c->K + k];
+        }
+    }
+}
+
+/* The reverse direction (NeMo AutoModel fused_a2a page,
+ * HybridEPDispatch.forward takes either a dense routing map or compact
+ * indices).  Readings: the experts a token's row marks (any nonzero byte)
+ * fill its slots in ascending expert order, the rest get -1 and
+ * probability 0; a row marking more than K experts keeps the lowest K and
+ * raises flag bit 3 (value 8).  Returns the flag bits. */
+int32_t orc_multihot_to_indices(const orc_cfg* c, const uint8_t* routing_map, const float* dense_probs,
+                                int32_t* ids, float* probs)
+{
+    int32_t flags = 0;
+    for (int32_t t = 0; t < c->T; ++t) {
+        int32_t n = 0;
+        for (int32_t e = 0; e < c->E; ++e) {
+            if (!routing_map[(int64_t)t * c->E + e]) continue;
+            if (n == c->K) {
+                flags |= 8;
+                break;
+            }
+            ids[(int64_t)t * c->K + n] = e;
+            if (probs) probs[(int64_t)t * c->K + n] = dense_probs ? dense_probs[(int64_t)t * c->E + e] : 0.0f;
+            ++n;
+        }
+        for (; n < c->K; ++n) {
+            ids[(int64_t)t * c->K + n] = -1;
+            if (probs) probs[(int64_t)t * c->K + n] = 0.0f;
+        }
+    }
+    return flags;
+}
+
+/* ------------------------------------------------------------------ */
 /* FP8 (E4M3) dispatch                                                 */
 /* ------------------------------------------------------------------ */
 

@@ -19,7 +19,8 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 PINS = ["tests/test_oracle_formats.py", "tests/test_oracle_layout.py",
-        "tests/test_oracle_payload.py", "tests/test_oracle_nvfp4.py", "tests/test_oracle_fp8.py"]
+        "tests/test_oracle_payload.py", "tests/test_oracle_nvfp4.py", "tests/test_oracle_fp8.py",
+        "tests/test_oracle_routing_map.py"]
 
 MUTANTS = {
     "global_scale_448": ("2688.0f / rowmax", "448.0f / rowmax"),
@@ -60,6 +61,9 @@ MUTANTS = {
     "fp8_scale_formula": ("scales[b] = amax / 448.0f;", "scales[b] = amax / 447.0f;"),
     "fp8_inverse_scale": ("float inv = 448.0f / amax;", "float inv = 480.0f / amax;"),
     "fp8_sign_dropped": ("return signbit(v) ? (uint8_t)(c | 0x80) : c;", "return c;"),
+    "multihot_overwrites": ("dense_probs[(int64_t)t * c->E + e] = dense_probs[(int64_t)t * c->E + e] + probs[(int64_t)t * c->K + k];",
+                            "dense_probs[(int64_t)t * c->E + e] = probs[(int64_t)t * c->K + k];"),
+    "map_overflow_unflagged": ("                flags |= 8;\n", ""),
     "bf16_truncates": ("if (rem > 0x8000u) return (uint16_t)(lo + 1);",
                        "if (rem > 0x8000u) return (uint16_t)(lo);"),
 }
