@@ -27,13 +27,13 @@ from typing import NamedTuple, Optional
 import torch
 
 from . import _lib
-from ._lib import (EP_FLAG_BAD_ID, EP_FLAG_DROPPED, EP_FLAG_INTERNAL, EP_ZERO_PAD_ROWS,  # noqa: F401
-                   EpCfg, EpLayout)
+from ._lib import (EP_FLAG_BAD_ID, EP_FLAG_DROPPED, EP_FLAG_INTERNAL, EP_FLAG_MAP_OVERFLOW,  # noqa: F401
+                   EP_ZERO_PAD_ROWS, EpCfg, EpLayout)
 
 __all__ = [
     "EpConfig", "Layout", "QueryResult", "ep_query", "workspace_for", "ep_dispatch_layout",
     "ep_dispatch", "ep_dispatch_nvfp4", "ep_dispatch_fp8", "ep_combine", "ep_dispatch_bwd", "ep_combine_bwd",
-    "ep_combine_bwd_probs", "assert_no_overflow", "EpError", "abi_version", "EP_ZERO_PAD_ROWS", "EP_FLAG_DROPPED",
+    "ep_combine_bwd_probs", "ep_indices_to_multihot", "ep_multihot_to_indices", "assert_no_overflow", "EpError", "abi_version", "EP_ZERO_PAD_ROWS", "EP_FLAG_DROPPED",
     "EP_FLAG_BAD_ID", "EP_FLAG_INTERNAL",
 ]
 
@@ -267,6 +267,44 @@ def ep_combine_bwd_probs(cfg: EpConfig, layout: Layout, grad_y: torch.Tensor, ex
     _check(_lib.lib().ep_combine_bwd_probs(ctypes.byref(c), ctypes.byref(L), grad_y.data_ptr(),
                                            expert_out.data_ptr(), grad_probs.data_ptr(),
                                            _stream(stream, dev)), "ep_combine_bwd_probs")
+
+
+def ep_indices_to_multihot(cfg: EpConfig, topk_ids: torch.Tensor, probs: Optional[torch.Tensor],
+                           routing_map: torch.Tensor, dense_probs: Optional[torch.Tensor] = None,
+                           stream=None) -> None:
+    """Compact top-k -> routing_map uint8 [T, E] (+ dense_probs float32 [T, E])."""
+    dev = topk_ids.device
+    T, E, K = cfg.num_tokens, cfg.num_experts, cfg.top_k
+    _tensor(topk_ids, "topk_ids", torch.int32, T * K)
+    _tensor(routing_map, "routing_map", torch.uint8, T * E, dev)
+    if dense_probs is not None:
+        _tensor(dense_probs, "dense_probs", torch.float32, T * E, dev)
+        _tensor(probs, "probs", torch.float32, T * K, dev)
+    c = cfg.to_c()
+    _check(_lib.lib().ep_indices_to_multihot(
+        ctypes.byref(c), topk_ids.data_ptr(), None if probs is None else probs.data_ptr(),
+        routing_map.data_ptr(), None if dense_probs is None else dense_probs.data_ptr(),
+        _stream(stream, dev)), "ep_indices_to_multihot")
+
+
+def ep_multihot_to_indices(cfg: EpConfig, routing_map: torch.Tensor, dense_probs: Optional[torch.Tensor],
+                           topk_ids: torch.Tensor, probs: Optional[torch.Tensor] = None,
+                           flags: Optional[torch.Tensor] = None, stream=None) -> None:
+    """routing_map uint8 [T, E] (+ dense_probs) -> compact top-k ids [T, K] (+ probs)."""
+    dev = routing_map.device
+    T, E, K = cfg.num_tokens, cfg.num_experts, cfg.top_k
+    _tensor(routing_map, "routing_map", torch.uint8, T * E)
+    _tensor(topk_ids, "topk_ids", torch.int32, T * K, dev)
+    if probs is not None:
+        _tensor(probs, "probs", torch.float32, T * K, dev)
+        _tensor(dense_probs, "dense_probs", torch.float32, T * E, dev)
+    if flags is not None:
+        _tensor(flags, "flags", torch.int32, 1, dev)
+    c = cfg.to_c()
+    _check(_lib.lib().ep_multihot_to_indices(
+        ctypes.byref(c), routing_map.data_ptr(), None if dense_probs is None else dense_probs.data_ptr(),
+        topk_ids.data_ptr(), None if probs is None else probs.data_ptr(),
+        None if flags is None else flags.data_ptr(), _stream(stream, dev)), "ep_multihot_to_indices")
 
 
 def assert_no_overflow(layout: Layout, capacity: Optional[int] = None) -> None:

@@ -19,12 +19,13 @@ EP_ZERO_PAD_ROWS = 1
 EP_FLAG_DROPPED = 1
 EP_FLAG_BAD_ID = 2
 EP_FLAG_INTERNAL = 4
+EP_FLAG_MAP_OVERFLOW = 8
 EP_MAX_GROUPS = 2048
 
 # Every symbol include/epx.h declares.
 SYMBOLS = ("ep_query", "ep_dispatch_layout", "ep_dispatch", "ep_dispatch_nvfp4", "ep_dispatch_fp8",
-           "ep_combine", "ep_dispatch_bwd", "ep_combine_bwd", "ep_combine_bwd_probs", "ep_strerror",
-           "ep_abi_version")
+           "ep_combine", "ep_dispatch_bwd", "ep_combine_bwd", "ep_combine_bwd_probs",
+           "ep_indices_to_multihot", "ep_multihot_to_indices", "ep_strerror", "ep_abi_version")
 
 
 class EpCfg(ctypes.Structure):
@@ -69,7 +70,9 @@ def lib():
         L.ep_combine_bwd.argtypes = [cfg_p, lay_p, P, P, P, P]
         L.ep_combine_bwd_probs.argtypes = [cfg_p, lay_p, P, P, P, P]
         L.ep_dispatch_fp8.argtypes = [cfg_p, lay_p, P, P, P, P]
-        for name in SYMBOLS[:9]:
+        L.ep_indices_to_multihot.argtypes = [cfg_p, P, P, P, P, P]
+        L.ep_multihot_to_indices.argtypes = [cfg_p, P, P, P, P, P, P]
+        for name in SYMBOLS[:11]:
             getattr(L, name).restype = I
         L.ep_strerror.argtypes = [I]
         L.ep_strerror.restype = ctypes.c_char_p

@@ -316,4 +316,51 @@ int ep_combine_bwd_probs(const ep_cfg_t* cfg, const ep_layout_t* layout, const u
     return status_of(launch_probs_grad(m, grad_probs, static_cast<hipStream_t>(stream)));
 }
 
+int ep_indices_to_multihot(const ep_cfg_t* cfg, const int32_t* topk_ids, const float* probs,
+                           uint8_t* routing_map, float* dense_probs, void* stream) {
+    Shape d;
+    int rc = derive(cfg, &d);
+    if (rc != EP_OK) return rc;
+    if (bad_buffer(topk_ids, (int64_t)d.T * d.K * 4, 4) || bad_buffer(routing_map, (int64_t)d.T * d.E, 1))
+        return EP_EINVAL;
+    if (dense_probs != nullptr && (bad_buffer(dense_probs, (int64_t)d.T * d.E * 4, 4) ||
+                                   bad_buffer(probs, (int64_t)d.T * d.K * 4, 4)))
+        return EP_EINVAL;
+    if ((rc = check_device()) != EP_OK) return rc;
+    RouteArgs a;
+    a.ids = const_cast<int32_t*>(topk_ids);
+    a.probs = dense_probs != nullptr ? const_cast<float*>(probs) : nullptr;
+    a.map = routing_map;
+    a.dense_probs = dense_probs;
+    a.flags = nullptr;
+    a.T = d.T;
+    a.K = d.K;
+    a.E = d.E;
+    return status_of(launch_indices_to_multihot(a, static_cast<hipStream_t>(stream)));
+}
+
+int ep_multihot_to_indices(const ep_cfg_t* cfg, const uint8_t* routing_map, const float* dense_probs,
+                           int32_t* topk_ids, float* probs, int32_t* flags, void* stream) {
+    Shape d;
+    int rc = derive(cfg, &d);
+    if (rc != EP_OK) return rc;
+    if (bad_buffer(routing_map, (int64_t)d.T * d.E, 1) || bad_buffer(topk_ids, (int64_t)d.T * d.K * 4, 4))
+        return EP_EINVAL;
+    if (probs != nullptr && (bad_buffer(probs, (int64_t)d.T * d.K * 4, 4) ||
+                             bad_buffer(dense_probs, (int64_t)d.T * d.E * 4, 4)))
+        return EP_EINVAL;
+    if (flags != nullptr && misaligned(flags, 4)) return EP_EINVAL;
+    if ((rc = check_device()) != EP_OK) return rc;
+    RouteArgs a;
+    a.ids = topk_ids;
+    a.probs = probs;
+    a.map = const_cast<uint8_t*>(routing_map);
+    a.dense_probs = probs != nullptr ? const_cast<float*>(dense_probs) : nullptr;
+    a.flags = flags;
+    a.T = d.T;
+    a.K = d.K;
+    a.E = d.E;
+    return status_of(launch_multihot_to_indices(a, static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

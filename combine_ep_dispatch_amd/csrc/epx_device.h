@@ -154,6 +154,17 @@ struct Fp8Args {
 hipError_t launch_fp8(const Fp8Args& a, hipStream_t stream);
 int fp8_max_hidden();
 
+struct RouteArgs {
+    int32_t* ids;         // [T, K]
+    float* probs;         // [T, K] or nullptr
+    uint8_t* map;         // [T, E]
+    float* dense_probs;   // [T, E] or nullptr
+    int32_t* flags;       // OR-ed with EP_FLAG_MAP_OVERFLOW, or nullptr
+    int32_t T, K, E;
+};
+hipError_t launch_indices_to_multihot(const RouteArgs& a, hipStream_t stream);
+hipError_t launch_multihot_to_indices(const RouteArgs& a, hipStream_t stream);
+
 // Zero the payload bytes of every pad row ([count, align_up(count)) of each
 // group, below capacity).  row_bytes = bytes of one row of `base`.
 hipError_t launch_zero_pad_rows(void* base, int64_t row_bytes, const ep_layout_t& L, int32_t S,

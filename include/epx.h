@@ -64,6 +64,7 @@ extern "C" {
 #define EP_FLAG_DROPPED 1      /* a slot was dropped at segment capacity [TD]  */
 #define EP_FLAG_BAD_ID 2       /* an expert id outside [-1, E) (slot masked)   */
 #define EP_FLAG_INTERNAL 4     /* the layout scan gave up waiting (never seen) */
+#define EP_FLAG_MAP_OVERFLOW 8 /* a routing-map row marked more than top_k experts */
 
 /* Largest number of groups S * (E/S + shared_expert) a layout may have. */
 #define EP_MAX_GROUPS 2048
@@ -256,6 +257,34 @@ int ep_combine_bwd(const ep_cfg_t* cfg, const ep_layout_t* layout, const uint16_
  */
 int ep_combine_bwd_probs(const ep_cfg_t* cfg, const ep_layout_t* layout, const uint16_t* grad_y,
                          const uint16_t* expert_out, float* grad_probs, void* stream);
+
+/*
+ * Compact top-k -> dense routing form ([TD] _HybridEPManager._indices_to_multihot;
+ * [FA] HybridEPDispatch.forward accepts a Boolean routing map [tokens,
+ * experts] with dense probabilities).  Only the fields T, E, K (and their
+ * validity) of cfg are used.
+ *   topk_ids     int32 [T, K]; -1 and ids outside [0, E) mark nothing
+ *   probs        float [T, K]; required iff dense_probs is not NULL
+ *   routing_map  uint8 [T, E]: 1 where some slot names the expert, else 0
+ *   dense_probs  float [T, E] or NULL: sum of the probabilities of the slots
+ *                naming the expert, added in slot order; 0 elsewhere
+ */
+int ep_indices_to_multihot(const ep_cfg_t* cfg, const int32_t* topk_ids, const float* probs,
+                           uint8_t* routing_map, float* dense_probs, void* stream);
+
+/*
+ * Dense routing form -> compact top-k (the reverse; [FA] routing_map takes
+ * precedence over topk_idx, so a caller holding both converts the map).
+ *   routing_map  uint8 [T, E]; any nonzero byte marks the expert
+ *   dense_probs  float [T, E]; required iff probs is not NULL
+ *   topk_ids     int32 [T, K]: the marked experts in ascending order, then -1
+ *   probs        float [T, K] or NULL: their dense probabilities, then 0
+ *   flags        int32 [1] or NULL: OR-ed with EP_FLAG_MAP_OVERFLOW when a
+ *                row marks more than K experts (the lowest K are kept); the
+ *                caller clears it
+ */
+int ep_multihot_to_indices(const ep_cfg_t* cfg, const uint8_t* routing_map, const float* dense_probs,
+                           int32_t* topk_ids, float* probs, int32_t* flags, void* stream);
 
 /* Static description of a status code. */
 const char* ep_strerror(int status);
