@@ -189,3 +189,41 @@ def test_product_package_does_not_touch_the_oracle():
                 text = open(os.path.join(dirpath, f)).read()
                 assert "import oracle" not in text and "from oracle" not in text, f
                 assert "liboracle" not in text, f
+
+
+def test_new_entry_points_reject_bad_arguments(L):
+    from combine_ep_dispatch_amd._lib import EpLayout
+
+    c = cfg(hidden=256)
+    st, rows, ws, g = query(L, c)
+    fake = 0x10000  # never dereferenced: every call below fails validation first
+    lay = EpLayout(*([fake] * 8))
+    c.recv_rows = rows
+    cc = c.to_c()
+    # combine_bwd_probs: missing / misaligned buffers, too few rows
+    assert L.ep_combine_bwd_probs(ctypes.byref(cc), ctypes.byref(lay), fake, fake, None, None) == -1
+    assert L.ep_combine_bwd_probs(ctypes.byref(cc), ctypes.byref(lay), fake + 2, fake, fake, None) == -1
+    assert L.ep_combine_bwd_probs(ctypes.byref(cc), ctypes.byref(lay), fake, fake, fake + 2, None) == -1
+    assert L.ep_combine_bwd_probs(ctypes.byref(cc), None, fake, fake, fake, None) == -1
+    # fp8 dispatch: H must be a multiple of 128 and at most 16384
+    assert L.ep_dispatch_fp8(ctypes.byref(cc), ctypes.byref(lay), fake, fake, None, None) == -1
+    assert L.ep_dispatch_fp8(ctypes.byref(cc), ctypes.byref(lay), fake, fake + 8, fake, None) == -1
+    for h in (192, 16384 + 128):
+        ch = cfg(hidden=h)
+        ch.recv_rows = rows
+        cch = ch.to_c()
+        assert L.ep_dispatch_fp8(ctypes.byref(cch), ctypes.byref(lay), fake, fake, fake, None) == -1
+    short = cfg(hidden=256)
+    short.recv_rows = rows - 1
+    cs = short.to_c()
+    assert L.ep_dispatch_fp8(ctypes.byref(cs), ctypes.byref(lay), fake, fake, fake, None) == -1
+    assert L.ep_combine_bwd_probs(ctypes.byref(cs), ctypes.byref(lay), fake, fake, fake, None) == -1
+    # routing-map conversions: dense probabilities need compact ones and vice versa
+    assert L.ep_indices_to_multihot(ctypes.byref(cc), None, None, fake, None, None) == -1
+    assert L.ep_indices_to_multihot(ctypes.byref(cc), fake, None, None, None, None) == -1
+    assert L.ep_indices_to_multihot(ctypes.byref(cc), fake, None, fake, fake, None) == -1
+    assert L.ep_indices_to_multihot(ctypes.byref(cc), fake + 1, fake, fake, fake, None) == -1
+    assert L.ep_multihot_to_indices(ctypes.byref(cc), None, None, fake, None, None, None) == -1
+    assert L.ep_multihot_to_indices(ctypes.byref(cc), fake, None, fake, fake, None, None) == -1
+    assert L.ep_multihot_to_indices(ctypes.byref(cc), fake, fake, fake, fake, fake + 2, None) == -1
+    assert L.ep_multihot_to_indices(None, fake, fake, fake, fake, None, None) == -1
