@@ -42,7 +42,8 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, published
 METRIC = "dispatch+combine tokens/s and effective HBM GB/s (% of peak), 1 MI355X"
 KERNEL_SOURCES = ("combine_ep_dispatch_amd/csrc/move.hip", "combine_ep_dispatch_amd/csrc/nvfp4.hip",
-                  "combine_ep_dispatch_amd/csrc/layout.hip", "combine_ep_dispatch_amd/csrc/epx_device.h")
+                  "combine_ep_dispatch_amd/csrc/layout.hip", "combine_ep_dispatch_amd/csrc/fp8.hip",
+                  "combine_ep_dispatch_amd/csrc/epx_device.h")
 
 
 def log(*a):

@@ -1,0 +1,104 @@
+"""Autograd wrappers over the C ABI, shaped after the forward/backward pairs
+the NeMo AutoModel fused_a2a page documents (HybridEPDispatch: dispatch
+forward, combine-of-gradients backward; HybridEPCombine: combine forward,
+redispatch backward).
+
+Marshalling only: every step runs in libepx's HIP kernels.
+
+    d = EpDispatcher(cfg, device)            # owns layout, workspace, buffers
+    recv = d.dispatch(x, topk_ids)           # [R, H] bf16, differentiable in x
+    y = d.combine(expert_out, probs)         # [T, H] bf16, differentiable in
+                                             # expert_out and probs
+    y.backward(grad)                         # -> x.grad, expert_out.grad, probs.grad
+
+dispatch() builds the layout (the "handle") and keeps it for the combine
+and both backward passes; rows past a segment's used rows are left as the
+buffers held them (zero for the buffers allocated here).  The routing is
+not differentiable; probs is, through the router-probability gradient.
+"""
+
+from __future__ import annotations
+
+from typing import Optional
+
+import torch
+
+from . import (EpConfig, Layout, ep_combine, ep_combine_bwd, ep_combine_bwd_probs, ep_dispatch,
+               ep_dispatch_bwd, ep_dispatch_layout, ep_query, workspace_for)
+
+__all__ = ["EpDispatcher"]
+
+
+class _Dispatch(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, x, disp):
+        recv = torch.zeros(disp.cfg.recv_rows, disp.cfg.hidden, dtype=torch.bfloat16, device=x.device)
+        ep_dispatch(disp.cfg, disp.layout, x.contiguous().view(-1), recv.view(-1))
+        ctx.disp = disp
+        return recv
+
+    @staticmethod
+    def backward(ctx, grad_recv):
+        disp = ctx.disp
+        gx = torch.empty(disp.cfg.num_tokens, disp.cfg.hidden, dtype=torch.bfloat16, device=grad_recv.device)
+        ep_dispatch_bwd(disp.cfg, disp.layout, grad_recv.to(torch.bfloat16).contiguous().view(-1), gx.view(-1))
+        return gx, None
+
+
+class _Combine(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, expert_out, probs, disp):
+        cfg = disp.cfg
+        y = torch.empty(cfg.num_tokens, cfg.hidden, dtype=torch.bfloat16, device=expert_out.device)
+        eo = expert_out.contiguous()
+        p = None if probs is None else probs.contiguous().float()
+        ep_combine(cfg, disp.layout, eo.view(-1), None if p is None else p.view(-1), y.view(-1))
+        ctx.disp = disp
+        ctx.has_probs = probs is not None
+        ctx.save_for_backward(eo, p if p is not None else torch.empty(0, device=eo.device))
+        return y
+
+    @staticmethod
+    def backward(ctx, grad_y):
+        disp = ctx.disp
+        cfg = disp.cfg
+        eo, p = ctx.saved_tensors
+        gy = grad_y.to(torch.bfloat16).contiguous()
+        g_out = torch.zeros(cfg.recv_rows, cfg.hidden, dtype=torch.bfloat16, device=gy.device)
+        ep_combine_bwd(cfg, disp.layout, gy.view(-1), p.view(-1) if ctx.has_probs else None, g_out.view(-1))
+        g_probs = None
+        if ctx.has_probs and ctx.needs_input_grad[1]:
+            g_probs = torch.empty(cfg.num_tokens, cfg.top_k, dtype=torch.float32, device=gy.device)
+            ep_combine_bwd_probs(cfg, disp.layout, gy.view(-1), eo.view(-1), g_probs.view(-1))
+        return g_out, g_probs, None
+
+
+class EpDispatcher:
+    """Dispatch / combine with autograd for one configuration on one device."""
+
+    def __init__(self, cfg: EpConfig, device, recv_rows: Optional[int] = None):
+        q = ep_query(cfg)
+        cfg.recv_rows = q.min_recv_rows if recv_rows is None else recv_rows
+        self.cfg = cfg
+        self.device = torch.device(device)
+        self.layout = Layout.empty(cfg, self.device)
+        self.workspace = workspace_for(cfg, self.device)
+
+    def route(self, topk_ids: torch.Tensor) -> Layout:
+        """Build the layout (counts, offsets, token_row, expert_ids, src_info, flags)."""
+        ep_dispatch_layout(self.cfg, topk_ids.to(torch.int32).contiguous().view(-1), self.workspace, self.layout)
+        return self.layout
+
+    def dispatch(self, x: torch.Tensor, topk_ids: Optional[torch.Tensor] = None) -> torch.Tensor:
+        """[T, H] bf16 -> [R, H] bf16 receive rows; routes first when topk_ids is given."""
+        if topk_ids is not None:
+            self.route(topk_ids)
+        return _Dispatch.apply(x, self)
+
+    def combine(self, expert_out: torch.Tensor, probs: Optional[torch.Tensor]) -> torch.Tensor:
+        """[R, H] bf16 expert outputs -> [T, H] bf16, weighted by probs [T, K] (or 1)."""
+        return _Combine.apply(expert_out, probs, self)
+
+    def tokens_per_expert(self) -> torch.Tensor:
+        """Routed rows per group [S, G] (the shared group included)."""
+        return self.layout.counts

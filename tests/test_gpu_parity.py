@@ -310,3 +310,41 @@ def test_graph_replays_match_eager(G):
             else:
                 a, b = v, ref[k]
             assert torch.equal(a, b), (i, k)
+
+
+def test_autograd_dispatcher_matches_fp64_reference(G):
+    """EpDispatcher: dispatch -> (x2) -> combine with autograd, against torch
+    fp64 autograd of an index_select / index_add formulation on the oracle's
+    layout (CPU).  Gradients pass through bf16 roundings on the GPU path,
+    hence the 2^-7 relative tolerance."""
+    from combine_ep_dispatch_amd.autograd import EpDispatcher
+
+    c = G.random_case(41, T=300, S=4, E_loc=6, K=4, H=256, A=8, shared=1, src=2, mask_p=0.1)
+    cfg = G.epx.EpConfig(num_tokens=c.cfg.num_tokens, hidden=c.cfg.hidden, num_experts=c.cfg.num_experts,
+                         num_segments=c.cfg.num_segments, top_k=c.cfg.top_k, align=c.cfg.align,
+                         shared_expert=1, src_segment=2)
+    d = EpDispatcher(cfg, G.DEV)
+    T, H, K = cfg.num_tokens, cfg.hidden, cfg.top_k
+    x = G.u16_tensor(c.x).view(T, H).clone().requires_grad_(True)
+    probs = torch.from_numpy(c.probs).to(G.DEV).requires_grad_(True)
+    ids = torch.from_numpy(c.ids).to(G.DEV)
+    recv = d.dispatch(x, ids)
+    expert_out = recv * 2.0
+    y = d.combine(expert_out, probs)
+    gy = G.u16_tensor(G.wl.make_tensor_like_rows(T, H, 9)).view(T, H)
+    (y.float() * gy.float()).sum().backward()
+    torch.cuda.synchronize()
+    assert np.array_equal(d.layout.token_row.cpu().numpy(), c.L["token_row"])
+
+    tr = torch.from_numpy(c.L["token_row"].astype(np.int64))
+    xr = torch.from_numpy(G.f32(c.x).astype(np.float64)).requires_grad_(True)
+    pr = torch.from_numpy(c.probs.astype(np.float64)).requires_grad_(True)
+    yr = torch.zeros(T, H, dtype=torch.float64)
+    for k in range(cfg.kp):
+        ok = tr[:, k] >= 0
+        w = pr[:, k] if k < K else torch.ones(T, dtype=torch.float64)
+        yr = yr + torch.where(ok[:, None], w[:, None] * 2.0 * xr, torch.zeros(()))
+    (yr * torch.from_numpy(G.f32(G.bits_of(gy)).reshape(T, H).astype(np.float64))).sum().backward()
+    assert np.allclose(y.detach().float().cpu().numpy(), yr.detach().numpy(), rtol=2 ** -7, atol=1e-5)
+    assert np.allclose(x.grad.float().cpu().numpy(), xr.grad.numpy(), rtol=2 ** -6, atol=1e-4)
+    assert np.allclose(probs.grad.cpu().numpy(), pr.grad.numpy(), rtol=1e-3, atol=1e-3)
