@@ -16,7 +16,13 @@
 //
 // Arithmetic is IEEE binary32 with round-to-nearest-even everywhere; the
 // library is built with correctly rounded division and without FMA
-// contraction, so the results are bit-identical to the plain definition:
+// contraction, so the results are bit-identical to the plain definition.
+// The E2M1 encode is gfx950's v_cvt_scalef32_pk_fp4_f32 with scale 1, two
+// elements per instruction: on every finite and infinite input it is the
+// RNE, ties-to-even, saturating, sign-kept encode below (checked over all
+// 2^32 float patterns).  It turns NaN into code 7, so a block whose
+// per-element factor g / e4m3(s) overflowed (a row max below 2688/FLT_MAX,
+// where 0 * inf can occur) takes the threshold encoder instead:
 //   s = (bmax / 6) * g            -> E4M3, RNE, saturating to 448
 //   v = x * (g / e4m3(s))         -> E2M1, RNE (ties to even), saturating
 //                                   at 6, sign bit of v kept
@@ -51,6 +57,22 @@ __device__ __forceinline__ uint32_t codes_of_word(uint32_t w, float inv) {
     const uint32_t c0 = e2m1_encode(bf16_lo(w) * inv);
     const uint32_t c1 = e2m1_encode(bf16_hi(w) * inv);
     return c0 | (c1 << 4);
+}
+
+// Eight codes (words w0..w3) by the hardware conversion: operand a fills the
+// low nibble of the selected byte, operand b the high one.
+__device__ __forceinline__ uint32_t codes_of_words_hw(const uint4& w, float inv) {
+    uint32_t r = 0;
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, bf16_lo(w.x) * inv, bf16_hi(w.x) * inv, 1.0f, 0);
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, bf16_lo(w.y) * inv, bf16_hi(w.y) * inv, 1.0f, 1);
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, bf16_lo(w.z) * inv, bf16_hi(w.z) * inv, 1.0f, 2);
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, bf16_lo(w.w) * inv, bf16_hi(w.w) * inv, 1.0f, 3);
+    return r;
+}
+
+__device__ __forceinline__ uint32_t codes_of_words_sw(const uint4& w, float inv) {
+    return codes_of_word(w.x, inv) | (codes_of_word(w.y, inv) << 8) | (codes_of_word(w.z, inv) << 16) |
+           (codes_of_word(w.w, inv) << 24);
 }
 
 template <int NBL>
@@ -112,10 +134,13 @@ __global__ __launch_bounds__(kQuantThreads) void k_nvfp4(Nvfp4Args a) {
                 code[i] = make_uint2(0, 0);
             } else {
                 const float inv = g / sq;
-                code[i].x = codes_of_word(q[i][0].x, inv) | (codes_of_word(q[i][0].y, inv) << 8) |
-                            (codes_of_word(q[i][0].z, inv) << 16) | (codes_of_word(q[i][0].w, inv) << 24);
-                code[i].y = codes_of_word(q[i][1].x, inv) | (codes_of_word(q[i][1].y, inv) << 8) |
-                            (codes_of_word(q[i][1].z, inv) << 16) | (codes_of_word(q[i][1].w, inv) << 24);
+                if (inv <= __FLT_MAX__) {
+                    code[i].x = codes_of_words_hw(q[i][0], inv);
+                    code[i].y = codes_of_words_hw(q[i][1], inv);
+                } else {
+                    code[i].x = codes_of_words_sw(q[i][0], inv);
+                    code[i].y = codes_of_words_sw(q[i][1], inv);
+                }
             }
         }
         rs = f32_to_bf16(1.0f / g);
