@@ -24,13 +24,16 @@
 #include "epx_device.h"
 
 #ifndef EPX_SCATTER_VPL
-#define EPX_SCATTER_VPL 2
+#define EPX_SCATTER_VPL 1
 #endif
 #ifndef EPX_GATHER_VPL
 #define EPX_GATHER_VPL 1
 #endif
 #ifndef EPX_NT_LOADS
 #define EPX_NT_LOADS 1
+#endif
+#ifndef EPX_SCATTER_NT_LOADS
+#define EPX_SCATTER_NT_LOADS 0
 #endif
 #ifndef EPX_NT_STORES
 #define EPX_NT_STORES 0
@@ -47,6 +50,14 @@ typedef uint32_t v4u __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ v4u load_stream(const v4u* p) {
 #if EPX_NT_LOADS
+    return __builtin_nontemporal_load(p);
+#else
+    return *p;
+#endif
+}
+
+__device__ __forceinline__ v4u load_scatter_src(const v4u* p) {
+#if EPX_SCATTER_NT_LOADS
     return __builtin_nontemporal_load(p);
 #else
     return *p;
@@ -103,7 +114,7 @@ __global__ __launch_bounds__(kMoveThreads) void k_scatter(MoveArgs a, int32_t Hv
 #pragma unroll
     for (int i = 0; i < VPL; ++i) {
         const int32_t v = v0 + i * kWave;
-        if (FULL || v < Hv) buf[i] = load_stream(src + v);
+        if (FULL || v < Hv) buf[i] = load_scatter_src(src + v);
         else buf[i] = v4u{0, 0, 0, 0};
     }
     for (int32_t k = 0; k < a.Kp; ++k) {
