@@ -26,6 +26,7 @@ rocprofv3 FETCH_SIZE / WRITE_SIZE counters to bytes.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import os
@@ -85,7 +86,9 @@ def algorithmic_bytes(w, kept: int, used_rows: int, kept_routed: int = None) -> 
         "combine": row * kept + row * T + 4 * T * K + 4 * T * Kp,
         "combine_bwd": row * T + row * kept + 4 * T * K + 4 * T * Kp,
         "dispatch_bwd": row * kept + row * T + 4 * T * Kp,
-        # not part of the step: the router-probability gradient and FP8 dispatch
+        # not part of the step: the layout on its decoupled look-back path, the
+        # router-probability gradient and FP8 dispatch
+        "layout_lookback": 4 * T * K + 4 * T * Kp + 12 * used_rows,
         "combine_bwd_probs": row * T + row * kept_routed + 4 * T * Kp + 4 * T * K,
         "dispatch_fp8": row * T + kept * (H + 4 * (H // 128)) + 4 * T * Kp,
     }
@@ -192,7 +195,11 @@ def main() -> int:
     gprobs = torch.empty(T * w.K, dtype=torch.float32, device=dev)
     fp8_codes = torch.empty(R * H, dtype=torch.uint8, device=dev)
     fp8_scales = torch.empty(R * (H // 128), dtype=torch.float32, device=dev)
-    extra_ops = [("combine_bwd_probs", lambda: epx.ep_combine_bwd_probs(cfg, lay, gy, out, gprobs)),
+    cfg_lb = dataclasses.replace(cfg, flags=cfg.flags | epx.EP_LAYOUT_LOOKBACK)
+    lay_lb = epx.Layout.empty(cfg_lb, dev)
+    ws_lb = epx.workspace_for(cfg_lb, dev)
+    extra_ops = [("layout_lookback", lambda: epx.ep_dispatch_layout(cfg_lb, ids, ws_lb, lay_lb)),
+                 ("combine_bwd_probs", lambda: epx.ep_combine_bwd_probs(cfg, lay, gy, out, gprobs)),
                  ("dispatch_fp8", lambda: epx.ep_dispatch_fp8(cfg, lay, x, fp8_codes, fp8_scales))]
 
     def step():
@@ -257,6 +264,16 @@ def main() -> int:
     kept = int((tr >= 0).sum())
     rowoff = lay.row_offsets.cpu().numpy()
     used_rows = int(rowoff[:, -1].sum())
+    seg_base = lay.seg_base.cpu().numpy()
+    used = np.zeros(R, bool)  # rows past a segment's used rows are never written
+    for s_ in range(w.S):
+        used[seg_base[s_]:seg_base[s_] + rowoff[s_, -1]] = True
+    for k in ("counts", "seg_base", "row_offsets", "token_row", "flags", "expert_ids", "src_info"):
+        a, b = getattr(lay, k).cpu().numpy(), getattr(lay_lb, k).cpu().numpy()
+        if k in ("expert_ids", "src_info"):
+            a, b = a[used], b[used]
+        if not np.array_equal(a, b):
+            raise RuntimeError(f"the look-back layout differs from the direct one in {k}")
     kept_routed = int((tr[:, :w.K] >= 0).sum())
     nbytes = algorithmic_bytes(w, kept, used_rows, kept_routed)
     per_op = {}

@@ -28,12 +28,12 @@ import torch
 
 from . import _lib
 from ._lib import (EP_FLAG_BAD_ID, EP_FLAG_DROPPED, EP_FLAG_INTERNAL, EP_FLAG_MAP_OVERFLOW,  # noqa: F401
-                   EP_ZERO_PAD_ROWS, EpCfg, EpLayout)
+                   EP_ZERO_PAD_ROWS, EP_LAYOUT_LOOKBACK, EpCfg, EpLayout)
 
 __all__ = [
     "EpConfig", "Layout", "QueryResult", "ep_query", "workspace_for", "ep_dispatch_layout",
     "ep_dispatch", "ep_dispatch_nvfp4", "ep_dispatch_fp8", "ep_combine", "ep_dispatch_bwd", "ep_combine_bwd",
-    "ep_combine_bwd_probs", "ep_indices_to_multihot", "ep_multihot_to_indices", "assert_no_overflow", "EpError", "abi_version", "EP_ZERO_PAD_ROWS", "EP_FLAG_DROPPED",
+    "ep_combine_bwd_probs", "ep_indices_to_multihot", "ep_multihot_to_indices", "assert_no_overflow", "EpError", "abi_version", "EP_ZERO_PAD_ROWS", "EP_LAYOUT_LOOKBACK", "EP_FLAG_DROPPED",
     "EP_FLAG_BAD_ID", "EP_FLAG_INTERNAL",
 ]
 

@@ -16,6 +16,7 @@ EP_EINVAL = -1
 EP_ELAUNCH = -2
 EP_ENOTSUP = -3
 EP_ZERO_PAD_ROWS = 1
+EP_LAYOUT_LOOKBACK = 2
 EP_FLAG_DROPPED = 1
 EP_FLAG_BAD_ID = 2
 EP_FLAG_INTERNAL = 4

@@ -35,7 +35,7 @@ int derive(const ep_cfg_t* c, Shape* d) {
     if (c->shared_expert != 0 && c->shared_expert != 1) return EP_EINVAL;
     if (c->shared_expert && (c->src_segment < 0 || c->src_segment >= c->num_segments)) return EP_EINVAL;
     if (c->reserved0 != 0 || c->reserved1 != 0) return EP_EINVAL;
-    if (c->flags & ~EP_ZERO_PAD_ROWS) return EP_EINVAL;
+    if (c->flags & ~(EP_ZERO_PAD_ROWS | EP_LAYOUT_LOOKBACK)) return EP_EINVAL;
     d->T = c->num_tokens;
     d->H = c->hidden;
     d->E = c->num_experts;
@@ -62,7 +62,7 @@ int derive(const ep_cfg_t* c, Shape* d) {
     }
     if (d->min_rows >= (int64_t(1) << 31)) return EP_EINVAL;  // rows are int32
     d->tiles = layout_tiles((int64_t)d->T * d->K);
-    d->ws_bytes = kWorkspaceHeader + d->tiles * (int64_t)d->NG * 4;
+    d->ws_bytes = kWorkspaceHeader + layout_tiles_padded(d->tiles) * (int64_t)d->NG * 4;
     d->R = c->recv_rows;
     d->flags = c->flags;
     return EP_OK;
@@ -185,6 +185,8 @@ int ep_dispatch_layout(const ep_cfg_t* cfg, const int32_t* topk_ids, void* works
     a.src_seg = d.src;
     a.recv_rows = d.R;
     a.tiles = (int32_t)d.tiles;
+    a.tiles_pad = (int32_t)layout_tiles_padded(d.tiles);
+    a.direct = layout_direct(d.tiles) && !(d.flags & EP_LAYOUT_LOOKBACK);
     a.slots_per_thread = layout_slots_per_thread((int64_t)d.T * d.K);
     return status_of(launch_layout(a, static_cast<hipStream_t>(stream)));
 }

@@ -13,32 +13,43 @@
 //    row_offsets, expert_ids per received token, src_info, atomic counters
 //    coordinating work across thread blocks.
 //
-// Three launches on the caller's stream:
-//  1. k_layout_clear  zero the counts (the shared group gets T) and the flags
-//                     word.
-//  2. k_layout_hist   per tile of 256 x {2,4,8} routed slots (chosen so that
+// Two launches on the caller's stream (the direct path, up to
+// kDirectMaxTiles tiles; every configuration up to ~500k routed slots):
+//  1. k_layout_hist   per tile of 256 x {2,4,8} routed slots (chosen so that
 //                     there are about 64 tiles), a wave64 match-any over
 //                     the group key (one ballot per key bit); the lowest lane
 //                     of each match set adds the set's popcount into an LDS
 //                     counter, so a hot expert costs one LDS atomic per wave
-//                     instead of one per slot.  Each tile publishes its
-//                     per-group aggregate as a look-back descriptor (tile 0
-//                     publishes its inclusive prefix directly) and adds its
-//                     nonzero counters into `counts`.
-//  3. k_layout_rank   single pass: every workgroup scans the aligned group
-//                     sizes (from the finished counts) into group start
+//                     instead of one per slot.  Each tile stores its
+//                     per-group counts into a group-major [group][tile]
+//                     table; tile 0 also clears the flags word.
+//  2. k_layout_rank   every workgroup reads, for each group, the group's row
+//                     of tile counts with 16-byte loads (one round trip for
+//                     up to 64 tiles) and sums it twice: over all tiles (the
+//                     group total) and over the tiles before its own (its
+//                     in-group prefix).  No workgroup waits on another, and
+//                     there are no atomics on global memory but the flags.
+//                     It then scans the aligned group sizes into group start
 //                     rows, ranks its tile's slots inside their groups
-//                     (per-wave running counters in LDS + match-any),
-//                     resolves its per-group prefix over earlier tiles by
-//                     decoupled look-back (16 predecessor descriptors per
-//                     round trip, folded nearest-first until an inclusive
-//                     prefix is met), upgrades its own descriptors to
-//                     inclusive prefixes for the tiles after it, and writes
-//                     token_row, expert_ids and src_info.  Pad-row metadata
-//                     and the fused shared-expert rows are spread over the
-//                     tiles.  Every aggregate is published by the previous
-//                     launch, so no workgroup ever waits on another one and
-//                     tiles need no ordering ticket.
+//                     (per-wave running counters in LDS + match-any), and
+//                     writes counts (tile 0), offsets, token_row, expert_ids
+//                     and src_info.  Pad-row metadata and the fused
+//                     shared-expert rows are spread over the tiles.
+// Above kDirectMaxTiles the per-workgroup row sums would grow with the tile
+// count, so three launches are used instead (also on request, with
+// EP_LAYOUT_LOOKBACK; the results are the same):
+//  0. k_layout_clear  zero the counts (the shared group gets T) and flags.
+//  1. k_layout_hist   publishes each tile's per-group aggregate as a
+//                     look-back descriptor ([tile][group], 2 status bits
+//                     over a 30-bit count; tile 0 publishes its inclusive
+//                     prefix) and adds its nonzero counters into `counts`.
+//  2. k_layout_rank   resolves its per-group prefix by decoupled look-back
+//                     (16 predecessor descriptors per round trip, folded
+//                     nearest-first until an inclusive prefix is met) and
+//                     upgrades its own descriptors to inclusive prefixes.
+//                     Every aggregate is published by the previous launch,
+//                     so no workgroup ever waits on another one.
+// Invalid ids are detected where the slots are ranked (k_layout_rank).
 #include "epx_device.h"
 
 namespace epx {
@@ -65,23 +76,20 @@ __global__ __launch_bounds__(256) void k_layout_clear(LayoutArgs a) {
     if (threadIdx.x == 0) a.out.flags[0] = 0;
 }
 
-template <int SPT>
+template <int SPT, bool DIRECT>
 __global__ __launch_bounds__(kLayoutThreads) void k_layout_hist(LayoutArgs a) {
     constexpr int kTileSlots = kLayoutThreads * SPT;
     __shared__ int32_t s_hist[EP_MAX_GROUPS];
     __shared__ int32_t s_gof[EP_MAX_GROUPS];  // group of each routed expert
-    __shared__ int32_t s_bad;
     const int tid = threadIdx.x;
     for (int g = tid; g < a.NG; g += kLayoutThreads) s_hist[g] = 0;
     for (int e = tid; e < a.E; e += kLayoutThreads)
         s_gof[e] = (e / a.E_loc) * a.G + a.shared + (e % a.E_loc);
-    if (tid == 0) s_bad = 0;
     __syncthreads();
 
     const int64_t routed = (int64_t)a.T * a.K;
     const int nbits = 32 - __clz(a.NG);  // keys live in [0, NG]; NG = "no group"
     const int64_t base = (int64_t)blockIdx.x * kTileSlots;
-    bool bad = false;
 #pragma unroll
     for (int it = 0; it < SPT; ++it) {
         const int64_t f = base + it * kLayoutThreads + tid;
@@ -89,25 +97,28 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout_hist(LayoutArgs a) {
         if (f < routed) {
             const int32_t e = a.topk_ids[f];
             if ((uint32_t)e < (uint32_t)a.E) key = (uint32_t)s_gof[e];
-            else if (e != -1) bad = true;
         }
         const uint64_t m = match_any(key, nbits);
         if (key != (uint32_t)a.NG && lanes_below(m) == 0)
             atomicAdd(&s_hist[key], (int32_t)__popcll(m));
     }
-    if (bad) s_bad = 1;
     __syncthreads();
-    const uint32_t status = blockIdx.x == 0 ? kDescInc : kDescAgg;  // tile 0: prefix 0 + aggregate
-    uint32_t* desc = a.desc + (int64_t)blockIdx.x * a.NG;
-    for (int g = tid; g < a.NG; g += kLayoutThreads) {
-        const int32_t c = s_hist[g];
-        desc_store(&desc[g], status | (uint32_t)c);
-        if (c) atomicAdd(&a.out.counts[g], c);
+    if (DIRECT) {
+        for (int g = tid; g < a.NG; g += kLayoutThreads)
+            a.desc[(int64_t)g * a.tiles_pad + blockIdx.x] = (uint32_t)s_hist[g];
+        if (blockIdx.x == 0 && tid == 0) a.out.flags[0] = 0;
+    } else {
+        const uint32_t status = blockIdx.x == 0 ? kDescInc : kDescAgg;  // tile 0: prefix 0 + aggregate
+        uint32_t* desc = a.desc + (int64_t)blockIdx.x * a.NG;
+        for (int g = tid; g < a.NG; g += kLayoutThreads) {
+            const int32_t c = s_hist[g];
+            desc_store(&desc[g], status | (uint32_t)c);
+            if (c) atomicAdd(&a.out.counts[g], c);
+        }
     }
-    if (tid == 0 && s_bad) atomicOr(a.out.flags, EP_FLAG_BAD_ID);
 }
 
-template <int SPT>
+template <int SPT, bool DIRECT>
 __global__ __launch_bounds__(kLayoutThreads) void k_layout_rank(LayoutArgs a) {
     constexpr int kTileSlots = kLayoutThreads * SPT;
     constexpr int kSlotsPerWave = kWave * SPT;
@@ -134,8 +145,37 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout_rank(LayoutArgs a) {
         const int64_t f = wslot0 + it * kWave + lane;
         eid[it] = f < routed ? a.topk_ids[f] : -1;
     }
+    const int32_t shared_group = a.shared ? a.src_seg * G : -1;
     if (tid == 0) s_flag = 0;
-    for (int g = tid; g < NG; g += kLayoutThreads) s_cnt[g] = a.out.counts[g];
+    if (DIRECT) {
+        // Group totals and this tile's in-group prefix from the [group][tile]
+        // table: 16-byte loads, up to 64 of them in flight per thread.
+        const int nq = a.tiles_pad / 4;
+        for (int g = tid; g < NG; g += kLayoutThreads) {
+            const uint4* row = reinterpret_cast<const uint4*>(a.desc + (int64_t)g * a.tiles_pad);
+            int32_t tot = 0, pre = 0;
+            for (int q0 = 0; q0 < nq; q0 += 16) {
+                uint4 v[16];
+#pragma unroll
+                for (int i = 0; i < 16; ++i) v[i] = q0 + i < nq ? row[q0 + i] : make_uint4(0, 0, 0, 0);
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int t4 = 4 * (q0 + i);
+                    const uint32_t c[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const int32_t n = t4 + j < a.tiles ? (int32_t)c[j] : 0;  // pad tiles hold garbage
+                        tot += n;
+                        pre += t4 + j < (int)tile ? n : 0;
+                    }
+                }
+            }
+            s_cnt[g] = tot + (g == shared_group ? a.T : 0);
+            s_pref[g] = pre;
+        }
+    } else {
+        for (int g = tid; g < NG; g += kLayoutThreads) s_cnt[g] = a.out.counts[g];
+    }
     for (int e = tid; e < a.E; e += kLayoutThreads)
         s_gof[e] = (e / a.E_loc) * G + a.shared + (e % a.E_loc);
 #pragma unroll
@@ -178,8 +218,10 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout_rank(LayoutArgs a) {
     }
     __syncthreads();
 
-    // Offsets and segment bases (one tile writes them).
+    // Counts (direct path), offsets and segment bases: one tile writes them.
     if (tile == 0) {
+        if (DIRECT)
+            for (int g = tid; g < NG; g += kLayoutThreads) a.out.counts[g] = s_cnt[g];
         const int n = a.S * (G + 1);
         for (int idx = tid; idx < n; idx += kLayoutThreads) {
             const int s = idx / (G + 1), gl = idx - s * (G + 1);
@@ -231,10 +273,12 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout_rank(LayoutArgs a) {
     // ---- in-tile ranks (per-wave running counters + match-any) ----
     const int nbits = 32 - __clz(NG);
     uint32_t key[SPT], rnk[SPT];
+    int32_t flag = 0;
 #pragma unroll
     for (int it = 0; it < SPT; ++it) {
         const int32_t e = eid[it];
         const uint32_t k = (uint32_t)e < (uint32_t)a.E ? (uint32_t)s_gof[e] : (uint32_t)NG;
+        if (e != -1 && (uint32_t)e >= (uint32_t)a.E) flag |= EP_FLAG_BAD_ID;  // -1 = masked slot
         const uint64_t m = match_any(k, nbits);
         const uint32_t r = lanes_below(m);
         rnk[it] = 0;
@@ -249,7 +293,6 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout_rank(LayoutArgs a) {
 
     // ---- per-wave exclusive prefixes and the tile aggregate per group ----
     int32_t agg[EP_MAX_GROUPS / kLayoutThreads];
-    const int32_t shared_group = a.shared ? a.src_seg * G : -1;
 #pragma unroll
     for (int j = 0; j < EP_MAX_GROUPS / kLayoutThreads; ++j) {
         const int g = tid + j * kLayoutThreads;
@@ -265,12 +308,11 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout_rank(LayoutArgs a) {
             agg[j] = run;
         }
     }
-    // ---- decoupled look-back over earlier tiles ----
-    int32_t lost = 0;
+    // ---- decoupled look-back over earlier tiles (look-back path only) ----
 #pragma unroll
     for (int j = 0; j < EP_MAX_GROUPS / kLayoutThreads; ++j) {
         const int g = tid + j * kLayoutThreads;
-        if (g >= NG) continue;
+        if (DIRECT || g >= NG) continue;
         uint32_t pref = 0;
         if (tile > 0 && s_cnt[g] > 0 && g != shared_group) {
             // Read a window of kLookback predecessors at once (independent
@@ -296,7 +338,7 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout_rank(LayoutArgs a) {
                     int spins = 0;
                     while ((di & ~kDescValue) == 0u) {  // not published yet
                         if (++spins > kMaxSpins) {
-                            lost = EP_FLAG_INTERNAL;
+                            flag |= EP_FLAG_INTERNAL;
                             di = kDescInc;
                             break;
                         }
@@ -314,7 +356,6 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout_rank(LayoutArgs a) {
     __syncthreads();
 
     // ---- write the routed slots of this tile ----
-    int32_t flag = lost;
     const uint32_t R = (uint32_t)a.recv_rows;
 #pragma unroll
     for (int it = 0; it < SPT; ++it) {
@@ -392,22 +433,25 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout_rank(LayoutArgs a) {
 
 }  // namespace
 
-hipError_t launch_layout(const LayoutArgs& a, hipStream_t stream) {
-    hipLaunchKernelGGL(k_layout_clear, dim3(1), dim3(256), 0, stream, a);
+template <int SPT, bool DIRECT>
+void launch_passes(const LayoutArgs& a, hipStream_t stream) {
     const dim3 grid((unsigned)a.tiles), block(kLayoutThreads);
+    if (!DIRECT) hipLaunchKernelGGL(k_layout_clear, dim3(1), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((k_layout_hist<SPT, DIRECT>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((k_layout_rank<SPT, DIRECT>), grid, block, 0, stream, a);
+}
+
+template <int SPT>
+void launch_spt(const LayoutArgs& a, hipStream_t stream) {
+    if (a.direct) launch_passes<SPT, true>(a, stream);
+    else launch_passes<SPT, false>(a, stream);
+}
+
+hipError_t launch_layout(const LayoutArgs& a, hipStream_t stream) {
     switch (a.slots_per_thread) {
-        case 2:
-            hipLaunchKernelGGL(k_layout_hist<2>, grid, block, 0, stream, a);
-            hipLaunchKernelGGL(k_layout_rank<2>, grid, block, 0, stream, a);
-            break;
-        case 4:
-            hipLaunchKernelGGL(k_layout_hist<4>, grid, block, 0, stream, a);
-            hipLaunchKernelGGL(k_layout_rank<4>, grid, block, 0, stream, a);
-            break;
-        default:
-            hipLaunchKernelGGL(k_layout_hist<8>, grid, block, 0, stream, a);
-            hipLaunchKernelGGL(k_layout_rank<8>, grid, block, 0, stream, a);
-            break;
+        case 2: launch_spt<2>(a, stream); break;
+        case 4: launch_spt<4>(a, stream); break;
+        default: launch_spt<8>(a, stream); break;
     }
     return hipGetLastError();
 }

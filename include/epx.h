@@ -58,7 +58,11 @@ extern "C" {
 #define EP_ENOTSUP (-3)  /* the current device is not gfx950                   */
 
 /* Bits of ep_cfg_t.flags. */
-#define EP_ZERO_PAD_ROWS 1u  /* also write zeros into the payload of pad rows */
+#define EP_ZERO_PAD_ROWS 1u    /* also write zeros into the payload of pad rows */
+#define EP_LAYOUT_LOOKBACK 2u  /* ep_dispatch_layout: resolve tile prefixes by
+                                  decoupled look-back even where the direct
+                                  tile-count sums apply (same results; selects
+                                  the kernel path) */
 
 /* Bits of the device flags word (ep_layout_t.flags[0]). */
 #define EP_FLAG_DROPPED 1      /* a slot was dropped at segment capacity [TD]  */
@@ -98,7 +102,7 @@ typedef struct ep_cfg_t {
                               src_info, recv, codes, ...); R >= ep_query's
                               min_recv_rows and R < 2^31.  A host integer, so no
                               call ever reads a count back from the device [FA]. */
-    uint32_t flags;        /* EP_ZERO_PAD_ROWS or 0                               */
+    uint32_t flags;        /* EP_ZERO_PAD_ROWS | EP_LAYOUT_LOOKBACK, or 0         */
     uint32_t reserved1;    /* must be 0                                           */
 } ep_cfg_t;
 
@@ -156,10 +160,14 @@ int ep_query(const ep_cfg_t* cfg, int64_t* min_recv_rows, int64_t* workspace_byt
  *   workspace  >= workspace_bytes from ep_query, 16-byte aligned; its
  *              contents on entry do not matter and are clobbered
  *   layout     the arrays above, all written here
- * Steps (three kernels): clear the counters; per-tile wavefront
- * ballot/popcount histogram into counts; one pass that scans the aligned
- * group sizes, ranks every slot inside its group with a decoupled look-back
- * over tiles, and writes token_row, expert_ids and src_info.
+ * Steps: a per-tile wavefront ballot/popcount histogram, then one pass
+ * that resolves each tile's in-group prefix, scans the aligned group sizes,
+ * ranks every slot inside its group and writes token_row, expert_ids and
+ * src_info.  The prefix over earlier tiles comes from direct sums of a
+ * group-major table of tile counts (two kernels, up to 256 tiles), or from
+ * a single-pass decoupled look-back over per-tile descriptors (three
+ * kernels: the counters are cleared first), which is taken above 256 tiles
+ * or when cfg->flags has EP_LAYOUT_LOOKBACK.  Both give identical results.
  */
 int ep_dispatch_layout(const ep_cfg_t* cfg, const int32_t* topk_ids, void* workspace,
                        int64_t workspace_bytes, const ep_layout_t* layout, void* stream);

@@ -189,6 +189,14 @@ def check_layout(c: Case, name: str) -> epx.Layout:
     say(f"[gpu] layout {name}: T={c.cfg.num_tokens} E={c.cfg.num_experts} S={c.cfg.num_segments} "
         f"K={c.cfg.top_k} A={c.cfg.align} C={c.cfg.seg_capacity} shared={c.cfg.shared_expert} "
         f"R={c.cfg.recv_rows}")
+    # Both prefix paths (direct tile-count sums, decoupled look-back) must
+    # give the oracle's layout; the direct (default) one is returned.
+    saved = c.cfg.flags
+    try:
+        c.cfg.flags = saved | epx.EP_LAYOUT_LOOKBACK
+        assert_layout_equal(layout_np(gpu_layout(c.cfg, c.ids)), c.L, name + " (look-back)")
+    finally:
+        c.cfg.flags = saved
     lay = gpu_layout(c.cfg, c.ids)
     assert_layout_equal(layout_np(lay), c.L, name)
     return lay

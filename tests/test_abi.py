@@ -85,7 +85,8 @@ def test_query_sizes(L, orc):
         per = -(-routed // (256 * 64))  # tiles of 256 x {2,4,8} slots, about 64 of them
         spt = 2 if per <= 2 else (4 if per <= 4 else 8)
         tiles = max(1, -(-routed // (256 * spt)))
-        assert ws == 256 + tiles * c.num_segments * g * 4
+        tiles_pad = -(-tiles // 4) * 4  # a group's row of tile counts is read as 16-byte vectors
+        assert ws == 256 + tiles_pad * c.num_segments * g * 4
     # the bound is reached by some routing and never exceeded (oracle layout)
     rng = np.random.default_rng(0)
     c = cfg(num_tokens=9, num_experts=12, num_segments=3, top_k=3, align=5, shared_expert=1)
@@ -100,7 +101,7 @@ INVALID = [
     dict(num_tokens=-1), dict(hidden=0), dict(hidden=12), dict(num_experts=0), dict(num_segments=0),
     dict(num_experts=9), dict(top_k=0), dict(top_k=9), dict(align=0), dict(seg_capacity=-1),
     dict(shared_expert=2), dict(shared_expert=1, src_segment=2), dict(shared_expert=1, src_segment=-1),
-    dict(flags=8), dict(num_experts=4096, num_segments=2),  # > EP_MAX_GROUPS groups
+    dict(flags=4), dict(flags=8), dict(num_experts=4096, num_segments=2),  # > EP_MAX_GROUPS groups
     dict(num_tokens=1 << 28, top_k=4),  # 2^30 slots
 ]
 
@@ -108,6 +109,15 @@ INVALID = [
 @pytest.mark.parametrize("kw", INVALID, ids=[str(k) for k in INVALID])
 def test_query_rejects_invalid_config(L, kw):
     assert query(L, cfg(**kw))[0] == -1
+
+
+@pytest.mark.parametrize("flags", [0, 1, 2, 3])
+def test_query_accepts_documented_flags(L, flags):
+    """EP_ZERO_PAD_ROWS (1) and EP_LAYOUT_LOOKBACK (2), alone or together."""
+    from combine_ep_dispatch_amd import EP_LAYOUT_LOOKBACK, EP_ZERO_PAD_ROWS
+
+    assert (EP_ZERO_PAD_ROWS, EP_LAYOUT_LOOKBACK) == (1, 2)
+    assert query(L, cfg(flags=flags))[0] == 0
 
 
 def test_null_config_and_reserved_fields(L):
