@@ -62,7 +62,7 @@ int derive(const ep_cfg_t* c, Shape* d) {
     }
     if (d->min_rows >= (int64_t(1) << 31)) return EP_EINVAL;  // rows are int32
     d->tiles = layout_tiles((int64_t)d->T * d->K);
-    d->ws_bytes = kWorkspaceHeader + layout_tiles_padded(d->tiles) * (int64_t)d->NG * 4;
+    d->ws_bytes = kWorkspaceHeader + d->tiles * (int64_t)d->NG * 4;
     d->R = c->recv_rows;
     d->flags = c->flags;
     return EP_OK;
@@ -185,7 +185,6 @@ int ep_dispatch_layout(const ep_cfg_t* cfg, const int32_t* topk_ids, void* works
     a.src_seg = d.src;
     a.recv_rows = d.R;
     a.tiles = (int32_t)d.tiles;
-    a.tiles_pad = (int32_t)layout_tiles_padded(d.tiles);
     a.direct = layout_direct(d.tiles) && !(d.flags & EP_LAYOUT_LOOKBACK);
     a.slots_per_thread = layout_slots_per_thread((int64_t)d.T * d.K);
     return status_of(launch_layout(a, static_cast<hipStream_t>(stream)));

@@ -35,15 +35,13 @@ inline int64_t layout_tiles(int64_t routed_slots) {
 }
 
 // Up to this many tiles the layout takes the direct path: the histogram
-// launch stores each tile's per-group counts group-major, and every rank
-// workgroup sums a group's whole row (its prefix over earlier tiles and the
-// group total) with a few 16-byte loads.  Above it, the decoupled look-back
-// over [tile][group] descriptors keeps the work linear in the tile count.
+// launch stores each tile's per-group counts as a row of a [tile][group]
+// table, and every rank workgroup sums each group's whole column (its prefix
+// over earlier tiles and the group total).  Above it, the decoupled
+// look-back over [tile][group] descriptors keeps the work linear in the
+// tile count.
 constexpr int kDirectMaxTiles = 256;
 inline bool layout_direct(int64_t tiles) { return tiles <= kDirectMaxTiles; }
-// Tile count padded to a multiple of 4 (a group's row of tile counts is read
-// as 16-byte vectors).
-inline int64_t layout_tiles_padded(int64_t tiles) { return (tiles + 3) & ~int64_t(3); }
 
 // Look-back descriptor: 2 status bits over a 30-bit count.
 constexpr uint32_t kDescAgg = 1u << 30;   // tile aggregate only
@@ -119,12 +117,11 @@ __device__ __forceinline__ T uniform(T v) {
 // ---------------------------------------------------------------------------
 struct LayoutArgs {
     const int32_t* topk_ids;
-    uint32_t* desc;  // direct: [NG][tiles_pad] tile counts; else [tiles][NG] look-back descriptors
+    uint32_t* desc;  // [tiles][NG]: tile counts (direct) or look-back descriptors
     ep_layout_t out;
     int32_t T, K, Kp, E, S, G, NG, E_loc, A, C, shared, src_seg;
     int64_t recv_rows;
     int32_t tiles;
-    int32_t tiles_pad;         // layout_tiles_padded(tiles)
     int32_t direct;            // 1: direct tile-count sums; 0: decoupled look-back
     int32_t slots_per_thread;  // 2, 4 or 8 (layout_slots_per_thread)
 };

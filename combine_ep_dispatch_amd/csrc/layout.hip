@@ -21,20 +21,22 @@
 //                     of each match set adds the set's popcount into an LDS
 //                     counter, so a hot expert costs one LDS atomic per wave
 //                     instead of one per slot.  Each tile stores its
-//                     per-group counts into a group-major [group][tile]
+//                     per-group counts as one row of a [tile][group]
 //                     table; tile 0 also clears the flags word.
-//  2. k_layout_rank   every workgroup reads, for each group, the group's row
-//                     of tile counts with 16-byte loads (one round trip for
-//                     up to 64 tiles) and sums it twice: over all tiles (the
-//                     group total) and over the tiles before its own (its
-//                     in-group prefix).  No workgroup waits on another, and
+//  2. k_layout_rank   every workgroup reads, for each group, the group's
+//                     column of tile counts (lanes over groups, so wave
+//                     loads are contiguous; 64 loads in flight per lane, and
+//                     several lanes per group when groups are few) and sums
+//                     it twice: over all tiles (the group total) and over the
+//                     tiles before its own (its in-group prefix).  No workgroup waits on another, and
 //                     there are no atomics on global memory but the flags.
 //                     It then scans the aligned group sizes into group start
 //                     rows, ranks its tile's slots inside their groups
 //                     (per-wave running counters in LDS + match-any), and
-//                     writes counts (tile 0), offsets, token_row, expert_ids
-//                     and src_info.  Pad-row metadata and the fused
-//                     shared-expert rows are spread over the tiles.
+//                     writes counts (tile 0), offsets, token_row and
+//                     src_info.  The fused shared-expert rows, and
+//                     expert_ids of whole groups (pad rows included) as
+//                     coalesced runs, are spread over the tiles.
 // Above kDirectMaxTiles the per-workgroup row sums would grow with the tile
 // count, so three launches are used instead (also on request, with
 // EP_LAYOUT_LOOKBACK; the results are the same):
@@ -104,8 +106,8 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout_hist(LayoutArgs a) {
     }
     __syncthreads();
     if (DIRECT) {
-        for (int g = tid; g < a.NG; g += kLayoutThreads)
-            a.desc[(int64_t)g * a.tiles_pad + blockIdx.x] = (uint32_t)s_hist[g];
+        uint32_t* row = a.desc + (int64_t)blockIdx.x * a.NG;
+        for (int g = tid; g < a.NG; g += kLayoutThreads) row[g] = (uint32_t)s_hist[g];
         if (blockIdx.x == 0 && tid == 0) a.out.flags[0] = 0;
     } else {
         const uint32_t status = blockIdx.x == 0 ? kDescInc : kDescAgg;  // tile 0: prefix 0 + aggregate
@@ -148,30 +150,39 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout_rank(LayoutArgs a) {
     const int32_t shared_group = a.shared ? a.src_seg * G : -1;
     if (tid == 0) s_flag = 0;
     if (DIRECT) {
-        // Group totals and this tile's in-group prefix from the [group][tile]
-        // table: 16-byte loads, up to 64 of them in flight per thread.
-        const int nq = a.tiles_pad / 4;
-        for (int g = tid; g < NG; g += kLayoutThreads) {
-            const uint4* row = reinterpret_cast<const uint4*>(a.desc + (int64_t)g * a.tiles_pad);
+        // Group totals and this tile's in-group prefix from the [tile][group]
+        // table.  tpg (a power of two, tpg * NG <= 256) lanes share a group:
+        // lane r of the group sums tiles r, r + tpg, ...; with 64 loads in
+        // flight per lane this is one round trip for up to 64 * tpg tiles.
+        // The partial sums meet by xor-shuffles inside the lane group (all
+        // lanes of a group are active or inactive together).
+        constexpr int kBatch = 64;
+        const int tpg = NG > 128 ? 1 : (NG > 64 ? 2 : (NG > 32 ? 4 : (NG > 16 ? 8 : (NG > 8 ? 16 : (NG > 4 ? 32 : 64)))));
+        const int r = tid & (tpg - 1);
+        for (int g = tid / tpg; g < NG; g += kLayoutThreads / tpg) {
+            const uint32_t* col = a.desc + g;
             int32_t tot = 0, pre = 0;
-            for (int q0 = 0; q0 < nq; q0 += 16) {
-                uint4 v[16];
+            for (int j0 = r; j0 < a.tiles; j0 += kBatch * tpg) {
+                uint32_t v[kBatch];
 #pragma unroll
-                for (int i = 0; i < 16; ++i) v[i] = q0 + i < nq ? row[q0 + i] : make_uint4(0, 0, 0, 0);
+                for (int i = 0; i < kBatch; ++i) {
+                    const int j = j0 + i * tpg;
+                    v[i] = j < a.tiles ? col[(int64_t)j * NG] : 0u;
+                }
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int t4 = 4 * (q0 + i);
-                    const uint32_t c[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const int32_t n = t4 + j < a.tiles ? (int32_t)c[j] : 0;  // pad tiles hold garbage
-                        tot += n;
-                        pre += t4 + j < (int)tile ? n : 0;
-                    }
+                for (int i = 0; i < kBatch; ++i) {
+                    tot += (int32_t)v[i];
+                    pre += j0 + i * tpg < (int)tile ? (int32_t)v[i] : 0;
                 }
             }
-            s_cnt[g] = tot + (g == shared_group ? a.T : 0);
-            s_pref[g] = pre;
+            for (int o = 1; o < tpg; o <<= 1) {
+                tot += __shfl_xor(tot, o, kWave);
+                pre += __shfl_xor(pre, o, kWave);
+            }
+            if (r == 0) {
+                s_cnt[g] = tot + (g == shared_group ? a.T : 0);
+                s_pref[g] = pre;
+            }
         }
     } else {
         for (int g = tid; g < NG; g += kLayoutThreads) s_cnt[g] = a.out.counts[g];
@@ -380,7 +391,6 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout_rank(LayoutArgs a) {
             continue;
         }
         *tr = (int32_t)row;
-        a.out.expert_ids[row] = eid[it];
         a.out.src_info[2 * (int64_t)row] = (int32_t)t;
         a.out.src_info[2 * (int64_t)row + 1] = (int32_t)k;
     }
@@ -402,27 +412,35 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout_rank(LayoutArgs a) {
                 flag |= EP_FLAG_INTERNAL;
             } else {
                 *tr = (int32_t)row;
-                a.out.expert_ids[row] = a.E;
                 a.out.src_info[2 * (int64_t)row] = t;
                 a.out.src_info[2 * (int64_t)row + 1] = a.K;
             }
         }
     }
 
-    // ---- pad-row metadata of groups g = tile (mod tiles) ----
+    // ---- expert_ids of every used row, and pad-row src_info, of groups
+    // g = tile (mod tiles).  A group's rows are contiguous and all hold the
+    // group's expert (E for the fused shared expert), so they are written as
+    // one coalesced run instead of one scattered word per slot; pad rows get
+    // -1 in expert_ids and src_info.
     for (int g = (int)tile; g < NG; g += a.tiles) {
         const int32_t c = s_cnt[g];
-        const int32_t npad = align_up(c, a.A) - c;
-        for (int32_t r = tid; r < npad; r += kLayoutThreads) {
-            const uint32_t row = (uint32_t)s_start[g] + (uint32_t)c + (uint32_t)r;
+        const int32_t n = align_up(c, a.A);
+        const int32_t gs = g / G, gl = g - gs * G;
+        const int32_t expert = (a.shared && gl == 0) ? a.E : gs * a.E_loc + (gl - a.shared);
+        for (int32_t r = tid; r < n; r += kLayoutThreads) {
+            const uint32_t row = (uint32_t)s_start[g] + (uint32_t)r;
             if (row >= (uint32_t)s_lim[g]) break;
             if (row >= R) {
                 flag |= EP_FLAG_INTERNAL;
                 break;
             }
-            a.out.expert_ids[row] = -1;
-            a.out.src_info[2 * (int64_t)row] = -1;
-            a.out.src_info[2 * (int64_t)row + 1] = -1;
+            const bool pad = r >= c;
+            a.out.expert_ids[row] = pad ? -1 : expert;
+            if (pad) {
+                a.out.src_info[2 * (int64_t)row] = -1;
+                a.out.src_info[2 * (int64_t)row + 1] = -1;
+            }
         }
     }
 

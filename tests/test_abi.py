@@ -85,8 +85,7 @@ def test_query_sizes(L, orc):
         per = -(-routed // (256 * 64))  # tiles of 256 x {2,4,8} slots, about 64 of them
         spt = 2 if per <= 2 else (4 if per <= 4 else 8)
         tiles = max(1, -(-routed // (256 * spt)))
-        tiles_pad = -(-tiles // 4) * 4  # a group's row of tile counts is read as 16-byte vectors
-        assert ws == 256 + tiles_pad * c.num_segments * g * 4
+        assert ws == 256 + tiles * c.num_segments * g * 4
     # the bound is reached by some routing and never exceeded (oracle layout)
     rng = np.random.default_rng(0)
     c = cfg(num_tokens=9, num_experts=12, num_segments=3, top_k=3, align=5, shared_expert=1)

@@ -98,7 +98,7 @@ EDGE = {
     "hot_expert": dict(T=4000, S=2, E_loc=1, K=1, H=32, A=8),
     "tile4_ragged": dict(T=5001, S=8, E_loc=8, K=8, H=16, A=4),          # 4 slots/thread tiles
     "tile8_79_tiles": dict(T=20011, S=4, E_loc=16, K=8, H=16, A=2),       # 8 slots/thread, 79 tiles
-    "direct_254_tiles": dict(T=65000, S=4, E_loc=16, K=8, H=16, A=2, bad_p=0.01),  # padded rows of tile counts
+    "direct_254_tiles": dict(T=65000, S=4, E_loc=16, K=8, H=16, A=2, bad_p=0.01),  # direct path, near its tile limit
     "lookback_274_tiles": dict(T=70001, S=4, E_loc=16, K=8, H=16, A=2, shared=1, src=3, bad_p=0.01),  # look-back path
 }
 
