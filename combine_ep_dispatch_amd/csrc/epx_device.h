@@ -56,16 +56,19 @@ __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w 
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
 // float -> bf16 bits, round to nearest-even; NaN keeps sign and payload top
-// bits and is made quiet.
-__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (u >> 16) | 0x40u;
-    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-}
+// bits and is made quiet (bit 6 of the bf16 set).  This is gfx950's
+// v_cvt_pk_bf16_f32, two values per instruction: over all 2^32 float
+// patterns it equals (u + 0x7FFF + ((u >> 16) & 1)) >> 16 for non-NaN u and
+// (u >> 16) | 0x40 for NaN, denormals included.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+    const f32x2_t v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
+
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) { return pack_bf16x2(f, 0.0f) & 0xFFFFu; }
 
 // E4M3 ("fn" variant of OCP OFP8: bias 7, largest finite 448, exponent
 // field 0 subnormal with step 2^-9).
