@@ -17,12 +17,13 @@
 // contiguous.  When the pieces tile the row exactly the lane guards vanish.
 //  - The scatters run one wave per (token, piece, slot), with 2 KiB pieces:
 //    the wave loads its row index, weight and payload piece together (one
-//    round trip), then issues its nontemporal stores.  The 8 waves of a
-//    workgroup are the slots of one (token, piece), so a token's x row is
+//    round trip), then issues its nontemporal stores.  The 4 waves of a
+//    workgroup are 4 slots of one (token, piece), and the slot blocks of a
+//    (token, piece) run on one XCD (see ScatterGrid), so a token's x row is
 //    fetched from HBM once and re-read by the other slots from L2.  Short
 //    waves with streaming stores keep many more writes in flight than one
 //    wave storing all K' copies: at DeepSeek-V3 size the dispatch scatter
-//    went from 106 to ~91 us and the combine-backward one from 102 to ~94.
+//    went from 106 to ~92 us and the combine-backward one from 102 to ~90.
 //    The (token, piece, slot) of a workgroup comes from its index with a
 //    mask, a shift and a multiply by a precomputed reciprocal: the per-wave
 //    scalar work bounds these short waves, and a division there cost more
