@@ -5,6 +5,8 @@
 
 #include <mutex>
 
+#include <algorithm>
+
 #include "epx_device.h"
 
 namespace {
@@ -186,6 +188,7 @@ int ep_dispatch_layout(const ep_cfg_t* cfg, const int32_t* topk_ids, void* works
     a.recv_rows = d.R;
     a.tiles = (int32_t)d.tiles;
     a.direct = layout_direct(d.tiles) && !(d.flags & EP_LAYOUT_LOOKBACK);
+    a.rank_blocks = (int32_t)std::max<int64_t>(d.tiles, std::min<int32_t>(d.NG, 256));
     a.slots_per_thread = layout_slots_per_thread((int64_t)d.T * d.K);
     return status_of(launch_layout(a, static_cast<hipStream_t>(stream)));
 }

@@ -126,6 +126,7 @@ struct LayoutArgs {
     int64_t recv_rows;
     int32_t tiles;
     int32_t direct;            // 1: direct tile-count sums; 0: decoupled look-back
+    int32_t rank_blocks;       // workgroups of the rank pass: max(tiles, min(NG, 256))
     int32_t slots_per_thread;  // 2, 4 or 8 (layout_slots_per_thread)
 };
 hipError_t launch_layout(const LayoutArgs& a, hipStream_t stream);

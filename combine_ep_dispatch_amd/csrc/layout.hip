@@ -36,7 +36,9 @@
 //                     writes counts (tile 0), offsets, token_row and
 //                     src_info.  The fused shared-expert rows, and
 //                     expert_ids of whole groups (pad rows included) as
-//                     coalesced runs, are spread over the tiles.
+//                     coalesced runs, are spread over at least
+//                     min(groups, 256) workgroups: the ones past the last
+//                     tile do only this.
 // Above kDirectMaxTiles the per-workgroup row sums would grow with the tile
 // count, so three launches are used instead (also on request, with
 // EP_LAYOUT_LOOKBACK; the results are the same):
@@ -135,7 +137,11 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout_rank(LayoutArgs a) {
 
     const int tid = threadIdx.x, lane = tid & (kWave - 1), w = tid / kWave;
     const int NG = a.NG, G = a.G;
+    // Workgroups past the last tile own no slots: they only fill their share
+    // of the groups' metadata runs (below), which at small T is most of the
+    // work (every group padded to a multiple of A).
     const uint32_t tile = blockIdx.x;
+    const bool owns_tile = tile < (uint32_t)a.tiles;
     // This tile's routed slots: wave w owns [w*64*SPT, (w+1)*64*SPT), in SPT
     // rounds of 64.  The ids are fetched first so their latency hides behind the
     // offset scan.
@@ -325,7 +331,7 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout_rank(LayoutArgs a) {
         const int g = tid + j * kLayoutThreads;
         if (DIRECT || g >= NG) continue;
         uint32_t pref = 0;
-        if (tile > 0 && s_cnt[g] > 0 && g != shared_group) {
+        if (owns_tile && tile > 0 && s_cnt[g] > 0 && g != shared_group) {
             // Read a window of kLookback predecessors at once (independent
             // loads, one round trip), then fold them nearest-first until an
             // inclusive prefix is found.  Tile 0's descriptor is inclusive
@@ -397,7 +403,7 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout_rank(LayoutArgs a) {
 
     // ---- the fused shared expert: token t is rank t of group 0 of src_seg ----
     if (a.shared) {
-        const int32_t per_tile = (a.T + a.tiles - 1) / a.tiles;
+        const int32_t per_tile = (a.T + a.rank_blocks - 1) / a.rank_blocks;
         const int32_t t0 = (int32_t)tile * per_tile;
         const int32_t t1 = min(a.T, t0 + per_tile);
         const uint32_t st0 = (uint32_t)s_start[shared_group], lim0 = (uint32_t)s_lim[shared_group];
@@ -419,11 +425,11 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout_rank(LayoutArgs a) {
     }
 
     // ---- expert_ids of every used row, and pad-row src_info, of groups
-    // g = tile (mod tiles).  A group's rows are contiguous and all hold the
+    // g = blockIdx (mod rank_blocks).  A group's rows are contiguous and all hold the
     // group's expert (E for the fused shared expert), so they are written as
     // one coalesced run instead of one scattered word per slot; pad rows get
     // -1 in expert_ids and src_info.
-    for (int g = (int)tile; g < NG; g += a.tiles) {
+    for (int g = (int)tile; g < NG; g += a.rank_blocks) {
         const int32_t c = s_cnt[g];
         const int32_t n = align_up(c, a.A);
         const int32_t gs = g / G, gl = g - gs * G;
@@ -453,10 +459,10 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout_rank(LayoutArgs a) {
 
 template <int SPT, bool DIRECT>
 void launch_passes(const LayoutArgs& a, hipStream_t stream) {
-    const dim3 grid((unsigned)a.tiles), block(kLayoutThreads);
+    const dim3 block(kLayoutThreads);
     if (!DIRECT) hipLaunchKernelGGL(k_layout_clear, dim3(1), dim3(256), 0, stream, a);
-    hipLaunchKernelGGL((k_layout_hist<SPT, DIRECT>), grid, block, 0, stream, a);
-    hipLaunchKernelGGL((k_layout_rank<SPT, DIRECT>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((k_layout_hist<SPT, DIRECT>), dim3((unsigned)a.tiles), block, 0, stream, a);
+    hipLaunchKernelGGL((k_layout_rank<SPT, DIRECT>), dim3((unsigned)a.rank_blocks), block, 0, stream, a);
 }
 
 template <int SPT>
