@@ -187,9 +187,15 @@ int ep_dispatch_layout(const ep_cfg_t* cfg, const int32_t* topk_ids, void* works
     a.src_seg = d.src;
     a.recv_rows = d.R;
     a.tiles = (int32_t)d.tiles;
-    a.direct = layout_direct(d.tiles) && !(d.flags & EP_LAYOUT_LOOKBACK);
+    const int64_t routed = (int64_t)d.T * d.K;
+    if (d.flags & EP_LAYOUT_LOOKBACK) a.mode = kLayoutLookback;
+    else if (routed <= kSmallMaxSlots) a.mode = kLayoutSmall;
+    else if (layout_direct(d.tiles)) a.mode = kLayoutDirect;
+    else a.mode = kLayoutLookback;
     a.rank_blocks = (int32_t)std::max<int64_t>(d.tiles, std::min<int32_t>(d.NG, 256));
-    a.slots_per_thread = layout_slots_per_thread((int64_t)d.T * d.K);
+    // One tile holds every slot in the single-pass mode.
+    a.slots_per_thread = a.mode == kLayoutSmall ? (routed <= 512 ? 2 : (routed <= 1024 ? 4 : 8))
+                                                : layout_slots_per_thread(routed);
     return status_of(launch_layout(a, static_cast<hipStream_t>(stream)));
 }
 

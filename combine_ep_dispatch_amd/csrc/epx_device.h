@@ -43,6 +43,15 @@ inline int64_t layout_tiles(int64_t routed_slots) {
 constexpr int kDirectMaxTiles = 256;
 inline bool layout_direct(int64_t tiles) { return tiles <= kDirectMaxTiles; }
 
+// Up to this many routed slots (one tile of 256 x 8) the layout is one
+// launch: every workgroup ranks all slots in LDS to learn the group totals.
+constexpr int64_t kSmallMaxSlots = 2048;
+
+// How k_layout_rank resolves a tile's in-group prefix.
+constexpr int kLayoutLookback = 0;  // decoupled look-back over descriptors
+constexpr int kLayoutDirect = 1;    // sums of the [tile][group] count table
+constexpr int kLayoutSmall = 2;     // single pass: the only tile, prefix 0
+
 // Look-back descriptor: 2 status bits over a 30-bit count.
 constexpr uint32_t kDescAgg = 1u << 30;   // tile aggregate only
 constexpr uint32_t kDescInc = 2u << 30;   // inclusive prefix through this tile
@@ -125,7 +134,7 @@ struct LayoutArgs {
     int32_t T, K, Kp, E, S, G, NG, E_loc, A, C, shared, src_seg;
     int64_t recv_rows;
     int32_t tiles;
-    int32_t direct;            // 1: direct tile-count sums; 0: decoupled look-back
+    int32_t mode;              // kLayoutLookback, kLayoutDirect or kLayoutSmall
     int32_t rank_blocks;       // workgroups of the rank pass: max(tiles, min(NG, 256))
     int32_t slots_per_thread;  // 2, 4 or 8 (layout_slots_per_thread)
 };

@@ -122,8 +122,9 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout_hist(LayoutArgs a) {
     }
 }
 
-template <int SPT, bool DIRECT>
+template <int SPT, int MODE>
 __global__ __launch_bounds__(kLayoutThreads) void k_layout_rank(LayoutArgs a) {
+    constexpr bool DIRECT = MODE == kLayoutDirect, SMALL = MODE == kLayoutSmall, LOOKBACK = MODE == kLayoutLookback;
     constexpr int kTileSlots = kLayoutThreads * SPT;
     constexpr int kSlotsPerWave = kWave * SPT;
     __shared__ int32_t s_cnt[EP_MAX_GROUPS];    // group totals
@@ -139,14 +140,17 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout_rank(LayoutArgs a) {
     const int NG = a.NG, G = a.G;
     // Workgroups past the last tile own no slots: they only fill their share
     // of the groups' metadata runs (below), which at small T is most of the
-    // work (every group padded to a multiple of A).
+    // work (every group padded to a multiple of A).  In the single-pass mode
+    // every workgroup ranks the one tile (to learn the group totals) and
+    // workgroup 0 alone writes the per-slot results.
     const uint32_t tile = blockIdx.x;
-    const bool owns_tile = tile < (uint32_t)a.tiles;
+    const uint32_t slot_tile = SMALL ? 0u : tile;
+    const bool owns_tile = SMALL ? tile == 0 : tile < (uint32_t)a.tiles;
     // This tile's routed slots: wave w owns [w*64*SPT, (w+1)*64*SPT), in SPT
     // rounds of 64.  The ids are fetched first so their latency hides behind the
     // offset scan.
     const int64_t routed = (int64_t)a.T * a.K;
-    const int64_t wslot0 = (int64_t)tile * kTileSlots + (int64_t)w * kSlotsPerWave;
+    const int64_t wslot0 = (int64_t)slot_tile * kTileSlots + (int64_t)w * kSlotsPerWave;
     int32_t eid[SPT];
 #pragma unroll
     for (int it = 0; it < SPT; ++it) {
@@ -169,16 +173,22 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout_rank(LayoutArgs a) {
             const uint32_t* col = a.desc + g;
             int32_t tot = 0, pre = 0;
             for (int j0 = r; j0 < a.tiles; j0 += kBatch * tpg) {
+                // Unconditional loads at clamped 32-bit offsets (tiles * NG
+                // < 2^20), masked afterwards: no branch around a load and no
+                // 64-bit address temporaries, which let the compiler reuse
+                // pending loads' registers and wait on each load in turn.
                 uint32_t v[kBatch];
 #pragma unroll
                 for (int i = 0; i < kBatch; ++i) {
                     const int j = j0 + i * tpg;
-                    v[i] = j < a.tiles ? col[(int64_t)j * NG] : 0u;
+                    v[i] = col[(uint32_t)min(j, a.tiles - 1) * (uint32_t)NG];
                 }
 #pragma unroll
                 for (int i = 0; i < kBatch; ++i) {
-                    tot += (int32_t)v[i];
-                    pre += j0 + i * tpg < (int)tile ? (int32_t)v[i] : 0;
+                    const int j = j0 + i * tpg;
+                    const int32_t n = j < a.tiles ? (int32_t)v[i] : 0;
+                    tot += n;
+                    pre += j < (int)tile ? n : 0;
                 }
             }
             for (int o = 1; o < tpg; o <<= 1) {
@@ -190,7 +200,7 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout_rank(LayoutArgs a) {
                 s_pref[g] = pre;
             }
         }
-    } else {
+    } else if (LOOKBACK) {
         for (int g = tid; g < NG; g += kLayoutThreads) s_cnt[g] = a.out.counts[g];
     }
     for (int e = tid; e < a.E; e += kLayoutThreads)
@@ -199,6 +209,63 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout_rank(LayoutArgs a) {
     for (int w2 = 0; w2 < kLayoutWaves; ++w2)
         for (int g = tid; g < NG; g += kLayoutThreads) s_wcnt[w2][g] = 0;
     __syncthreads();
+
+    // In-tile ranks (per-wave running counters + match-any), then the
+    // per-wave exclusive prefixes and the tile's aggregate per group.
+    uint32_t key[SPT], rnk[SPT];
+    int32_t flag = 0;
+    int32_t agg[EP_MAX_GROUPS / kLayoutThreads];
+    auto rank_slots = [&]() {
+        // ---- in-tile ranks (per-wave running counters + match-any) ----
+        const int nbits = 32 - __clz(NG);
+#pragma unroll
+        for (int it = 0; it < SPT; ++it) {
+            const int32_t e = eid[it];
+            const uint32_t k = (uint32_t)e < (uint32_t)a.E ? (uint32_t)s_gof[e] : (uint32_t)NG;
+            if (e != -1 && (uint32_t)e >= (uint32_t)a.E) flag |= EP_FLAG_BAD_ID;  // -1 = masked slot
+            const uint64_t m = match_any(k, nbits);
+            const uint32_t r = lanes_below(m);
+            rnk[it] = 0;
+            if (k != (uint32_t)NG) {
+                const uint32_t before = s_wcnt[w][k];
+                rnk[it] = before + r;
+                if (r == 0) s_wcnt[w][k] = (uint16_t)(before + (uint32_t)__popcll(m));
+            }
+            key[it] = k;
+        }
+        __syncthreads();
+
+        // ---- per-wave exclusive prefixes and the tile aggregate per group ----
+#pragma unroll
+        for (int j = 0; j < EP_MAX_GROUPS / kLayoutThreads; ++j) {
+            const int g = tid + j * kLayoutThreads;
+            agg[j] = 0;
+            if (g < NG) {
+                int32_t run = 0;
+#pragma unroll
+                for (int w2 = 0; w2 < kLayoutWaves; ++w2) {
+                    const int32_t c = s_wcnt[w2][g];
+                    s_wcnt[w2][g] = (uint16_t)run;
+                    run += c;
+                }
+                agg[j] = run;
+            }
+        }
+    };
+
+    // Single pass: the group totals come from ranking the one tile.
+    if (SMALL) {
+        rank_slots();
+#pragma unroll
+        for (int j = 0; j < EP_MAX_GROUPS / kLayoutThreads; ++j) {
+            const int g = tid + j * kLayoutThreads;
+            if (g < NG) {
+                s_cnt[g] = agg[j] + (g == shared_group ? a.T : 0);
+                s_pref[g] = 0;
+            }
+        }
+        __syncthreads();
+    }
 
     // ---- aligned exclusive prefix P over all groups (segment-major) ----
     // Thread i covers groups [8i, 8i + 8); NG <= 2048 = 256 * 8.
@@ -235,9 +302,10 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout_rank(LayoutArgs a) {
     }
     __syncthreads();
 
-    // Counts (direct path), offsets and segment bases: one tile writes them.
+    // Counts (direct and single-pass paths), offsets and segment bases: one
+    // tile writes them.
     if (tile == 0) {
-        if (DIRECT)
+        if (!LOOKBACK)
             for (int g = tid; g < NG; g += kLayoutThreads) a.out.counts[g] = s_cnt[g];
         const int n = a.S * (G + 1);
         for (int idx = tid; idx < n; idx += kLayoutThreads) {
@@ -287,49 +355,13 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout_rank(LayoutArgs a) {
         }
     }
 
-    // ---- in-tile ranks (per-wave running counters + match-any) ----
-    const int nbits = 32 - __clz(NG);
-    uint32_t key[SPT], rnk[SPT];
-    int32_t flag = 0;
-#pragma unroll
-    for (int it = 0; it < SPT; ++it) {
-        const int32_t e = eid[it];
-        const uint32_t k = (uint32_t)e < (uint32_t)a.E ? (uint32_t)s_gof[e] : (uint32_t)NG;
-        if (e != -1 && (uint32_t)e >= (uint32_t)a.E) flag |= EP_FLAG_BAD_ID;  // -1 = masked slot
-        const uint64_t m = match_any(k, nbits);
-        const uint32_t r = lanes_below(m);
-        rnk[it] = 0;
-        if (k != (uint32_t)NG) {
-            const uint32_t before = s_wcnt[w][k];
-            rnk[it] = before + r;
-            if (r == 0) s_wcnt[w][k] = (uint16_t)(before + (uint32_t)__popcll(m));
-        }
-        key[it] = k;
-    }
-    __syncthreads();
+    if (!SMALL) rank_slots();
 
-    // ---- per-wave exclusive prefixes and the tile aggregate per group ----
-    int32_t agg[EP_MAX_GROUPS / kLayoutThreads];
-#pragma unroll
-    for (int j = 0; j < EP_MAX_GROUPS / kLayoutThreads; ++j) {
-        const int g = tid + j * kLayoutThreads;
-        agg[j] = 0;
-        if (g < NG) {
-            int32_t run = 0;
-#pragma unroll
-            for (int w2 = 0; w2 < kLayoutWaves; ++w2) {
-                const int32_t c = s_wcnt[w2][g];
-                s_wcnt[w2][g] = (uint16_t)run;
-                run += c;
-            }
-            agg[j] = run;
-        }
-    }
     // ---- decoupled look-back over earlier tiles (look-back path only) ----
 #pragma unroll
     for (int j = 0; j < EP_MAX_GROUPS / kLayoutThreads; ++j) {
         const int g = tid + j * kLayoutThreads;
-        if (DIRECT || g >= NG) continue;
+        if (!LOOKBACK || g >= NG) continue;
         uint32_t pref = 0;
         if (owns_tile && tile > 0 && s_cnt[g] > 0 && g != shared_group) {
             // Read a window of kLookback predecessors at once (independent
@@ -377,7 +409,7 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout_rank(LayoutArgs a) {
 #pragma unroll
     for (int it = 0; it < SPT; ++it) {
         const int64_t f = wslot0 + it * kWave + lane;
-        if (f >= routed) continue;
+        if (!owns_tile || f >= routed) continue;
         const uint32_t t = (uint32_t)f / (uint32_t)a.K, k = (uint32_t)f - t * (uint32_t)a.K;
         int32_t* tr = &a.out.token_row[(int64_t)t * a.Kp + k];
         const uint32_t g = key[it];
@@ -450,6 +482,24 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout_rank(LayoutArgs a) {
         }
     }
 
+    if (SMALL) {
+        // No earlier launch cleared the flags word, so workgroup 0 stores it
+        // whole.  Every bit is a function of the group totals, starts and
+        // limits, so it also covers rows other workgroups handled: a group
+        // drops slots if start + count > limit, and reaches past the buffer
+        // if its used rows (pad included) end beyond R.
+        if (tile != 0) return;
+        for (int g = tid; g < NG; g += kLayoutThreads) {
+            const uint32_t st = (uint32_t)s_start[g], lim = (uint32_t)s_lim[g], c = (uint32_t)s_cnt[g];
+            if (st + c > lim) flag |= EP_FLAG_DROPPED;
+            const uint32_t end = min(st + (uint32_t)align_up((int32_t)c, a.A), lim);
+            if (end > st && end > R) flag |= EP_FLAG_INTERNAL;
+        }
+        if (flag) atomicOr(&s_flag, flag);
+        __syncthreads();
+        if (tid == 0) a.out.flags[0] = s_flag;
+        return;
+    }
     if (flag) atomicOr(&s_flag, flag);
     __syncthreads();
     if (tid == 0 && s_flag) atomicOr(a.out.flags, s_flag);
@@ -459,16 +509,22 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout_rank(LayoutArgs a) {
 
 template <int SPT, bool DIRECT>
 void launch_passes(const LayoutArgs& a, hipStream_t stream) {
+    constexpr int kMode = DIRECT ? kLayoutDirect : kLayoutLookback;
     const dim3 block(kLayoutThreads);
     if (!DIRECT) hipLaunchKernelGGL(k_layout_clear, dim3(1), dim3(256), 0, stream, a);
     hipLaunchKernelGGL((k_layout_hist<SPT, DIRECT>), dim3((unsigned)a.tiles), block, 0, stream, a);
-    hipLaunchKernelGGL((k_layout_rank<SPT, DIRECT>), dim3((unsigned)a.rank_blocks), block, 0, stream, a);
+    hipLaunchKernelGGL((k_layout_rank<SPT, kMode>), dim3((unsigned)a.rank_blocks), block, 0, stream, a);
 }
 
 template <int SPT>
 void launch_spt(const LayoutArgs& a, hipStream_t stream) {
-    if (a.direct) launch_passes<SPT, true>(a, stream);
-    else launch_passes<SPT, false>(a, stream);
+    if (a.mode == kLayoutSmall)
+        hipLaunchKernelGGL((k_layout_rank<SPT, kLayoutSmall>), dim3((unsigned)a.rank_blocks), dim3(kLayoutThreads),
+                           0, stream, a);
+    else if (a.mode == kLayoutDirect)
+        launch_passes<SPT, true>(a, stream);
+    else
+        launch_passes<SPT, false>(a, stream);
 }
 
 hipError_t launch_layout(const LayoutArgs& a, hipStream_t stream) {
