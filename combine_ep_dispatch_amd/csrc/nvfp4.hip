@@ -7,9 +7,10 @@
 // 2688 = 448 * 6: the largest finite E4M3 block scale times the largest
 // E2M1 magnitude, so the block that holds rowmax gets scale 448.
 //
-// One wave64 per token.  Lane l holds 16-element blocks l, l+64, ... of the
-// row in registers (two 16-byte loads per block), so a block's amax is
-// lane-local and the row max is one wave reduction.  The token is quantized
+// One wave64 per token (four for batches under kSmallBatchTokens).  Lane l
+// holds 16-element blocks l, l+64, ... of the row in registers (two 16-byte
+// loads per block), so a block's amax is lane-local and the row max is one
+// wave reduction (plus an LDS exchange when a token has several waves).  The token is quantized
 // once (VALU only: there is no contraction here for MFMA), then its bytes
 // are written to each of the token's K' rows: 8 code bytes per block per
 // lane (512 contiguous bytes per wave store), one scale byte per block.
@@ -36,6 +37,10 @@ namespace {
 constexpr int kQuantThreads = 256;
 constexpr int kQuantWaves = kQuantThreads / kWave;
 constexpr int kMaxBlocksPerLane = 16;  // H <= 16 * 64 * 16 = 16384
+#ifndef EPX_NVFP4_SMALL_BATCH
+#define EPX_NVFP4_SMALL_BATCH 4096
+#endif
+constexpr int kSmallBatchTokens = EPX_NVFP4_SMALL_BATCH;  // below this, 4 waves per token
 
 // v -> E2M1 code.  Thresholds are the midpoints between the magnitudes
 // {0, .5, 1, 1.5, 2, 3, 4, 6}; at a midpoint the even code wins (the
@@ -75,20 +80,28 @@ __device__ __forceinline__ uint32_t codes_of_words_sw(const uint4& w, float inv)
            (codes_of_word(w.w, inv) << 24);
 }
 
-template <int NBL>
+// W waves per token (1, or 4 for small batches, where a token's quantize
+// latency would otherwise leave the chip idle): wave `part` of the token
+// holds blocks part*64 + lane + i*64*W, and with W > 1 the row max meets in
+// LDS.  A workgroup is 4 waves, so with W = 4 it is one token and the early
+// exit below is the same for the whole workgroup.
+template <int NBL, int W>
 __global__ __launch_bounds__(kQuantThreads) void k_nvfp4(Nvfp4Args a) {
-    const int32_t t = uniform((int32_t)(blockIdx.x * kQuantWaves + threadIdx.x / kWave));
+    const int wv = threadIdx.x / kWave;
+    const int32_t t = uniform((int32_t)(blockIdx.x * (kQuantWaves / W) + wv / W));
     if (t >= a.T) return;
+    const int part = wv % W;
     const int lane = threadIdx.x & (kWave - 1);
     const int32_t nblk = a.H / 16;
     const uint4* xr = reinterpret_cast<const uint4*>(a.x + (int64_t)t * a.H);
+    const int32_t b0 = part * kWave + lane;  // this lane's first block
 
     uint4 q[NBL][2];
     uint32_t bmax[NBL];
     uint32_t lmax = 0;
 #pragma unroll
     for (int i = 0; i < NBL; ++i) {
-        const int32_t b = lane + i * kWave;
+        const int32_t b = b0 + i * kWave * W;
         if (b < nblk) {
             q[i][0] = xr[2 * b];
             q[i][1] = xr[2 * b + 1];
@@ -110,6 +123,13 @@ __global__ __launch_bounds__(kQuantThreads) void k_nvfp4(Nvfp4Args a) {
     }
 #pragma unroll
     for (int o = kWave / 2; o > 0; o >>= 1) lmax = max(lmax, (uint32_t)__shfl_xor((int)lmax, o, kWave));
+    if (W > 1) {
+        __shared__ uint32_t s_rmax[kQuantWaves];
+        if (lane == 0) s_rmax[wv] = lmax;
+        __syncthreads();
+#pragma unroll
+        for (int p2 = 0; p2 < W; ++p2) lmax = max(lmax, s_rmax[(wv / W) * W + p2]);
+    }
     const float rowmax = __uint_as_float(lmax << 16);
 
     uint2 code[NBL];
@@ -155,20 +175,21 @@ __global__ __launch_bounds__(kQuantThreads) void k_nvfp4(Nvfp4Args a) {
         uint8_t* srow = a.scales + (int64_t)row * sstride;
 #pragma unroll
         for (int i = 0; i < NBL; ++i) {
-            const int32_t b = lane + i * kWave;
+            const int32_t b = b0 + i * kWave * W;
             if (b < nblk) {
                 *reinterpret_cast<uint2*>(crow + 8 * (int64_t)b) = code[i];
                 srow[b] = (uint8_t)sc[i];
             }
         }
-        if (lane == 0) a.rowscale[row] = (uint16_t)rs;
+        if (part == 0 && lane == 0) a.rowscale[row] = (uint16_t)rs;
     }
 }
 
-template <int NBL>
+template <int NBL, int W>
 hipError_t launch_nbl(const Nvfp4Args& a, hipStream_t stream) {
-    const unsigned blocks = (unsigned)((a.T + kQuantWaves - 1) / kQuantWaves);
-    hipLaunchKernelGGL(k_nvfp4<NBL>, dim3(blocks), dim3(kQuantThreads), 0, stream, a);
+    constexpr int kTokensPerBlock = kQuantWaves / W;
+    const unsigned blocks = (unsigned)((a.T + kTokensPerBlock - 1) / kTokensPerBlock);
+    hipLaunchKernelGGL((k_nvfp4<NBL, W>), dim3(blocks), dim3(kQuantThreads), 0, stream, a);
     return hipGetLastError();
 }
 
@@ -178,17 +199,26 @@ int nvfp4_max_hidden() { return 16 * kWave * kMaxBlocksPerLane; }
 
 hipError_t launch_nvfp4(const Nvfp4Args& a, hipStream_t stream) {
     if (a.T == 0) return hipSuccess;
+    if (a.T < kSmallBatchTokens) {  // 4 waves per token
+        const int nbl = (a.H / 16 + 4 * kWave - 1) / (4 * kWave);
+        switch (nbl) {
+            case 1: return launch_nbl<1, 4>(a, stream);
+            case 2: return launch_nbl<2, 4>(a, stream);
+            case 3: return launch_nbl<3, 4>(a, stream);
+            default: return launch_nbl<4, 4>(a, stream);
+        }
+    }
     const int nbl = (a.H / 16 + kWave - 1) / kWave;
     switch (nbl) {
-        case 1: return launch_nbl<1>(a, stream);
-        case 2: return launch_nbl<2>(a, stream);
-        case 3: return launch_nbl<3>(a, stream);
-        case 4: return launch_nbl<4>(a, stream);
-        case 5: case 6: return launch_nbl<6>(a, stream);
-        case 7: return launch_nbl<7>(a, stream);
-        case 8: return launch_nbl<8>(a, stream);
-        case 9: case 10: case 11: case 12: return launch_nbl<12>(a, stream);
-        default: return launch_nbl<kMaxBlocksPerLane>(a, stream);
+        case 1: return launch_nbl<1, 1>(a, stream);
+        case 2: return launch_nbl<2, 1>(a, stream);
+        case 3: return launch_nbl<3, 1>(a, stream);
+        case 4: return launch_nbl<4, 1>(a, stream);
+        case 5: case 6: return launch_nbl<6, 1>(a, stream);
+        case 7: return launch_nbl<7, 1>(a, stream);
+        case 8: return launch_nbl<8, 1>(a, stream);
+        case 9: case 10: case 11: case 12: return launch_nbl<12, 1>(a, stream);
+        default: return launch_nbl<kMaxBlocksPerLane, 1>(a, stream);
     }
 }
 
