@@ -140,6 +140,9 @@ def main() -> int:
     ap.add_argument("--workload", default="dsv3")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--latency-sweep", default="",
+                    help="comma-separated token counts: print per-op latency of the workload's "
+                         "shape at each (small-batch serving), instead of the benchmark line")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU's share of the work; --gpus {args.gpus} is not supported "
@@ -158,6 +161,8 @@ def main() -> int:
 
     if args.copy_calibration:
         return copy_calibration(torch, epx, dev)
+    if args.latency_sweep:
+        return latency_sweep(torch, epx, wl, dev, args.workload, [int(v) for v in args.latency_sweep.split(",")])
 
     w = wl.CONFIGS[args.workload]
     log(f"[bench] workload {wl.describe(w)}")
@@ -350,6 +355,65 @@ def capture(torch, fn):
         fn()
     torch.cuda.synchronize()
     return g
+
+
+def latency_sweep(torch, epx, wl, dev, workload: str, token_counts) -> int:
+    """Per-op latency (µs, graphs of 8 back-to-back launches, median of 10)
+    of the workload's shape at each token count, plus the whole step (the
+    ops of the benchmark step, FP8 dispatch excluded).  One JSON line per T."""
+    for T in token_counts:
+        w = wl.CONFIGS[workload].at_tokens(T)
+        d = wl.make_workload(w)
+        cfg = epx.EpConfig(num_tokens=T, hidden=w.H, num_experts=w.E, num_segments=w.S, top_k=w.K,
+                           align=w.align, seg_capacity=w.capacity, shared_expert=w.shared_expert,
+                           src_segment=w.src_segment)
+        cfg.recv_rows = epx.ep_query(cfg).min_recv_rows
+        R, H = cfg.recv_rows, w.H
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(1)
+        x = torch.from_numpy(d["x"].view(np.int16)).to(dev).view(torch.bfloat16)
+        ids = torch.from_numpy(d["topk_ids"].reshape(-1)).to(dev)
+        probs = torch.from_numpy(d["probs"].reshape(-1)).to(dev)
+        out = torch.randn(R * H, generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
+        gy = torch.randn(T * H, generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
+        lay, ws = epx.Layout.empty(cfg, dev), epx.workspace_for(cfg, dev)
+        recv = torch.empty(R * H, dtype=torch.bfloat16, device=dev)
+        codes = torch.empty(R * H // 2, dtype=torch.uint8, device=dev)
+        scales = torch.empty(R * H // 16, dtype=torch.uint8, device=dev)
+        rowscale = torch.empty(R, dtype=torch.bfloat16, device=dev)
+        f8c = torch.empty(R * H, dtype=torch.uint8, device=dev)
+        f8s = torch.empty(R * (H // 128), dtype=torch.float32, device=dev)
+        y = torch.empty(T * H, dtype=torch.bfloat16, device=dev)
+        gout = torch.empty(R * H, dtype=torch.bfloat16, device=dev)
+        gx = torch.empty(T * H, dtype=torch.bfloat16, device=dev)
+        step_ops = [("layout", lambda: epx.ep_dispatch_layout(cfg, ids, ws, lay)),
+                    ("dispatch", lambda: epx.ep_dispatch(cfg, lay, x, recv)),
+                    ("dispatch_nvfp4", lambda: epx.ep_dispatch_nvfp4(cfg, lay, x, codes, scales, rowscale)),
+                    ("combine", lambda: epx.ep_combine(cfg, lay, out, probs, y)),
+                    ("combine_bwd", lambda: epx.ep_combine_bwd(cfg, lay, gy, probs, gout)),
+                    ("dispatch_bwd", lambda: epx.ep_dispatch_bwd(cfg, lay, out, gx))]
+        ops = step_ops + [("dispatch_fp8", lambda: epx.ep_dispatch_fp8(cfg, lay, x, f8c, f8s)),
+                          ("step", lambda: [fn() for _, fn in step_ops])]
+        step_ops[0][1]()
+        torch.cuda.synchronize()
+        res = {}
+        for n, fn in ops:
+            def many(fn=fn):
+                for _ in range(8):
+                    fn()
+            g = capture(torch, many)
+            times = []
+            for _ in range(10):
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record()
+                g.replay()
+                b.record()
+                times.append((a, b))
+            torch.cuda.synchronize()
+            res[n] = round(statistics.median(a.elapsed_time(b) * 1e3 / 8 for a, b in times), 2)
+            del g
+        print(json.dumps({"latency_us": res, "workload": wl.describe(w), "tokens": T}), flush=True)
+    return 0
 
 
 def copy_calibration(torch, epx, dev) -> int:
