@@ -163,11 +163,15 @@ int ep_query(const ep_cfg_t* cfg, int64_t* min_recv_rows, int64_t* workspace_byt
  * Steps: a per-tile wavefront ballot/popcount histogram, then one pass
  * that resolves each tile's in-group prefix, scans the aligned group sizes,
  * ranks every slot inside its group and writes token_row, expert_ids and
- * src_info.  The prefix over earlier tiles comes from direct sums of a
- * group-major table of tile counts (two kernels, up to 256 tiles), or from
- * a single-pass decoupled look-back over per-tile descriptors (three
- * kernels: the counters are cleared first), which is taken above 256 tiles
- * or when cfg->flags has EP_LAYOUT_LOOKBACK.  Both give identical results.
+ * src_info.  The prefix over earlier tiles comes from one of three paths,
+ * all with identical results:
+ *  - up to 2048 routed slots (one tile): a single launch in which every
+ *    workgroup ranks all slots itself;
+ *  - up to 256 tiles: direct sums of a [tile][group] table of tile counts
+ *    (two kernels);
+ *  - otherwise, or when cfg->flags has EP_LAYOUT_LOOKBACK: a single-pass
+ *    decoupled look-back over per-tile descriptors (three kernels: the
+ *    counters are cleared first).
  */
 int ep_dispatch_layout(const ep_cfg_t* cfg, const int32_t* topk_ids, void* workspace,
                        int64_t workspace_bytes, const ep_layout_t* layout, void* stream);
