@@ -42,6 +42,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, published
+COLD_REPS = 10
 METRIC = "dispatch+combine tokens/s and effective HBM GB/s (% of peak), 1 MI355X"
 KERNEL_SOURCES = ("combine_ep_dispatch_amd/csrc/move.hip", "combine_ep_dispatch_amd/csrc/nvfp4.hip",
                   "combine_ep_dispatch_amd/csrc/layout.hip", "combine_ep_dispatch_amd/csrc/fp8.hip",
@@ -108,15 +109,18 @@ def cpu_baseline(w, host) -> dict:
     orc.build(force=False)
     oc = orc.Cfg(T=w.T, H=w.H, E=w.E, S=w.S, K=w.K, A=w.align, C=w.capacity, shared=w.shared_expert,
                  src_seg=w.src_segment, recv_rows=host["R"])
-    t0 = time.perf_counter()
-    L = orc.layout(oc, host["ids"])
-    tr = L["token_row"]
-    orc.dispatch(oc, tr, host["x"])
-    orc.dispatch_nvfp4(oc, tr, host["x"])
-    orc.combine(oc, tr, host["out"], host["probs"])
-    orc.combine_bwd(oc, tr, host["gy"], host["probs"])
-    orc.dispatch_bwd(oc, tr, host["grad_recv"])
-    dt = time.perf_counter() - t0
+    runs = []
+    for _ in range(3):  # median of 3
+        t0 = time.perf_counter()
+        L = orc.layout(oc, host["ids"])
+        tr = L["token_row"]
+        orc.dispatch(oc, tr, host["x"])
+        orc.dispatch_nvfp4(oc, tr, host["x"])
+        orc.combine(oc, tr, host["out"], host["probs"])
+        orc.combine_bwd(oc, tr, host["gy"], host["probs"])
+        orc.dispatch_bwd(oc, tr, host["grad_recv"])
+        runs.append(time.perf_counter() - t0)
+    dt = statistics.median(runs)
     cpu = platform.processor() or platform.machine()
     try:
         with open("/proc/cpuinfo") as f:
@@ -128,7 +132,7 @@ def cpu_baseline(w, host) -> dict:
         pass
     return {"value": round(w.T / dt, 1), "unit": "tokens/s", "cores": 1, "kind": "oracle",
             "sample": f"one full step (layout, bf16 + NVFP4 dispatch, combine, both backward passes) "
-                      f"over the whole {w.T}-token batch, single-threaded C oracle, {dt:.2f} s; "
+                      f"over the whole {w.T}-token batch, single-threaded C oracle, median of 3 runs {dt:.2f} s; "
                       f"host {cpu}, os.cpu_count()={os.cpu_count()}"}
 
 
@@ -270,6 +274,38 @@ def main() -> int:
         torch.cuda.synchronize()
         op_us[n] = [a.elapsed_time(b) * 1e3 / LAUNCHES for a, b in times]
         del g
+    # cold per-op durations: one launch after an untimed read of 1 GiB that
+    # evicts L2 and the 256 MB MALL.  A read leaves no dirty lines behind
+    # (a fill would, and the timed launch would pay for writing them back),
+    # and it writes back what the previous launch left dirty.
+    flush = torch.ones(1 << 28, dtype=torch.int32, device=dev)
+    cold_us = {}
+    for n, fn in ops + extra_ops:
+        times = []
+        for r in range(COLD_REPS):
+            flush.sum()
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn()
+            b.record(stream)
+            times.append((a, b))
+        torch.cuda.synchronize()
+        cold_us[n] = [a.elapsed_time(b) * 1e3 for a, b in times]
+    # context: torch's own device-to-device copy of 1 GiB (read + write)
+    src_c = torch.empty(1 << 28, dtype=torch.int32, device=dev).fill_(1)
+    copy_times = []
+    for _ in range(6):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        flush.copy_(src_c)
+        b.record(stream)
+        copy_times.append((a, b))
+    torch.cuda.synchronize()
+    copy_gbps = 2 * (1 << 30) / (statistics.median(a.elapsed_time(b) for a, b in copy_times[1:]) * 1e-3) / 1e9
+    del flush, src_c
+
     flags = int(lay.flags.item())
     tr = lay.token_row.cpu().numpy()
     kept = int((tr >= 0).sum())
@@ -291,11 +327,20 @@ def main() -> int:
     for n in names + [n for n, _ in extra_ops]:
         us = statistics.mean(op_us[n])
         med = statistics.median(op_us[n])
+        dec = statistics.quantiles(op_us[n], n=10)
+        cdec = statistics.quantiles(cold_us[n], n=10)
+        cmed = statistics.median(cold_us[n])
         gbps = nbytes[n] / (us * 1e-6) / 1e9
-        per_op[n] = {"us": round(us, 2), "us_median": round(med, 2), "bytes": nbytes[n],
-                     "GBps": round(gbps, 1), "frac": round(gbps / HBM_PEAK_GBPS, 4)}
-        log(f"[bench] {n:15s} {us:9.2f} us  {nbytes[n] / 1e6:9.2f} MB  {gbps:8.1f} GB/s  "
-            f"{100 * gbps / HBM_PEAK_GBPS:5.1f}% of 8 TB/s")
+        per_op[n] = {"us": round(us, 2), "us_median": round(med, 2), "us_p10": round(dec[0], 2),
+                     "us_p90": round(dec[-1], 2), "bytes": nbytes[n],
+                     "GBps": round(gbps, 1), "frac": round(gbps / HBM_PEAK_GBPS, 4),
+                     "frac_of_copy": round(gbps / copy_gbps, 4),
+                     "cold": {"us_median": round(cmed, 2), "us_p10": round(cdec[0], 2), "us_p90": round(cdec[-1], 2),
+                              "GBps": round(nbytes[n] / (cmed * 1e-6) / 1e9, 1),
+                              "frac": round(nbytes[n] / (cmed * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)}}
+        log(f"[bench] {n:17s} {us:8.2f} us  {nbytes[n] / 1e6:8.2f} MB  {gbps:7.1f} GB/s  "
+            f"{100 * gbps / HBM_PEAK_GBPS:5.1f}% of 8 TB/s   cold {cmed:8.2f} us "
+            f"{100 * per_op[n]['cold']['frac']:5.1f}%")
     step_bytes = sum(nbytes[n] for n in names)
     dom = max((n for n in names if n != "layout"), key=lambda n: per_op[n]["us"])
     fwd_us = per_op["layout"]["us"] + per_op["dispatch"]["us"] + per_op["combine"]["us"]
@@ -326,6 +371,10 @@ def main() -> int:
         "hbm_frac": round(step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
         "fwd_dispatch_combine_tokens_per_s": round(T / (fwd_us * 1e-6), 1),
         "ops": per_op,
+        "ops_note": ("us/us_median/us_p10/us_p90: warm, graphs of 8 back-to-back launches; cold: one launch "
+                     f"after an untimed read of 1 GiB that evicts L2 and MALL ({COLD_REPS} reps); frac_of_copy: "
+                     "against torch's 1 GiB device copy"),
+        "copy_context_GBps": round(copy_gbps, 1),
         "overflow_flags": flags,
         "roofline": roof,
     }
