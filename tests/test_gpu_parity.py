@@ -100,6 +100,7 @@ EDGE = {
     "tile8_79_tiles": dict(T=20011, S=4, E_loc=16, K=8, H=16, A=2),       # 8 slots/thread, 79 tiles
     "direct_254_tiles": dict(T=65000, S=4, E_loc=16, K=8, H=16, A=2, bad_p=0.01),  # direct path, near its tile limit
     "lookback_274_tiles": dict(T=70001, S=4, E_loc=16, K=8, H=16, A=2, shared=1, src=3, bad_p=0.01),  # look-back path
+    "single_pass_max_groups": dict(T=200, S=8, E_loc=255, K=8, shared=1, A=4, H=32),  # 2048 groups, one launch
     "single_pass_2048": dict(T=256, S=8, E_loc=32, K=8, H=64, A=128, shared=1, src=5),  # largest one-launch layout
     "single_pass_2047": dict(T=2047, S=4, E_loc=8, K=1, H=16, A=4),                   # one slot under it
     "single_pass_512": dict(T=128, S=2, E_loc=16, K=4, H=32, A=8, bad_p=0.02),        # 2 slots/thread bound
