@@ -78,17 +78,17 @@ int check_rows(const Shape& d) {
 // The current device must be a gfx950; the answer is cached per device.
 int check_device() {
     static std::mutex mu;
-    static int verdict[64];  // 0 unknown, 1 ok, 2 not supported
+    static int arch_state[64];  // 0 unknown, 1 ok, 2 not supported
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return EP_ELAUNCH;
     if (dev < 0 || dev >= 64) return EP_ENOTSUP;
     std::lock_guard<std::mutex> lock(mu);
-    if (verdict[dev] == 0) {
+    if (arch_state[dev] == 0) {
         hipDeviceProp_t prop;
         if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return EP_ELAUNCH;
-        verdict[dev] = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+        arch_state[dev] = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
     }
-    return verdict[dev] == 1 ? EP_OK : EP_ENOTSUP;
+    return arch_state[dev] == 1 ? EP_OK : EP_ENOTSUP;
 }
 
 int status_of(hipError_t e) { return e == hipSuccess ? EP_OK : EP_ELAUNCH; }

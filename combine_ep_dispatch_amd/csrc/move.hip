@@ -65,6 +65,11 @@ namespace {
 
 constexpr int kMoveThreads = 256;
 constexpr int kMoveWaves = kMoveThreads / kWave;
+#ifndef EPX_GATHER_THREADS
+#define EPX_GATHER_THREADS 256
+#endif
+constexpr int kGatherThreads = EPX_GATHER_THREADS;
+constexpr int kGatherWaves = kGatherThreads / kWave;
 constexpr int kSlotBatch = 8;  // slots whose loads are in flight together in k_gather
 
 typedef uint32_t v4u __attribute__((ext_vector_type(4)));
@@ -200,9 +205,9 @@ __device__ __forceinline__ void accumulate(float (&acc)[8], v4u v, float w, bool
 }
 
 template <bool WEIGHTED, bool FULL>
-__global__ __launch_bounds__(kMoveThreads) void k_gather(MoveArgs a, int32_t Hv, int32_t pieces) {
+__global__ __launch_bounds__(kGatherThreads) void k_gather(MoveArgs a, int32_t Hv, int32_t pieces) {
     constexpr int VPL = EPX_GATHER_VPL;
-    const int32_t wave = uniform((int32_t)(blockIdx.x * kMoveWaves + threadIdx.x / kWave));
+    const int32_t wave = uniform((int32_t)(blockIdx.x * kGatherWaves + threadIdx.x / kWave));
     const int32_t t = wave / pieces;
     if (t >= a.T) return;
     const int32_t piece = wave - t * pieces;
@@ -332,7 +337,7 @@ Grid move_grid(const MoveArgs& a, int vpl) {
     g.pieces = (g.Hv + per_piece - 1) / per_piece;
     g.full = g.Hv % per_piece == 0;
     const int64_t waves = (int64_t)a.T * g.pieces;
-    g.blocks = dim3((unsigned)((waves + kMoveWaves - 1) / kMoveWaves));
+    g.blocks = dim3((unsigned)((waves + kGatherWaves - 1) / kGatherWaves));
     return g;
 }
 
@@ -376,9 +381,9 @@ template <bool WEIGHTED>
 hipError_t gather(const MoveArgs& a, hipStream_t stream) {
     const Grid g = move_grid(a, EPX_GATHER_VPL);
     if (g.full)
-        hipLaunchKernelGGL((k_gather<WEIGHTED, true>), g.blocks, dim3(kMoveThreads), 0, stream, a, g.Hv, g.pieces);
+        hipLaunchKernelGGL((k_gather<WEIGHTED, true>), g.blocks, dim3(kGatherThreads), 0, stream, a, g.Hv, g.pieces);
     else
-        hipLaunchKernelGGL((k_gather<WEIGHTED, false>), g.blocks, dim3(kMoveThreads), 0, stream, a, g.Hv, g.pieces);
+        hipLaunchKernelGGL((k_gather<WEIGHTED, false>), g.blocks, dim3(kGatherThreads), 0, stream, a, g.Hv, g.pieces);
     return hipGetLastError();
 }
 

@@ -37,7 +37,7 @@
  *    Microscaling (E2M1: magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6); bfloat16
  *    = upper 16 bits of IEEE binary32, rounded to nearest-even.
  *
- * Readings where the pages are silent (each also listed in the design doc):
+ * Readings where the pages are silent (the design notes list each one too):
  *  - segment of expert e is e / (E/S); with a fused shared expert every
  *    segment gets an extra group 0, only segment src_seg receives rows in
  *    it (all T tokens, slot index K, expert id E, weight 1 in combine);
