@@ -114,13 +114,14 @@ def cpu_baseline(w, host) -> dict:
         t0 = time.perf_counter()
         L = orc.layout(oc, host["ids"])
         tr = L["token_row"]
-        orc.dispatch(oc, tr, host["x"])
-        orc.dispatch_nvfp4(oc, tr, host["x"])
-        orc.combine(oc, tr, host["out"], host["probs"])
-        orc.combine_bwd(oc, tr, host["gy"], host["probs"])
-        orc.dispatch_bwd(oc, tr, host["grad_recv"])
+        res = {"layout": L, "recv": orc.dispatch(oc, tr, host["x"]),
+               "nvfp4": orc.dispatch_nvfp4(oc, tr, host["x"]),
+               "y": orc.combine(oc, tr, host["out"], host["probs"]),
+               "gout": orc.combine_bwd(oc, tr, host["gy"], host["probs"]),
+               "gx": orc.dispatch_bwd(oc, tr, host["grad_recv"])}
         runs.append(time.perf_counter() - t0)
     dt = statistics.median(runs)
+    host["oracle_results"] = res
     cpu = platform.processor() or platform.machine()
     try:
         with open("/proc/cpuinfo") as f:
@@ -385,10 +386,41 @@ def main() -> int:
                 "gy": gy.view(torch.int16).cpu().numpy().view(np.uint16).reshape(T, H),
                 "grad_recv": grad_recv.view(torch.int16).cpu().numpy().view(np.uint16).reshape(R, H)}
         result["cpu_baseline"] = cpu_baseline(w, host)
+        result["parity"] = parity_of_run(torch, host["oracle_results"], lay, recv, codes, scales, rowscale,
+                                         y, gout, gx, R, T, H)
+        log(f"[bench] parity of this run against the oracle: {result['parity']}")
     else:
         result["cpu_baseline"] = None
+        result["parity"] = None
     print(json.dumps(result), flush=True)
     return 0
+
+
+def parity_of_run(torch, o: dict, lay, recv, codes, scales, rowscale, y, gout, gx, R, T, H) -> dict:
+    """Compare the outputs of this run's last step with the oracle's results
+    on the same inputs, bit for bit (rows a layout leaves unused are not
+    part of the contract and are skipped)."""
+    def host(t):
+        return t.contiguous().view(-1).view(torch.uint8).cpu().numpy()
+
+    L = o["layout"]
+    tr = L["token_row"]
+    kept = np.unique(tr[tr >= 0])
+    ok = {}
+    ok["layout"] = bool(all(np.array_equal(getattr(lay, k).cpu().numpy().reshape(-1), L[k].reshape(-1))
+                            for k in ("counts", "seg_base", "row_offsets", "token_row", "flags"))
+                        and np.array_equal(lay.expert_ids.cpu().numpy()[kept], L["expert_ids"][kept])
+                        and np.array_equal(lay.src_info.cpu().numpy()[kept], L["src_info"][kept]))
+    ok["dispatch"] = bool(np.array_equal(host(recv).view(np.uint16).reshape(R, H)[kept], o["recv"][kept]))
+    oc, os_, orr = o["nvfp4"]
+    ok["dispatch_nvfp4"] = bool(np.array_equal(host(codes).reshape(R, H // 2)[kept], oc.reshape(R, H // 2)[kept])
+                                and np.array_equal(host(scales).reshape(R, H // 16)[kept], os_.reshape(R, H // 16)[kept])
+                                and np.array_equal(host(rowscale).view(np.uint16)[kept], orr.reshape(-1)[kept]))
+    ok["combine"] = bool(np.array_equal(host(y).view(np.uint16).reshape(T, H), o["y"].reshape(T, H)))
+    ok["combine_bwd"] = bool(np.array_equal(host(gout).view(np.uint16).reshape(R, H)[kept], o["gout"].reshape(R, H)[kept]))
+    ok["dispatch_bwd"] = bool(np.array_equal(host(gx).view(np.uint16).reshape(T, H), o["gx"].reshape(T, H)))
+    ok["all_bit_exact"] = all(ok.values())
+    return ok
 
 
 def capture(torch, fn):
