@@ -63,7 +63,7 @@ int derive(const ep_cfg_t* c, Shape* d) {
         d->min_rows = slots + (slots < groups ? slots : groups) * (int64_t)(d->A - 1);
     }
     if (d->min_rows >= (int64_t(1) << 31)) return EP_EINVAL;  // rows are int32
-    d->tiles = layout_tiles((int64_t)d->T * d->K);
+    d->tiles = layout_tiles((int64_t)d->T * d->K, d->NG);
     d->ws_bytes = kWorkspaceHeader + d->tiles * (int64_t)d->NG * 4;
     d->R = c->recv_rows;
     d->flags = c->flags;
@@ -195,7 +195,7 @@ int ep_dispatch_layout(const ep_cfg_t* cfg, const int32_t* topk_ids, void* works
     a.rank_blocks = (int32_t)std::max<int64_t>(d.tiles, std::min<int32_t>(d.NG, 256));
     // One tile holds every slot in the single-pass mode.
     a.slots_per_thread = a.mode == kLayoutSmall ? (routed <= 512 ? 2 : (routed <= 1024 ? 4 : 8))
-                                                : layout_slots_per_thread(routed);
+                                                : layout_slots_per_thread(routed, d.NG);
     return status_of(launch_layout(a, static_cast<hipStream_t>(stream)));
 }
 

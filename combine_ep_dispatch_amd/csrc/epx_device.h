@@ -18,22 +18,6 @@ constexpr int kMaxSlots = EP_MAX_SLOTS;  // K + shared_expert: one slot per lane
 constexpr int kLayoutThreads = 256;                      // 4 waves
 constexpr int kLayoutWaves = kLayoutThreads / kWave;
 constexpr int kWorkspaceHeader = 256;                    // reserved header before the descriptors
-constexpr int kTargetTiles = 64;                         // tiles aimed for by the tile-size choice
-
-// Routed slots per thread in one layout tile (2, 4 or 8): the smallest that
-// keeps the number of tiles near kTargetTiles, so that short inputs get more
-// workgroups and long ones a short look-back.
-inline int layout_slots_per_thread(int64_t routed_slots) {
-    const int64_t per = (routed_slots + (int64_t)kLayoutThreads * kTargetTiles - 1) /
-                        ((int64_t)kLayoutThreads * kTargetTiles);
-    return per <= 2 ? 2 : (per <= 4 ? 4 : 8);
-}
-inline int64_t layout_tiles(int64_t routed_slots) {
-    const int64_t tile = (int64_t)kLayoutThreads * layout_slots_per_thread(routed_slots);
-    const int64_t nt = (routed_slots + tile - 1) / tile;
-    return nt < 1 ? 1 : nt;
-}
-
 // Up to this many tiles the layout takes the direct path: the histogram
 // launch stores each tile's per-group counts as a row of a [tile][group]
 // table, and every rank workgroup sums each group's whole column (its prefix
@@ -42,6 +26,37 @@ inline int64_t layout_tiles(int64_t routed_slots) {
 // tile count.
 constexpr int kDirectMaxTiles = 256;
 inline bool layout_direct(int64_t tiles) { return tiles <= kDirectMaxTiles; }
+
+// Direct-path column sums: lanes that share one group's column (a power of
+// two, lanes * NG <= 256 where NG allows), each summing every lanes-th tile
+// with kDirectBatch loads in flight.
+constexpr int kDirectBatch = 64;
+__host__ __device__ inline int direct_lanes_per_group(int NG) {
+    return NG > 128 ? 1 : (NG > 64 ? 2 : (NG > 32 ? 4 : (NG > 16 ? 8 : (NG > 8 ? 16 : (NG > 4 ? 32 : 64)))));
+}
+
+// Routed slots per thread in one layout tile (1, 2, 4 or 8).  Smaller tiles
+// mean more workgroups, each ranking fewer slots; the cost is more rows in
+// each column of the direct count table, and past kDirectBatch per lane a
+// column sum takes another round trip to memory.  Measured on MI355X: going
+// from 4 or 8 slots per thread down to 2 pays for that extra round trip
+// (fewer serial match-any rounds per wave), going from 2 to 1 does not.  So:
+// 1 when that fits one batch of loads, else the smallest of 2, 4, 8 that
+// keeps the direct path (at most kDirectMaxTiles tiles), else 8 (look-back).
+inline int layout_slots_per_thread(int64_t routed_slots, int NG) {
+    auto tiles_at = [&](int spt) {
+        return (routed_slots + (int64_t)kLayoutThreads * spt - 1) / ((int64_t)kLayoutThreads * spt);
+    };
+    if (tiles_at(1) <= (int64_t)kDirectBatch * direct_lanes_per_group(NG) && tiles_at(1) <= kDirectMaxTiles) return 1;
+    for (int spt = 2; spt < 8; spt *= 2)
+        if (tiles_at(spt) <= kDirectMaxTiles) return spt;
+    return 8;
+}
+inline int64_t layout_tiles(int64_t routed_slots, int NG) {
+    const int64_t tile = (int64_t)kLayoutThreads * layout_slots_per_thread(routed_slots, NG);
+    const int64_t nt = (routed_slots + tile - 1) / tile;
+    return nt < 1 ? 1 : nt;
+}
 
 // Up to this many routed slots (one tile of 256 x 8) the layout is one
 // launch: every workgroup ranks all slots in LDS to learn the group totals.
@@ -136,7 +151,7 @@ struct LayoutArgs {
     int32_t tiles;
     int32_t mode;              // kLayoutLookback, kLayoutDirect or kLayoutSmall
     int32_t rank_blocks;       // workgroups of the rank pass: max(tiles, min(NG, 256))
-    int32_t slots_per_thread;  // 2, 4 or 8 (layout_slots_per_thread)
+    int32_t slots_per_thread;  // 1, 2, 4 or 8 (layout_slots_per_thread)
 };
 hipError_t launch_layout(const LayoutArgs& a, hipStream_t stream);
 

@@ -166,8 +166,8 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout_rank(LayoutArgs a) {
         // flight per lane this is one round trip for up to 64 * tpg tiles.
         // The partial sums meet by xor-shuffles inside the lane group (all
         // lanes of a group are active or inactive together).
-        constexpr int kBatch = 64;
-        const int tpg = NG > 128 ? 1 : (NG > 64 ? 2 : (NG > 32 ? 4 : (NG > 16 ? 8 : (NG > 8 ? 16 : (NG > 4 ? 32 : 64)))));
+        constexpr int kBatch = kDirectBatch;
+        const int tpg = direct_lanes_per_group(NG);
         const int r = tid & (tpg - 1);
         for (int g = tid / tpg; g < NG; g += kLayoutThreads / tpg) {
             const uint32_t* col = a.desc + g;
@@ -183,6 +183,12 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout_rank(LayoutArgs a) {
                     const int j = j0 + i * tpg;
                     v[i] = col[(uint32_t)min(j, a.tiles - 1) * (uint32_t)NG];
                 }
+                // Every load of the batch is issued before the first is
+                // consumed: left to itself the scheduler may interleave the
+                // sums with the issue to save registers, which waits on the
+                // first loads with half the batch not yet sent (a second
+                // round trip to memory).
+                __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                 for (int i = 0; i < kBatch; ++i) {
                     const int j = j0 + i * tpg;
@@ -529,6 +535,7 @@ void launch_spt(const LayoutArgs& a, hipStream_t stream) {
 
 hipError_t launch_layout(const LayoutArgs& a, hipStream_t stream) {
     switch (a.slots_per_thread) {
+        case 1: launch_spt<1>(a, stream); break;
         case 2: launch_spt<2>(a, stream); break;
         case 4: launch_spt<4>(a, stream); break;
         default: launch_spt<8>(a, stream); break;

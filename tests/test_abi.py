@@ -14,6 +14,36 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
+def layout_tiles(routed, ng):
+    """Layout tiles: 256 threads x spt slots.  spt is 1 when every lane of
+    the direct column sums then covers its tiles in one 64-load batch (at
+    most 256 tiles), else the smallest of 2, 4, 8 giving at most 256 tiles,
+    else 8."""
+    lanes = 1
+    while lanes < 64 and ng * lanes * 2 <= 256:
+        lanes *= 2
+
+    def tiles_at(spt):
+        return max(1, -(-routed // (256 * spt)))
+
+    if tiles_at(1) <= min(256, 64 * lanes):
+        return tiles_at(1)
+    for spt in (2, 4):
+        if tiles_at(spt) <= 256:
+            return tiles_at(spt)
+    return tiles_at(8)
+
+
+def test_layout_tiles_rule():
+    # DeepSeek-V3 share (256 groups): one lane per group, 64 tiles per batch
+    assert layout_tiles(4096 * 8, 256) == 64          # 2 slots per thread (1 would need 2 batches)
+    assert layout_tiles(1024 * 8, 256) == 32          # 1 slot per thread
+    assert layout_tiles(16384 * 6, 68) == 192         # 2 slots per thread, 2 batches of 2 lanes
+    assert layout_tiles(4096 * 6, 68) == 96           # 1 slot per thread, 2 lanes per group
+    assert layout_tiles(70001 * 8, 64) == 274         # past the direct path
+    assert layout_tiles(0, 8) == 1
+
+
 @pytest.fixture(scope="module")
 def L():
     from combine_ep_dispatch_amd import _lib
@@ -82,10 +112,8 @@ def test_query_sizes(L, orc):
         assert rows == orc.min_recv_rows(oc)
         assert g == c.num_experts // c.num_segments + c.shared_expert
         routed = c.num_tokens * c.top_k
-        per = -(-routed // (256 * 64))  # tiles of 256 x {2,4,8} slots, about 64 of them
-        spt = 2 if per <= 2 else (4 if per <= 4 else 8)
-        tiles = max(1, -(-routed // (256 * spt)))
-        assert ws == 256 + tiles * c.num_segments * g * 4
+        ng = c.num_segments * g
+        assert ws == 256 + layout_tiles(routed, ng) * ng * 4
     # the bound is reached by some routing and never exceeded (oracle layout)
     rng = np.random.default_rng(0)
     c = cfg(num_tokens=9, num_experts=12, num_segments=3, top_k=3, align=5, shared_expert=1)

@@ -96,8 +96,11 @@ EDGE = {
     "big_align": dict(T=300, A=256, S=3, E_loc=3, K=2),
     "many_tiles": dict(T=9000, S=4, E_loc=16, K=8, A=16, H=16),
     "hot_expert": dict(T=4000, S=2, E_loc=1, K=1, H=32, A=8),
-    "tile4_ragged": dict(T=5001, S=8, E_loc=8, K=8, H=16, A=4),          # 4 slots/thread tiles
-    "tile8_79_tiles": dict(T=20011, S=4, E_loc=16, K=8, H=16, A=2),       # 8 slots/thread, 79 tiles
+    "spt1_157_tiles": dict(T=5001, S=8, E_loc=8, K=8, H=16, A=4),        # 1 slot/thread, ragged last tile
+    "spt1_at_cap": dict(T=4096, S=4, E_loc=32, K=8, H=16, A=8),           # 128 groups: 128 tiles, one batch
+    "spt2_past_cap": dict(T=4097, S=4, E_loc=32, K=8, H=16, A=8),         # one slot more: 2 slots/thread
+    "spt4_157_tiles": dict(T=20011, S=4, E_loc=16, K=8, H=16, A=2),       # 4 slots/thread
+    "direct_four_batches": dict(T=25000, S=8, E_loc=32, K=8, H=16, A=2),  # 256 groups, 196 tiles: 4 load batches
     "direct_254_tiles": dict(T=65000, S=4, E_loc=16, K=8, H=16, A=2, bad_p=0.01),  # direct path, near its tile limit
     "lookback_274_tiles": dict(T=70001, S=4, E_loc=16, K=8, H=16, A=2, shared=1, src=3, bad_p=0.01),  # look-back path
     "single_pass_max_groups": dict(T=200, S=8, E_loc=255, K=8, shared=1, A=4, H=32),  # 2048 groups, one launch
