@@ -126,8 +126,20 @@ __device__ __forceinline__ int32_t slot_row_of_lane(const MoveArgs& a, int32_t t
     return r;
 }
 
-__device__ __forceinline__ float slot_weight_of_lane(const MoveArgs& a, int32_t t, int lane) {
-    return (a.probs != nullptr && lane < a.K) ? a.probs[(int64_t)t * a.K + lane] : 1.0f;
+// Slot row and weight of token t in lane k together (row as above; weight
+// probs[t,k] for k < K, 1 for the shared slot, lanes past it and without
+// probs).  Both loads are issued before either value is tested: each reads
+// at a lane index clamped into the token's slots (K >= 1) instead of under
+// a lane branch, whose result test would otherwise wait for the row before
+// the weight load is sent (a second round trip to memory before the payload
+// loads can start).
+__device__ __forceinline__ void slot_row_and_weight_of_lane(const MoveArgs& a, int32_t t, int lane, int32_t& row,
+                                                            float& w) {
+    const int32_t r = a.token_row[(int64_t)t * a.Kp + min(lane, a.Kp - 1)];
+    float p = 1.0f;
+    if (a.probs != nullptr) p = a.probs[(int64_t)t * a.K + min(lane, a.K - 1)];
+    row = (lane < a.Kp && r < a.R) ? r : -1;
+    w = lane < a.K ? p : 1.0f;
 }
 
 // Geometry of the scatter grid.  Workgroups are handed to the 8 XCDs
@@ -215,8 +227,12 @@ __global__ __launch_bounds__(kGatherThreads) void k_gather(MoveArgs a, int32_t H
     const int32_t v0 = piece * (kWave * VPL) + lane;
     const v4u* src = reinterpret_cast<const v4u*>(a.src);
 
-    const int32_t my_row = slot_row_of_lane(a, t, lane);
-    const float my_w = WEIGHTED ? slot_weight_of_lane(a, t, lane) : 1.0f;
+    int32_t my_row;
+    float my_w = 1.0f;
+    if (WEIGHTED)
+        slot_row_and_weight_of_lane(a, t, lane, my_row, my_w);
+    else
+        my_row = slot_row_of_lane(a, t, lane);
 
     float acc[VPL][8];
 #pragma unroll
