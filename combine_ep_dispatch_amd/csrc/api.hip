@@ -194,7 +194,7 @@ int ep_dispatch_layout(const ep_cfg_t* cfg, const int32_t* topk_ids, void* works
     else a.mode = kLayoutLookback;
     a.rank_blocks = (int32_t)std::max<int64_t>(d.tiles, std::min<int32_t>(d.NG, 256));
     // One tile holds every slot in the single-pass mode.
-    a.slots_per_thread = a.mode == kLayoutSmall ? (routed <= 512 ? 2 : (routed <= 1024 ? 4 : 8))
+    a.slots_per_thread = a.mode == kLayoutSmall ? (routed <= 256 ? 1 : (routed <= 512 ? 2 : 4))
                                                 : layout_slots_per_thread(routed, d.NG);
     return status_of(launch_layout(a, static_cast<hipStream_t>(stream)));
 }

@@ -58,9 +58,13 @@ inline int64_t layout_tiles(int64_t routed_slots, int NG) {
     return nt < 1 ? 1 : nt;
 }
 
-// Up to this many routed slots (one tile of 256 x 8) the layout is one
+// Up to this many routed slots (one tile of 256 x 4) the layout is one
 // launch: every workgroup ranks all slots in LDS to learn the group totals.
-constexpr int64_t kSmallMaxSlots = 2048;
+// Measured on MI355X, the one launch beats the histogram + rank pair up to
+// 1024 slots (8.8 against 10.4 us at 1024); at 1280 and above the pair wins
+// (10.4 against 11.7 us), as every workgroup's ranking of the whole tile
+// then takes longer than the second launch.
+constexpr int64_t kSmallMaxSlots = 1024;
 
 // How k_layout_rank resolves a tile's in-group prefix.
 constexpr int kLayoutLookback = 0;  // decoupled look-back over descriptors

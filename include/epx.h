@@ -165,7 +165,7 @@ int ep_query(const ep_cfg_t* cfg, int64_t* min_recv_rows, int64_t* workspace_byt
  * ranks every slot inside its group and writes token_row, expert_ids and
  * src_info.  The prefix over earlier tiles comes from one of three paths,
  * all with identical results:
- *  - up to 2048 routed slots (one tile): a single launch in which every
+ *  - up to 1024 routed slots (one tile): a single launch in which every
  *    workgroup ranks all slots itself;
  *  - up to 256 tiles: direct sums of a [tile][group] table of tile counts
  *    (two kernels);
