@@ -35,7 +35,11 @@
 //    rows (and weights) arrive with one vector load, lane k holding slot k,
 //    are broadcast with v_readlane so every row address is wave-uniform, and
 //    the loads of up to 8 slots are issued before they are reduced in slot
-//    order.
+//    order.  The output row is written with nontemporal stores: with plain
+//    stores its lines stayed dirty in L2 and the MALL, and the next kernel
+//    paid for their write-back while reading its own cold input.  At
+//    DeepSeek-V3 size the whole six-kernel step went from ~455 to ~417 us,
+//    and combine alone from 91 to 88 us.
 #include "epx_device.h"
 
 #ifndef EPX_SCATTER_VPL
@@ -54,7 +58,7 @@
 #define EPX_SCATTER_NT_LOADS 0
 #endif
 #ifndef EPX_NT_STORES
-#define EPX_NT_STORES 0
+#define EPX_NT_STORES 1  // gathers: nontemporal output stores
 #endif
 #ifndef EPX_SCATTER_NT_STORES
 #define EPX_SCATTER_NT_STORES 1
