@@ -257,13 +257,15 @@ def main() -> int:
 
     # per-op kernel durations: a graph of LAUNCHES back-to-back launches per op,
     # bracketed by HIP events on the stream the kernels run on
-    LAUNCHES, REPS = 8, max(5, args.steps // 5)
+    LAUNCHES, REPS, OP_WARMUP = 8, max(10, args.steps // 2), 5
     op_us = {}
     for n, fn in ops + extra_ops:
         def many(fn=fn):
             for _ in range(LAUNCHES):
                 fn()
         g = capture(torch, many)
+        for _ in range(OP_WARMUP):  # untimed: the previous op's lines leave the caches
+            g.replay()
         times = []
         for _ in range(REPS):
             a = torch.cuda.Event(enable_timing=True)
@@ -372,7 +374,8 @@ def main() -> int:
         "hbm_frac": round(step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
         "fwd_dispatch_combine_tokens_per_s": round(T / (fwd_us * 1e-6), 1),
         "ops": per_op,
-        "ops_note": ("us/us_median/us_p10/us_p90: warm, graphs of 8 back-to-back launches; cold: one launch "
+        "ops_note": ("us/us_median/us_p10/us_p90: warm, graphs of 8 back-to-back launches, "
+                     f"{OP_WARMUP} untimed replays then {REPS} timed; cold: one launch "
                      f"after an untimed read of 1 GiB that evicts L2 and MALL ({COLD_REPS} reps); frac_of_copy: "
                      "against torch's 1 GiB device copy"),
         "copy_context_GBps": round(copy_gbps, 1),

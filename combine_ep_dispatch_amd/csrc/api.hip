@@ -93,6 +93,13 @@ int check_device() {
 
 int status_of(hipError_t e) { return e == hipSuccess ? EP_OK : EP_ELAUNCH; }
 
+// Kernels that launch one grid for the whole batch, with `per_token`
+// work-items per token: a grid dimension holds at most 2^32 - 1 work-items
+// (the movers split larger batches into chunks instead).
+bool grid_too_big(const Shape& d, int64_t per_token) {
+    return (int64_t)d.T * per_token + 1024 > 0xFFFFFFFFll;
+}
+
 // Layout arrays read by the payload calls.
 int check_layout_for_payload(const Shape& d, const ep_layout_t* L) {
     if (L == nullptr) return EP_EINVAL;
@@ -218,7 +225,7 @@ int ep_dispatch_nvfp4(const ep_cfg_t* cfg, const ep_layout_t* layout, const uint
     int rc = derive(cfg, &d);
     if (rc != EP_OK) return rc;
     if ((rc = check_rows(d)) != EP_OK) return rc;
-    if (d.H % 16 != 0 || d.H > nvfp4_max_hidden()) return EP_EINVAL;
+    if (d.H % 16 != 0 || d.H > nvfp4_max_hidden() || grid_too_big(d, 64)) return EP_EINVAL;
     if ((rc = check_layout_for_payload(d, layout)) != EP_OK) return rc;
     if (bad_buffer(x, (int64_t)d.T * d.H * 2, 16) || bad_buffer(codes, d.R * (d.H / 2), 16) ||
         bad_buffer(scales, d.R * (d.H / 16), 1) || bad_buffer(rowscale, d.R * 2, 2))
@@ -247,7 +254,7 @@ int ep_dispatch_fp8(const ep_cfg_t* cfg, const ep_layout_t* layout, const uint16
     int rc = derive(cfg, &d);
     if (rc != EP_OK) return rc;
     if ((rc = check_rows(d)) != EP_OK) return rc;
-    if (d.H % 128 != 0 || d.H > fp8_max_hidden()) return EP_EINVAL;
+    if (d.H % 128 != 0 || d.H > fp8_max_hidden() || grid_too_big(d, 64)) return EP_EINVAL;
     if ((rc = check_layout_for_payload(d, layout)) != EP_OK) return rc;
     if (bad_buffer(x, (int64_t)d.T * d.H * 2, 16) || bad_buffer(codes, d.R * d.H, 16) ||
         bad_buffer(scales, d.R * (d.H / 128) * 4, 4))
@@ -318,6 +325,7 @@ int ep_combine_bwd_probs(const ep_cfg_t* cfg, const ep_layout_t* layout, const u
     if (rc != EP_OK) return rc;
     if ((rc = check_rows(d)) != EP_OK) return rc;
     if (layout == nullptr || bad_buffer(layout->token_row, (int64_t)d.T * d.Kp * 4, 4)) return EP_EINVAL;
+    if (grid_too_big(d, 256)) return EP_EINVAL;
     if (bad_buffer(grad_y, (int64_t)d.T * d.H * 2, 16) || bad_buffer(expert_out, d.R * d.H * 2, 16) ||
         bad_buffer(grad_probs, (int64_t)d.T * d.K * 4, 4))
         return EP_EINVAL;
@@ -331,6 +339,7 @@ int ep_indices_to_multihot(const ep_cfg_t* cfg, const int32_t* topk_ids, const f
     Shape d;
     int rc = derive(cfg, &d);
     if (rc != EP_OK) return rc;
+    if (grid_too_big(d, 64)) return EP_EINVAL;
     if (bad_buffer(topk_ids, (int64_t)d.T * d.K * 4, 4) || bad_buffer(routing_map, (int64_t)d.T * d.E, 1))
         return EP_EINVAL;
     if (dense_probs != nullptr && (bad_buffer(dense_probs, (int64_t)d.T * d.E * 4, 4) ||
@@ -354,6 +363,7 @@ int ep_multihot_to_indices(const ep_cfg_t* cfg, const uint8_t* routing_map, cons
     Shape d;
     int rc = derive(cfg, &d);
     if (rc != EP_OK) return rc;
+    if (grid_too_big(d, 64)) return EP_EINVAL;
     if (bad_buffer(routing_map, (int64_t)d.T * d.E, 1) || bad_buffer(topk_ids, (int64_t)d.T * d.K * 4, 4))
         return EP_EINVAL;
     if (probs != nullptr && (bad_buffer(probs, (int64_t)d.T * d.K * 4, 4) ||

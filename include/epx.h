@@ -56,6 +56,13 @@ extern "C" {
 #define EP_EINVAL (-1)   /* an argument fails a host-side check                */
 #define EP_ELAUNCH (-2)  /* the HIP runtime reported an error enqueueing work  */
 #define EP_ENOTSUP (-3)  /* the current device is not gfx950                   */
+/* A HIP grid dimension holds at most 2^32 - 1 work-items.  ep_dispatch,
+ * ep_combine, ep_dispatch_bwd and ep_combine_bwd split larger batches into
+ * several launches.  The calls that launch one grid per batch return
+ * EP_EINVAL past it: ep_dispatch_nvfp4, ep_dispatch_fp8 and the routing-map
+ * conversions from T = 2^26 - 16 tokens (one wave per token), and
+ * ep_combine_bwd_probs from T = 2^24 - 4 (one 256-thread workgroup per
+ * token). */
 
 /* Bits of ep_cfg_t.flags. */
 #define EP_ZERO_PAD_ROWS 1u    /* also write zeros into the payload of pad rows */

@@ -264,3 +264,36 @@ def test_new_entry_points_reject_bad_arguments(L):
     assert L.ep_multihot_to_indices(ctypes.byref(cc), fake, None, fake, fake, None, None) == -1
     assert L.ep_multihot_to_indices(ctypes.byref(cc), fake, fake, fake, fake, fake + 2, None) == -1
     assert L.ep_multihot_to_indices(None, fake, fake, fake, fake, None, None) == -1
+
+
+def test_single_grid_calls_reject_batches_past_the_grid_limit(L):
+    """A HIP grid dimension holds at most 2^32 - 1 work-items.  The calls that
+    launch one grid per batch reject a batch whose grid would not fit: one
+    wave per token for the quantizing dispatches and the routing-map
+    conversions (T >= 2^26 - 16), one 256-thread workgroup per token for the
+    probability gradient (T >= 2^24 - 4).  The configurations themselves are
+    valid (ep_query accepts them), so the grid rule is what rejects them.
+    Only batches at the limit are passed: below it these fake pointers would
+    reach a launch."""
+    from combine_ep_dispatch_amd._lib import EpLayout
+
+    fake = 0x10000
+    lay = EpLayout(*([fake] * 8))
+    for T, calls in ((2 ** 26 - 16, ("nvfp4", "fp8", "to_multihot", "to_indices")), (2 ** 24 - 4, ("probs",))):
+        c = cfg(num_tokens=T, hidden=256, align=1)
+        st, rows, _, _ = query(L, c)
+        assert st == 0
+        c.recv_rows = rows
+        cc = c.to_c()
+        for name in calls:
+            if name == "nvfp4":
+                rc = L.ep_dispatch_nvfp4(ctypes.byref(cc), ctypes.byref(lay), fake, fake, fake, fake, None)
+            elif name == "fp8":
+                rc = L.ep_dispatch_fp8(ctypes.byref(cc), ctypes.byref(lay), fake, fake, fake, None)
+            elif name == "to_multihot":
+                rc = L.ep_indices_to_multihot(ctypes.byref(cc), fake, None, fake, None, None)
+            elif name == "to_indices":
+                rc = L.ep_multihot_to_indices(ctypes.byref(cc), fake, None, fake, None, None, None)
+            else:
+                rc = L.ep_combine_bwd_probs(ctypes.byref(cc), ctypes.byref(lay), fake, fake, fake, None)
+            assert rc == -1, (name, T)
