@@ -54,7 +54,7 @@ def test_named_workload_full_size(G, name):
         assert f == 0
 
 
-@pytest.mark.parametrize("seed", range(24))
+@pytest.mark.parametrize("seed", range(128))
 def test_random_shapes(G, seed):
     rng = np.random.default_rng(seed)
     kw = {}
