@@ -66,15 +66,21 @@ def source_digest() -> str:
     return h.hexdigest()[:16]
 
 
-def traffic_for(op: str):
-    """HBM bytes per launch of `op` measured with rocprofv3 counters (see
-    profiles/), or None when missing or taken on different kernel sources."""
-    path = os.path.join(ROOT, "profiles", "traffic_dsv3.json")
+WORKLOAD_TITLES = {"dsv3": "DeepSeek-V3-shaped share", "tiny": "tiny", "skewed": "skewed routing (Zipf 1.2)",
+                   "nvfp4": "NVFP4 dispatch with a fused shared expert",
+                   "capacity": "capacity overflow (Zipf 1.5)"}
+
+
+def traffic_for(op: str, workload: str):
+    """HBM bytes per launch of `op` measured with rocprofv3 counters on
+    `workload` (see profiles/), or None when missing, taken on another
+    workload or on different kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         doc = json.load(f)
-    if doc.get("source_digest") != source_digest():
+    if doc.get("workload") != workload or doc.get("source_digest") != source_digest():
         return None
     entry = doc.get("ops", {}).get(op)
     return None if entry is None else entry.get("bytes_per_launch")
@@ -348,7 +354,7 @@ def main() -> int:
     dom = max((n for n in names if n != "layout"), key=lambda n: per_op[n]["us"])
     fwd_us = per_op["layout"]["us"] + per_op["dispatch"]["us"] + per_op["combine"]["us"]
     roof = {"bound": "hbm", "kernel": dom, "achieved": per_op[dom]["GBps"], "peak": HBM_PEAK_GBPS,
-            "unit": "GB/s", "frac": per_op[dom]["frac"], "traffic": traffic_for(dom),
+            "unit": "GB/s", "frac": per_op[dom]["frac"], "traffic": traffic_for(dom, args.workload),
             "algorithmic_bytes_per_launch": nbytes[dom], "avg_launch_us": per_op[dom]["us"]}
 
     result = {
@@ -367,7 +373,7 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": f"DeepSeek-V3-shaped share: {wl.describe(w)}",
+        "config": {"workload": f"{WORKLOAD_TITLES.get(args.workload, args.workload)}: {wl.describe(w)}",
                    "step": "layout + bf16 dispatch + NVFP4 dispatch + combine + combine_bwd + dispatch_bwd",
                    "tokens_per_step": T, "recv_rows": R, "kept_slots": kept, "used_rows": used_rows},
         "effective_GBps": round(step_bytes / (ms_step * 1e-3) / 1e9, 1),

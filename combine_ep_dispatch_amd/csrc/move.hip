@@ -17,20 +17,21 @@
 // contiguous.  When the pieces tile the row exactly the lane guards vanish.
 //  - The scatters run one wave per (token, piece, slot), with 2 KiB pieces:
 //    the wave loads its row index, weight and payload piece together (one
-//    round trip), then issues its nontemporal stores.  The 8 waves of a
-//    workgroup are 8 slots of one (token, piece), and with K' > 8 the slot
-//    blocks of a (token, piece) run on one XCD (see ScatterGrid), so a
-//    token's x row is fetched from HBM once and re-read by the other slots
-//    from L2.  8 waves per workgroup rather than 4 shortened the whole
-//    step by 2% (461 against 470 us at DeepSeek-V3 size), with the same
-//    isolated kernel times.  Short
-//    waves with streaming stores keep many more writes in flight than one
-//    wave storing all K' copies: at DeepSeek-V3 size the dispatch scatter
-//    went from 106 to ~92 us and the combine-backward one from 102 to ~90.
-//    The (token, piece, slot) of a workgroup comes from its index with a
-//    mask, a shift and a multiply by a precomputed reciprocal: the per-wave
-//    scalar work bounds these short waves, and a division there cost more
-//    than the store.
+//    round trip), then issues its nontemporal stores.  The K' slot waves
+//    of a (token, piece) are consecutive waves on one XCD (see
+//    ScatterGrid), so a token's x row is fetched from HBM once and re-read
+//    by the other slots from L2, and no wave is idle whatever K' is (with
+//    K' = 9, slot blocks of 8 waves left 7 of every 16 idle, and the
+//    combine-backward scatter of a cold input took 133 instead of 107 us).
+//    8 waves per workgroup rather than 4 shortened the whole step by 2%
+//    (461 against 470 us at DeepSeek-V3 size), with the same isolated
+//    kernel times.  Short waves with streaming stores keep many more
+//    writes in flight than one wave storing all K' copies: at DeepSeek-V3
+//    size the dispatch scatter went from 106 to ~92 us and the
+//    combine-backward one from 102 to ~90.  The (token, piece, slot) of a
+//    wave comes from the workgroup index with masks, shifts and multiplies
+//    by precomputed reciprocals: the per-wave scalar work bounds these
+//    short waves, and a division there cost more than the store.
 //  - The gathers run one wave per (token, piece): the token's K' receive
 //    rows (and weights) arrive with one vector load, lane k holding slot k,
 //    are broadcast with v_readlane so every row address is wave-uniform, and
@@ -152,30 +153,35 @@ __device__ __forceinline__ void slot_row_and_weight_of_lane(const MoveArgs& a, i
 }
 
 // Geometry of the scatter grid.  Workgroups are handed to the 8 XCDs
-// round-robin by index, and the slot blocks of one (token, piece) should
-// share an XCD's L2 so that the piece is fetched once: workgroup
-// b = 8q + x takes slot block kb = q & (2^lg_kb - 1) of (token, piece)
-// number rest = 8 (q >> lg_kb) + x, so they are 8 indices apart.  Then
-// t = rest / pieces (as (rest * div_mul) >> div_shift, exact for every
-// 32-bit rest) and p = rest - t * pieces; t0 is added to t for launches
-// split in token chunks [t0, t1).  Indices past the last (token, piece)
-// exit.
+// round-robin by index, and the K' slot waves of one (token, piece) should
+// share an XCD's L2 so that the piece is fetched once.  Workgroup b = 8q + x
+// runs on XCD x; that XCD's waves j = 8q + w (w = wave in the workgroup)
+// take the (token, piece, slot) triples of (token, piece) numbers
+// x, x + 8, x + 16, ... in order: local pair l = j / K', slot k = j - l K',
+// pair rest = 8 l + x.  Every wave has a slot, whatever K' is, and the K'
+// waves of a pair are consecutive on one XCD.  With K' = 8 this is
+// workgroup b = pair b, one wave per slot.  Then t = rest / pieces and
+// p = rest - t * pieces; the divisions are multiplies by host-computed
+// reciprocals (exact for every 32-bit numerator); t0 is added to t for
+// launches split in token chunks [t0, t1).  Indices past the last
+// (token, piece) exit.
 struct ScatterGrid {
-    int32_t Hv, pieces, lg_kb, t0, t1;  // this launch covers tokens [t0, t1)
-    uint64_t div_mul;
-    uint32_t div_shift;
+    int32_t Hv, pieces, t0, t1;  // this launch covers tokens [t0, t1)
+    uint64_t div_mul, kp_mul;
+    uint32_t div_shift, kp_shift;
 };
 
 template <bool SCALED, bool FULL>
 __global__ __launch_bounds__(EPX_SCATTER_WAVES * kWave) void k_scatter(MoveArgs a, ScatterGrid g) {
     constexpr int VPL = EPX_SCATTER_VPL;
-    const uint32_t q = blockIdx.x >> 3;
-    const uint32_t kb = q & ((1u << g.lg_kb) - 1u), rest = ((q >> g.lg_kb) << 3) | (blockIdx.x & 7u);
+    const uint32_t j = (blockIdx.x >> 3) * EPX_SCATTER_WAVES + uniform((uint32_t)(threadIdx.x / kWave));
+    const uint32_t l = (uint32_t)(((uint64_t)j * g.kp_mul) >> g.kp_shift);
+    const int32_t k = (int32_t)(j - l * (uint32_t)a.Kp);
+    const uint32_t rest = (l << 3) | (blockIdx.x & 7u);
     const uint32_t tr = (uint32_t)(((uint64_t)rest * g.div_mul) >> g.div_shift);
     const int32_t p = (int32_t)(rest - tr * (uint32_t)g.pieces);
     const int32_t t = g.t0 + (int32_t)tr;
-    const int32_t k = (int32_t)kb * EPX_SCATTER_WAVES + uniform((int32_t)(threadIdx.x / kWave));
-    if (t >= g.t1 || k >= a.Kp) return;
+    if (t >= g.t1) return;
     const int lane = threadIdx.x & (kWave - 1);
     const int32_t Hv = g.Hv;
 
@@ -366,6 +372,16 @@ Grid move_grid(const MoveArgs& a, int vpl) {
     return g;
 }
 
+// q / d = (q * m) >> (32 + l) for every 32-bit q, with l = ceil(log2 d) and
+// m = floor(2^(32+l) / d) + 1 (Granlund and Montgomery, division by
+// invariant integers).
+void reciprocal(uint32_t d, uint64_t& m, uint32_t& shift) {
+    uint32_t l = 0;
+    while ((1ull << l) < d) ++l;
+    shift = 32 + l;
+    m = (uint64_t)(((unsigned __int128)1 << (32 + l)) / d) + 1;
+}
+
 template <bool SCALED>
 hipError_t scatter(const MoveArgs& a, hipStream_t stream) {
     if (a.T == 0) return hipSuccess;
@@ -374,24 +390,18 @@ hipError_t scatter(const MoveArgs& a, hipStream_t stream) {
     const int per_piece = kWave * EPX_SCATTER_VPL;
     g.pieces = (g.Hv + per_piece - 1) / per_piece;
     const bool full = g.Hv % per_piece == 0;
-    const int32_t kblocks = (a.Kp + EPX_SCATTER_WAVES - 1) / EPX_SCATTER_WAVES;
-    g.lg_kb = 0;
-    while ((1 << g.lg_kb) < kblocks) ++g.lg_kb;
-    // rest / pieces = (rest * m) >> (32 + l) with l = ceil(log2 pieces) and
-    // m = floor(2^(32+l) / pieces) + 1: exact for every rest < 2^32
-    // (Granlund and Montgomery, division by invariant integers).
-    uint32_t l = 0;
-    while ((1u << l) < (uint32_t)g.pieces) ++l;
-    g.div_shift = 32 + l;
-    g.div_mul = (uint64_t)(((unsigned __int128)1 << (32 + l)) / (uint32_t)g.pieces) + 1;
-    // A launch covers (token, piece) pairs rounded up to a multiple of 8,
-    // times the slot blocks, in workgroups of EPX_SCATTER_WAVES waves.
+    reciprocal((uint32_t)g.pieces, g.div_mul, g.div_shift);
+    reciprocal((uint32_t)a.Kp, g.kp_mul, g.kp_shift);
+    // A launch covers the (token, piece) pairs rounded up to a multiple of
+    // 8, times K' waves, in workgroups of EPX_SCATTER_WAVES waves per XCD.
     const int64_t max_blocks = kMaxLaunchItems / (EPX_SCATTER_WAVES * kWave);
-    const int64_t chunk = ((max_blocks >> g.lg_kb) - 7) / g.pieces;
+    const int64_t chunk = ((max_blocks - 8) / a.Kp * EPX_SCATTER_WAVES - 8) / g.pieces;
     if (chunk < 1) return hipErrorInvalidValue;
     for (int64_t t0 = 0; t0 < a.T; t0 += chunk) {
         const int64_t tokens = a.T - t0 < chunk ? a.T - t0 : chunk;
-        const int64_t n = ((tokens * g.pieces + 7) & ~int64_t(7)) << g.lg_kb;
+        const int64_t pairs_per_xcd = ((tokens * g.pieces + 7) & ~int64_t(7)) >> 3;
+        const int64_t blocks_per_xcd = (pairs_per_xcd * a.Kp + EPX_SCATTER_WAVES - 1) / EPX_SCATTER_WAVES;
+        const int64_t n = blocks_per_xcd * 8;
         g.t0 = (int32_t)t0;
         g.t1 = (int32_t)(t0 + tokens);
         if (full)
