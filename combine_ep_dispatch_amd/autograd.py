@@ -13,8 +13,11 @@ Marshalling only: every step runs in libepx's HIP kernels.
 
 dispatch() builds the layout (the "handle") and keeps it for the combine
 and both backward passes; rows past a segment's used rows are left as the
-buffers held them (zero for the buffers allocated here).  The routing is
-not differentiable; probs is, through the router-probability gradient.
+buffers held them (zero for the buffers allocated here).  Every routing
+gets a layout of its own, and each forward node keeps the layout it ran
+with, so routing the next batch before this one's backward is safe.  The
+routing is not differentiable; probs is, through the router-probability
+gradient.
 """
 
 from __future__ import annotations
@@ -31,46 +34,44 @@ __all__ = ["EpDispatcher"]
 
 class _Dispatch(torch.autograd.Function):
     @staticmethod
-    def forward(ctx, x, disp):
-        recv = torch.zeros(disp.cfg.recv_rows, disp.cfg.hidden, dtype=torch.bfloat16, device=x.device)
-        ep_dispatch(disp.cfg, disp.layout, x.contiguous().view(-1), recv.view(-1))
-        ctx.disp = disp
+    def forward(ctx, x, cfg, layout):
+        recv = torch.zeros(cfg.recv_rows, cfg.hidden, dtype=torch.bfloat16, device=x.device)
+        ep_dispatch(cfg, layout, x.contiguous().view(-1), recv.view(-1))
+        ctx.cfg, ctx.layout = cfg, layout
         return recv
 
     @staticmethod
     def backward(ctx, grad_recv):
-        disp = ctx.disp
-        gx = torch.empty(disp.cfg.num_tokens, disp.cfg.hidden, dtype=torch.bfloat16, device=grad_recv.device)
-        ep_dispatch_bwd(disp.cfg, disp.layout, grad_recv.to(torch.bfloat16).contiguous().view(-1), gx.view(-1))
-        return gx, None
+        cfg = ctx.cfg
+        gx = torch.empty(cfg.num_tokens, cfg.hidden, dtype=torch.bfloat16, device=grad_recv.device)
+        ep_dispatch_bwd(cfg, ctx.layout, grad_recv.to(torch.bfloat16).contiguous().view(-1), gx.view(-1))
+        return gx, None, None
 
 
 class _Combine(torch.autograd.Function):
     @staticmethod
-    def forward(ctx, expert_out, probs, disp):
-        cfg = disp.cfg
+    def forward(ctx, expert_out, probs, cfg, layout):
         y = torch.empty(cfg.num_tokens, cfg.hidden, dtype=torch.bfloat16, device=expert_out.device)
         eo = expert_out.contiguous()
         p = None if probs is None else probs.contiguous().float()
-        ep_combine(cfg, disp.layout, eo.view(-1), None if p is None else p.view(-1), y.view(-1))
-        ctx.disp = disp
+        ep_combine(cfg, layout, eo.view(-1), None if p is None else p.view(-1), y.view(-1))
+        ctx.cfg, ctx.layout = cfg, layout
         ctx.has_probs = probs is not None
         ctx.save_for_backward(eo, p if p is not None else torch.empty(0, device=eo.device))
         return y
 
     @staticmethod
     def backward(ctx, grad_y):
-        disp = ctx.disp
-        cfg = disp.cfg
+        cfg, layout = ctx.cfg, ctx.layout
         eo, p = ctx.saved_tensors
         gy = grad_y.to(torch.bfloat16).contiguous()
         g_out = torch.zeros(cfg.recv_rows, cfg.hidden, dtype=torch.bfloat16, device=gy.device)
-        ep_combine_bwd(cfg, disp.layout, gy.view(-1), p.view(-1) if ctx.has_probs else None, g_out.view(-1))
+        ep_combine_bwd(cfg, layout, gy.view(-1), p.view(-1) if ctx.has_probs else None, g_out.view(-1))
         g_probs = None
         if ctx.has_probs and ctx.needs_input_grad[1]:
             g_probs = torch.empty(cfg.num_tokens, cfg.top_k, dtype=torch.float32, device=gy.device)
-            ep_combine_bwd_probs(cfg, disp.layout, gy.view(-1), eo.view(-1), g_probs.view(-1))
-        return g_out, g_probs, None
+            ep_combine_bwd_probs(cfg, layout, gy.view(-1), eo.view(-1), g_probs.view(-1))
+        return g_out, g_probs, None, None
 
 
 class EpDispatcher:
@@ -85,19 +86,23 @@ class EpDispatcher:
         self.workspace = workspace_for(cfg, self.device)
 
     def route(self, topk_ids: torch.Tensor) -> Layout:
-        """Build the layout (counts, offsets, token_row, expert_ids, src_info, flags)."""
-        ep_dispatch_layout(self.cfg, topk_ids.to(torch.int32).contiguous().view(-1), self.workspace, self.layout)
-        return self.layout
+        """Build a new layout (counts, offsets, token_row, expert_ids, src_info,
+        flags) for these ids; later dispatch/combine calls use it.  Nodes
+        already recorded keep the layout they ran with."""
+        layout = Layout.empty(self.cfg, self.device)
+        ep_dispatch_layout(self.cfg, topk_ids.to(torch.int32).contiguous().view(-1), self.workspace, layout)
+        self.layout = layout
+        return layout
 
     def dispatch(self, x: torch.Tensor, topk_ids: Optional[torch.Tensor] = None) -> torch.Tensor:
         """[T, H] bf16 -> [R, H] bf16 receive rows; routes first when topk_ids is given."""
         if topk_ids is not None:
             self.route(topk_ids)
-        return _Dispatch.apply(x, self)
+        return _Dispatch.apply(x, self.cfg, self.layout)
 
     def combine(self, expert_out: torch.Tensor, probs: Optional[torch.Tensor]) -> torch.Tensor:
         """[R, H] bf16 expert outputs -> [T, H] bf16, weighted by probs [T, K] (or 1)."""
-        return _Combine.apply(expert_out, probs, self)
+        return _Combine.apply(expert_out, probs, self.cfg, self.layout)
 
     def tokens_per_expert(self) -> torch.Tensor:
         """Routed rows per group [S, G] (the shared group included)."""

@@ -365,3 +365,34 @@ def test_autograd_dispatcher_matches_fp64_reference(G):
     assert np.allclose(y.detach().float().cpu().numpy(), yr.detach().numpy(), rtol=2 ** -7, atol=1e-5)
     assert np.allclose(x.grad.float().cpu().numpy(), xr.grad.numpy(), rtol=2 ** -6, atol=1e-4)
     assert np.allclose(probs.grad.cpu().numpy(), pr.grad.numpy(), rtol=1e-3, atol=1e-3)
+
+
+def test_autograd_backward_keeps_the_layout_of_its_forward(G):
+    """Routing the next batch before this batch's backward must not change
+    this batch's gradients: every forward node keeps the layout it ran with.
+    The gradients with a second routing in between equal those without, bit
+    for bit."""
+    from combine_ep_dispatch_amd.autograd import EpDispatcher
+
+    c = G.random_case(43, T=200, S=2, E_loc=8, K=4, H=128, A=4, shared=0, mask_p=0.05)
+    other = G.random_case(44, T=200, S=2, E_loc=8, K=4, H=128, A=4, shared=0, mask_p=0.05)
+    T, H = c.cfg.num_tokens, c.cfg.hidden
+
+    def grads(reroute):
+        cfg = G.epx.EpConfig(num_tokens=T, hidden=H, num_experts=c.cfg.num_experts,
+                             num_segments=c.cfg.num_segments, top_k=c.cfg.top_k, align=c.cfg.align)
+        d = EpDispatcher(cfg, G.DEV)
+        x = G.u16_tensor(c.x).view(T, H).clone().requires_grad_(True)
+        probs = torch.from_numpy(c.probs).to(G.DEV).requires_grad_(True)
+        y = d.combine(d.dispatch(x, torch.from_numpy(c.ids).to(G.DEV)) * 2.0, probs)
+        if reroute:
+            d.route(torch.from_numpy(other.ids).to(G.DEV))
+        gy = G.u16_tensor(G.wl.make_tensor_like_rows(T, H, 5)).view(T, H)
+        (y.float() * gy.float()).sum().backward()
+        torch.cuda.synchronize()
+        return G.bits_of(x.grad), probs.grad.cpu().numpy().view(np.uint32)
+
+    gx0, gp0 = grads(False)
+    gx1, gp1 = grads(True)
+    assert np.array_equal(gx0, gx1)
+    assert np.array_equal(gp0, gp1)
