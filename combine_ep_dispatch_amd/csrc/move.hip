@@ -162,7 +162,8 @@ __device__ __forceinline__ void slot_row_and_weight_of_lane(const MoveArgs& a, i
 // waves of a pair are consecutive on one XCD.  With K' = 8 this is
 // workgroup b = pair b, one wave per slot.  Then t = rest / pieces and
 // p = rest - t * pieces; the divisions are multiplies by host-computed
-// reciprocals (exact for every 32-bit numerator); t0 is added to t for
+// reciprocals (exact below 2^31, where the 64-bit product cannot
+// overflow; the launcher keeps both numerators below 2^26); t0 is added to t for
 // launches split in token chunks [t0, t1).  Indices past the last
 // (token, piece) exit.
 struct ScatterGrid {
@@ -372,9 +373,10 @@ Grid move_grid(const MoveArgs& a, int vpl) {
     return g;
 }
 
-// q / d = (q * m) >> (32 + l) for every 32-bit q, with l = ceil(log2 d) and
+// q / d = (q * m) >> (32 + l) with l = ceil(log2 d) and
 // m = floor(2^(32+l) / d) + 1 (Granlund and Montgomery, division by
-// invariant integers).
+// invariant integers): exact for every q < 2^32, and m < 2^33, so the 64-bit
+// product q * m is exact for q < 2^31.
 void reciprocal(uint32_t d, uint64_t& m, uint32_t& shift) {
     uint32_t l = 0;
     while ((1ull << l) < d) ++l;

@@ -2,8 +2,9 @@
 in combine_ep_dispatch_amd/csrc/move.hip): the index arithmetic of the
 kernel and its launcher, written out in Python.
 
-Checked: the reciprocal multiplies equal integer division for every 32-bit
-numerator tried (boundaries of the range included); every (token, piece,
+Checked: the reciprocal multiplies, in 64-bit arithmetic as the kernel
+does them, equal integer division for every numerator tried below 2^31
+(the kernel's numerators stay below 2^26); every (token, piece,
 slot) of a batch is taken by exactly one wave; the K' waves of a (token,
 piece) run on one XCD (workgroup index mod 8); launches stay within 2^32 - 1
 work-items.  The GPU parity tests run the kernel itself on the same shapes
@@ -38,6 +39,14 @@ def launches(T, pieces, Kp):
     return out
 
 
+U64 = 2 ** 64 - 1
+
+
+def div64(q, m, s):
+    """(uint64)q * m >> s, as the kernel computes it."""
+    return ((q * m) & U64) >> s
+
+
 def waves(T, pieces, Kp):
     dm, ds = reciprocal(pieces)
     km, ks = reciprocal(Kp)
@@ -45,10 +54,12 @@ def waves(T, pieces, Kp):
         for b in range(n):
             for w in range(WAVES):
                 j = (b >> 3) * WAVES + w
-                pair = (j * km) >> ks
+                assert j < 2 ** 26
+                pair = div64(j, km, ks)
                 k = j - pair * Kp
                 rest = (pair << 3) | (b & 7)
-                tr = (rest * dm) >> ds
+                assert rest < 2 ** 26
+                tr = div64(rest, dm, ds)
                 p = rest - tr * pieces
                 t = t0 + tr
                 if t < t1:
@@ -75,11 +86,12 @@ def test_k8_is_one_workgroup_per_pair():
 @pytest.mark.parametrize("d", list(range(1, 70)) + [127, 128, 1000, 2 ** 20 + 3])
 def test_reciprocal_division_is_exact(d):
     m, s = reciprocal(d)
-    qs = [0, 1, d - 1, d, d + 1, 2 ** 31 - 1, 2 ** 31, 2 ** 32 - 2, 2 ** 32 - 1]
-    qs += [d * i - 1 for i in range(1, 50)] + [(2 ** 32 // d) * d + r for r in range(-2, 2)]
+    assert m < 2 ** 33  # so q * m < 2^64 for q < 2^31
+    qs = [0, 1, d - 1, d, d + 1, 2 ** 26, 2 ** 31 - 1]
+    qs += [d * i - 1 for i in range(1, 50)] + [(2 ** 31 // d) * d + r for r in range(-2, 2)]
     for q in qs:
-        if 0 <= q < 2 ** 32:
-            assert (q * m) >> s == q // d
+        if 0 <= q < 2 ** 31:
+            assert div64(q, m, s) == q // d
 
 
 @pytest.mark.parametrize("T,pieces,Kp", [(2 ** 24, 7, 8), (2 ** 22, 56, 9), (2 ** 26, 1, 64)])
