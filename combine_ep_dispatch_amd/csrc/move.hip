@@ -23,9 +23,10 @@
 //    by the other slots from L2, and no wave is idle whatever K' is (with
 //    K' = 9, slot blocks of 8 waves left 7 of every 16 idle, and the
 //    combine-backward scatter of a cold input took 133 instead of 107 us).
-//    8 waves per workgroup rather than 4 shortened the whole step by 2%
-//    (461 against 470 us at DeepSeek-V3 size), with the same isolated
-//    kernel times.  Short waves with streaming stores keep many more
+//    Workgroups of 8 waves: 4 shortened the DeepSeek-V3 step (409 against
+//    413 us) but slowed the weighted scatter of a cold input (116 against
+//    101 us), and with it the skewed workload's step (479 against 462 us).
+//    Short waves with streaming stores keep many more
 //    writes in flight than one wave storing all K' copies: at DeepSeek-V3
 //    size the dispatch scatter went from 106 to ~92 us and the
 //    combine-backward one from 102 to ~90.  The (token, piece, slot) of a
@@ -47,7 +48,7 @@
 #define EPX_SCATTER_VPL 2
 #endif
 #ifndef EPX_SCATTER_WAVES
-#define EPX_SCATTER_WAVES 8  // slots per scatter workgroup (one wave each)
+#define EPX_SCATTER_WAVES 8  // waves per scatter workgroup (one (token, piece, slot) each)
 #endif
 #ifndef EPX_GATHER_VPL
 #define EPX_GATHER_VPL 1
@@ -155,17 +156,16 @@ __device__ __forceinline__ void slot_row_and_weight_of_lane(const MoveArgs& a, i
 // Geometry of the scatter grid.  Workgroups are handed to the 8 XCDs
 // round-robin by index, and the K' slot waves of one (token, piece) should
 // share an XCD's L2 so that the piece is fetched once.  Workgroup b = 8q + x
-// runs on XCD x; that XCD's waves j = 8q + w (w = wave in the workgroup)
-// take the (token, piece, slot) triples of (token, piece) numbers
-// x, x + 8, x + 16, ... in order: local pair l = j / K', slot k = j - l K',
-// pair rest = 8 l + x.  Every wave has a slot, whatever K' is, and the K'
-// waves of a pair are consecutive on one XCD.  With K' = 8 this is
-// workgroup b = pair b, one wave per slot.  Then t = rest / pieces and
-// p = rest - t * pieces; the divisions are multiplies by host-computed
-// reciprocals (exact below 2^31, where the 64-bit product cannot
-// overflow; the launcher keeps both numerators below 2^26); t0 is added to t for
-// launches split in token chunks [t0, t1).  Indices past the last
-// (token, piece) exit.
+// runs on XCD x; with W = EPX_SCATTER_WAVES waves per workgroup, that XCD's
+// waves j = W q + w (w = wave in the workgroup) take the (token, piece,
+// slot) triples of (token, piece) numbers x, x + 8, x + 16, ... in order:
+// local pair l = j / K', slot k = j - l K', pair rest = 8 l + x.  Every
+// wave has a slot, whatever K' is, and the K' waves of a pair are
+// consecutive on one XCD (with K' = W = 8, one workgroup per pair).  Then t = rest / pieces and p = rest - t * pieces.
+// The divisions are multiplies by host-computed reciprocals, exact below
+// 2^31 where the 64-bit product cannot overflow; the launcher keeps both
+// numerators below 2^26.  t0 is added to t for launches split in token
+// chunks [t0, t1).  Indices past the last (token, piece) exit.
 struct ScatterGrid {
     int32_t Hv, pieces, t0, t1;  // this launch covers tokens [t0, t1)
     uint64_t div_mul, kp_mul;
