@@ -14,6 +14,8 @@ cases (no tokens, everything masked, the largest group count, tile
 boundaries, K = 1, one expert per segment, tiny capacities).
 """
 
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -54,7 +56,12 @@ def test_named_workload_full_size(G, name):
         assert f == 0
 
 
-@pytest.mark.parametrize("seed", range(128))
+# Wider sweeps: EPX_GPU_SEEDS=2424 EPX_GPU_LARGE_SEEDS=110 (about 10 minutes).
+SEEDS = int(os.environ.get("EPX_GPU_SEEDS", "128"))
+LARGE_SEEDS = int(os.environ.get("EPX_GPU_LARGE_SEEDS", "4"))
+
+
+@pytest.mark.parametrize("seed", range(SEEDS))
 def test_random_shapes(G, seed):
     rng = np.random.default_rng(seed)
     kw = {}
@@ -69,6 +76,38 @@ def test_random_shapes(G, seed):
         c.cfg.recv_rows = G.epx.ep_query(c.cfg).min_recv_rows
         c = G.Case(c.cfg, c.ids, c.probs, c.x, c.seed)
     name = f"random{seed}"
+    lay = G.check_layout(c, name)
+    G.check_dispatch(c, lay, name)
+    if c.cfg.hidden % 16 == 0:
+        G.check_nvfp4(c, lay, name)
+    if c.cfg.hidden % 128 == 0:
+        G.check_fp8(c, lay, name)
+    G.check_combine(c, lay, name, weighted=seed % 2 == 0)
+    G.check_dispatch_bwd(c, lay, name)
+    G.check_combine_bwd(c, lay, name, weighted=seed % 3 != 0)
+    G.check_probs_grad(c, lay, name)
+
+
+@pytest.mark.parametrize("seed", range(LARGE_SEEDS))
+def test_large_random_shapes(G, seed):
+    """Multi-tile layouts (direct and look-back paths), bench-like hidden
+    sizes, capacity drops and the shared expert at T = 1000..20000."""
+    rng = np.random.default_rng(10_000 + seed)
+    S = int(rng.choice([1, 2, 4, 8]))
+    E_loc = int(rng.choice([1, 4, 16, 32, 64]))
+    K = int(rng.integers(1, min(S * E_loc, 8) + 1))
+    kw = dict(T=int(rng.integers(1000, 20001)), H=int(rng.choice([512, 2048, 4096, 7168])), S=S, E_loc=E_loc, K=K,
+              A=int(rng.choice([1, 16, 128])), shared=int(rng.integers(0, 2)), src=int(rng.integers(0, S)),
+              mask_p=float(rng.choice([0.0, 0.01])), bad_p=float(rng.choice([0.0, 0.001])))
+    if kw["T"] * kw["H"] > 60_000_000:
+        kw["H"] = 2048
+    c = G.random_case(20_000 + seed, **kw)
+    if seed % 3 == 1:
+        load = max(1, c.cfg.num_tokens * c.cfg.kp // c.cfg.num_segments)
+        c.cfg.seg_capacity = int(rng.integers(load // 2, load + 2))
+        c.cfg.recv_rows = G.epx.ep_query(c.cfg).min_recv_rows
+        c = G.Case(c.cfg, c.ids, c.probs, c.x, c.seed)
+    name = f"large{seed}"
     lay = G.check_layout(c, name)
     G.check_dispatch(c, lay, name)
     if c.cfg.hidden % 16 == 0:
