@@ -7,11 +7,26 @@
 // An all-zero block gives zero codes and scale 0.  Each token is quantized
 // once and its bytes written to every kept (token, slot) row.
 //
-// One wave64 per token (four for batches under kSmallBatchTokens, taking
-// alternate iterations).  Lanes form 8 groups of 8; group j owns block
-// 8*it + j of iteration it and each lane 16 of its elements, so one wave
-// load covers 2 KiB of the row and one wave store 1 KiB of codes, both
-// contiguous.  The block amax is three xor-shuffles inside the 8-lane group.
+// One workgroup of 8 waves per token: the waves quantize the row into LDS
+// once (wave w takes iterations w, w + 8, ...), then wave w stores the
+// codes and scales to the rows of slots w, w + 8, ...  Short store runs per
+// wave rather than one wave storing all K' copies: at DeepSeek-V3 size the
+// kernel went from 51.0 to 48.0 us, and from 5.8 to 4.8 us at T = 128.
+// Outputs larger than half the MALL take nontemporal code stores (skewed
+// workload: 65.6 against 51.8 us; at DeepSeek-V3 size within 1%).  Rows
+// of fewer than 4 iterations (H < 3584) keep one wave per token.  After a
+// cache flush (cold input) the kernel is slower than the one-wave form at
+// DeepSeek-V3 size (61 against 48 us), whose plain stores then land in an
+// empty MALL; with the caches in the state that back-to-back launches leave,
+// and at small batches, it is the faster (T = 128 cold: 7.7 against
+// 9.3 us).  4 and 2 waves per token were slower than 8 warm and no better
+// cold.  Batches
+// past that kernel's grid (2^23 tokens) take one wave per token (four under
+// kSmallBatchTokens, taking alternate iterations).  In an iteration, lanes
+// form 8 groups of 8; group j owns block 8*it + j and each lane 16 of its
+// elements, so one wave load covers 2 KiB of the row and one wave store
+// 1 KiB of codes, both contiguous.  The block amax is three xor-shuffles
+// inside the 8-lane group.
 // IEEE division and no contraction keep the result bit-identical to the
 // plain definition.  The encode is gfx950's v_cvt_pk_fp8_f32 (OCP E4M3,
 // RNE), two elements per instruction: for |v| <= 464 it equals the RNE,
@@ -59,6 +74,42 @@ __device__ __forceinline__ uint32_t codes4_hw(uint32_t w0, uint32_t w1, float in
     return (uint32_t)r;
 }
 
+// Iteration `it` of a row: 8 blocks of 128 elements, block it*8 + lane/8
+// in lanes 8j..8j+7, 16 elements per lane (one 2 KiB wave load).  Gives this
+// lane's 16 codes and its block's scale (the same in all 8 lanes).
+__device__ __forceinline__ void quantize_iteration(const uint4* xr, int32_t it, int lane, int32_t nblk, uint4& code,
+                                                   float& scale) {
+    const int32_t b = it * 8 + lane / 8;  // this lane's block
+    uint4 p = make_uint4(0, 0, 0, 0), q = make_uint4(0, 0, 0, 0);
+    if (b < nblk) {
+        p = xr[128 * it + 2 * lane];
+        q = xr[128 * it + 2 * lane + 1];
+    }
+    uint32_t m = absmax16(p, q);
+    m = max(m, (uint32_t)__shfl_xor((int)m, 4, kWave));
+    m = max(m, (uint32_t)__shfl_xor((int)m, 2, kWave));
+    m = max(m, (uint32_t)__shfl_xor((int)m, 1, kWave));
+    const float amax = __uint_as_float(m << 16);
+    if (amax == 0.0f) {
+        code = make_uint4(0, 0, 0, 0);
+        scale = 0.0f;
+        return;
+    }
+    const float inv = 448.0f / amax;
+    if (inv > 0.0f && inv <= __FLT_MAX__) {  // 0 when amax is inf
+        code.x = codes4_hw(p.x, p.y, inv);
+        code.y = codes4_hw(p.z, p.w, inv);
+        code.z = codes4_hw(q.x, q.y, inv);
+        code.w = codes4_hw(q.z, q.w, inv);
+    } else {
+        code.x = codes4(p.x, p.y, inv);
+        code.y = codes4(p.z, p.w, inv);
+        code.z = codes4(q.x, q.y, inv);
+        code.w = codes4(q.z, q.w, inv);
+    }
+    scale = amax / 448.0f;
+}
+
 // W waves per token (1, or 4 for small batches): wave `part` takes the
 // iterations part, part + W, ...  A 128-element block lives in 8 lanes of
 // one wave, so the waves of a token never exchange anything.
@@ -75,38 +126,7 @@ __global__ __launch_bounds__(kFp8Threads) void k_fp8(Fp8Args a) {
     uint4 code[NIT];
     float scale[NIT];
 #pragma unroll
-    for (int j = 0; j < NIT; ++j) {
-        const int32_t it = part + j * W;        // this wave's iteration
-        const int32_t b = it * 8 + lane / 8;  // this lane's block
-        uint4 p = make_uint4(0, 0, 0, 0), q = make_uint4(0, 0, 0, 0);
-        if (b < nblk) {
-            p = xr[128 * it + 2 * lane];
-            q = xr[128 * it + 2 * lane + 1];
-        }
-        uint32_t m = absmax16(p, q);
-        m = max(m, (uint32_t)__shfl_xor((int)m, 4, kWave));
-        m = max(m, (uint32_t)__shfl_xor((int)m, 2, kWave));
-        m = max(m, (uint32_t)__shfl_xor((int)m, 1, kWave));
-        const float amax = __uint_as_float(m << 16);
-        if (amax == 0.0f) {
-            code[j] = make_uint4(0, 0, 0, 0);
-            scale[j] = 0.0f;
-        } else {
-            const float inv = 448.0f / amax;
-            if (inv > 0.0f && inv <= __FLT_MAX__) {  // 0 when amax is inf
-                code[j].x = codes4_hw(p.x, p.y, inv);
-                code[j].y = codes4_hw(p.z, p.w, inv);
-                code[j].z = codes4_hw(q.x, q.y, inv);
-                code[j].w = codes4_hw(q.z, q.w, inv);
-            } else {
-                code[j].x = codes4(p.x, p.y, inv);
-                code[j].y = codes4(p.z, p.w, inv);
-                code[j].z = codes4(q.x, q.y, inv);
-                code[j].w = codes4(q.z, q.w, inv);
-            }
-            scale[j] = amax / 448.0f;
-        }
-    }
+    for (int j = 0; j < NIT; ++j) quantize_iteration(xr, part + j * W, lane, nblk, code[j], scale[j]);
 
     const int32_t* tr = a.token_row + (int64_t)t * a.Kp;
     for (int32_t k = 0; k < a.Kp; ++k) {
@@ -126,6 +146,57 @@ __global__ __launch_bounds__(kFp8Threads) void k_fp8(Fp8Args a) {
     }
 }
 
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+#ifndef EPX_FP8_WPT
+#define EPX_FP8_WPT 8  // waves per token (one workgroup per token)
+#endif
+// Outputs larger than this (half the 256 MB MALL) take nontemporal code
+// stores: written straight through, they no longer evict the inputs and
+// other outputs from the MALL.  Smaller ones stay in it for their consumer.
+constexpr int64_t kFp8StreamBytes = int64_t(128) << 20;
+
+// One workgroup of WPT waves per token: the waves quantize the row's
+// iterations into LDS once, then wave w stores the codes and scales of the
+// token's slots w, w + WPT, ... (one short run of stores per slot row).
+// LDS (dynamic): nit * 1 KiB of codes, then nit * 8 scales.
+template <int WPT, bool NT>
+__global__ __launch_bounds__(WPT * kWave) void k_fp8_wg(Fp8Args a) {
+    extern __shared__ uint4 s_dyn[];
+    const int32_t t = blockIdx.x;
+    const int wv = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
+    const int32_t nblk = a.H / 128, nit = (nblk + 7) / 8;
+    uint4* s_code = s_dyn;
+    float* s_scale = reinterpret_cast<float*>(s_dyn + nit * kWave);
+    const int32_t* tr = a.token_row + (int64_t)t * a.Kp;
+    const int32_t row0 = wv < a.Kp ? tr[wv] : -1;  // fetched before the barrier
+    const uint4* xr = reinterpret_cast<const uint4*>(a.x + (int64_t)t * a.H);
+    for (int32_t it = wv; it < nit; it += WPT) {
+        uint4 code;
+        float scale;
+        quantize_iteration(xr, it, lane, nblk, code, scale);
+        s_code[it * kWave + lane] = code;
+        if ((lane & 7) == 0) s_scale[it * 8 + lane / 8] = scale;
+    }
+    __syncthreads();
+    for (int32_t k = wv; k < a.Kp; k += WPT) {
+        const int32_t row = uniform(k == wv ? row0 : tr[k]);
+        if (row < 0 || row >= a.R) continue;
+        uint4* crow = reinterpret_cast<uint4*>(a.codes + (int64_t)row * a.H);
+        float* srow = a.scales + (int64_t)row * nblk;
+        for (int32_t it = 0; it < nit; ++it) {
+            const int32_t b = it * 8 + lane / 8;
+            if (b < nblk) {
+                const uint4 c = s_code[it * kWave + lane];
+                if (NT)
+                    __builtin_nontemporal_store(v4u{c.x, c.y, c.z, c.w}, reinterpret_cast<v4u*>(crow + 64 * it + lane));
+                else
+                    crow[64 * it + lane] = c;
+            }
+        }
+        for (int32_t b = lane; b < nblk; b += kWave) srow[b] = s_scale[b];
+    }
+}
+
 template <int NIT, int W>
 hipError_t launch_nit(const Fp8Args& a, hipStream_t stream) {
     constexpr int kTokensPerBlock = kFp8Waves / W;
@@ -140,7 +211,23 @@ int fp8_max_hidden() { return 1024 * kFp8MaxIters; }
 
 hipError_t launch_fp8(const Fp8Args& a, hipStream_t stream) {
     if (a.T == 0) return hipSuccess;
-    const int nit = (a.H + 1023) / 1024;
+    constexpr int WPT = EPX_FP8_WPT;
+    const int32_t nit = (a.H / 128 + 7) / 8;
+    // One workgroup per token where a row has at least 4 iterations of 8
+    // blocks (H >= 3584).  With 2 (H = 2048, capacity workload) 6 of its 8
+    // waves idle while the row is quantized, and the kernel took 32.9 against
+    // 26.6 us with one wave per token.
+    if (nit >= 4 && (int64_t)a.T * WPT * kWave <= 0xFFFFFFFFll) {
+        const size_t lds = (size_t)nit * kWave * sizeof(uint4) + (size_t)nit * 8 * sizeof(float);
+        const int64_t out_bytes = (int64_t)a.T * a.Kp * (a.H + a.H / 128 * 4);
+        if (out_bytes > kFp8StreamBytes)
+            hipLaunchKernelGGL((k_fp8_wg<WPT, true>), dim3((unsigned)a.T), dim3(WPT * kWave), lds, stream, a);
+        else
+            hipLaunchKernelGGL((k_fp8_wg<WPT, false>), dim3((unsigned)a.T), dim3(WPT * kWave), lds, stream, a);
+        return hipGetLastError();
+    }
+    // Narrow rows, and batches past that grid (2^23 tokens): one wave per
+    // token (nit = (H + 1023) / 1024 as well: 1024 elements per iteration).
     if (a.T < kSmallBatchTokens) {  // 4 waves per token
         switch ((nit + 3) / 4) {
             case 1: return launch_nit<1, 4>(a, stream);
