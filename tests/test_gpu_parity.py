@@ -154,6 +154,9 @@ EDGE = {
     "slots_64": dict(T=300, S=1, E_loc=64, K=63, shared=1, src=0, H=64, A=4),  # K' = 64: 16 scatter slot blocks
     "hidden_8": dict(T=500, S=2, E_loc=4, K=3, H=8),                          # one ragged piece per row
     "hidden_16k": dict(T=300, S=2, E_loc=4, K=4, H=16384, A=8),               # 8 full pieces, 16 NVFP4 blocks per lane
+    # quantizing dispatch, one workgroup per token: K' = 9 (a wave stores two slot rows), masks, bad ids
+    "quant_wg_k9": dict(T=700, S=4, E_loc=8, K=8, shared=1, src=1, H=7168, A=4, mask_p=0.1, bad_p=0.01),
+    "quant_wg_capacity": dict(T=900, S=2, E_loc=16, K=6, H=4096, A=2, C=1500),       # capacity drops
 }
 
 
@@ -188,11 +191,15 @@ def test_tiny_capacities(G, C):
     G.check_probs_grad(c, lay, f"cap{C}")
 
 
-def test_nvfp4_special_rows(G):
+@pytest.mark.parametrize("H", [1040, 4096, 16384])
+def test_nvfp4_special_rows(G, H):
     """Zero tokens, negative zeros, subnormal bf16 values, huge outliers,
-    tiny blocks next to a large one (E4M3-subnormal and zero block scales)."""
+    tiny blocks next to a large one (E4M3-subnormal and zero block scales).
+    H = 1040: 65 blocks, the second block column of a lane is ragged (four
+    waves per token); 4096 and 16384: one workgroup per token, with one and
+    two blocks per lane."""
     rng = np.random.default_rng(3)
-    T, H = 64, 1040  # H/16 = 65 blocks: the second block column of a lane is ragged
+    T = 64
     x = rng.standard_normal((T, H)).astype(np.float32)
     x[0] = 0
     x[1] = -0.0
