@@ -28,10 +28,11 @@ import torch
 
 from . import _lib
 from ._lib import (EP_FLAG_BAD_ID, EP_FLAG_DROPPED, EP_FLAG_INTERNAL, EP_FLAG_MAP_OVERFLOW,  # noqa: F401
-                   EP_ZERO_PAD_ROWS, EP_LAYOUT_LOOKBACK, EpCfg, EpLayout)
+                   EP_NOALLOC_SCRATCH_BYTES, EP_ZERO_PAD_ROWS, EP_LAYOUT_LOOKBACK, EpCfg, EpLayout)
 
 __all__ = [
     "EpConfig", "Layout", "QueryResult", "ep_query", "workspace_for", "ep_dispatch_layout",
+    "ep_dispatch_layout_noalloc", "EP_NOALLOC_SCRATCH_BYTES",
     "ep_dispatch", "ep_dispatch_nvfp4", "ep_dispatch_fp8", "ep_combine", "ep_dispatch_bwd", "ep_combine_bwd",
     "ep_combine_bwd_probs", "ep_indices_to_multihot", "ep_multihot_to_indices", "assert_no_overflow", "EpError", "abi_version", "EP_ZERO_PAD_ROWS", "EP_LAYOUT_LOOKBACK", "EP_FLAG_DROPPED",
     "EP_FLAG_BAD_ID", "EP_FLAG_INTERNAL",
@@ -170,6 +171,17 @@ def ep_dispatch_layout(cfg: EpConfig, topk_ids: torch.Tensor, workspace: torch.T
     _check(_lib.lib().ep_dispatch_layout(ctypes.byref(c), topk_ids.data_ptr(), workspace.data_ptr(),
                                          workspace.numel(), ctypes.byref(L), _stream(stream, dev)),
            "ep_dispatch_layout")
+
+
+def ep_dispatch_layout_noalloc(cfg: EpConfig, topk_ids: torch.Tensor, layout: Layout, stream=None) -> None:
+    """ep_dispatch_layout with the library's built-in scratch instead of a
+    workspace: allocates nothing.  Calls that may overlap on one GPU race."""
+    dev = topk_ids.device
+    _tensor(topk_ids, "topk_ids", torch.int32, cfg.num_tokens * cfg.top_k)
+    layout.check(cfg, dev)
+    c, L = cfg.to_c(), layout.to_c()
+    _check(_lib.lib().ep_dispatch_layout_noalloc(ctypes.byref(c), topk_ids.data_ptr(), ctypes.byref(L),
+                                                 _stream(stream, dev)), "ep_dispatch_layout_noalloc")
 
 
 def ep_dispatch(cfg: EpConfig, layout: Layout, x: torch.Tensor, recv: torch.Tensor, stream=None) -> None:

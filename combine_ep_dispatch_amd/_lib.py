@@ -15,6 +15,8 @@ EP_OK = 0
 EP_EINVAL = -1
 EP_ELAUNCH = -2
 EP_ENOTSUP = -3
+EP_ESCRATCH = -4
+EP_NOALLOC_SCRATCH_BYTES = 4 << 20
 EP_ZERO_PAD_ROWS = 1
 EP_LAYOUT_LOOKBACK = 2
 EP_FLAG_DROPPED = 1
@@ -26,7 +28,8 @@ EP_MAX_GROUPS = 2048
 # Every symbol include/epx.h declares.
 SYMBOLS = ("ep_query", "ep_dispatch_layout", "ep_dispatch", "ep_dispatch_nvfp4", "ep_dispatch_fp8",
            "ep_combine", "ep_dispatch_bwd", "ep_combine_bwd", "ep_combine_bwd_probs",
-           "ep_indices_to_multihot", "ep_multihot_to_indices", "ep_strerror", "ep_abi_version")
+           "ep_indices_to_multihot", "ep_multihot_to_indices", "ep_dispatch_layout_noalloc",
+           "ep_strerror", "ep_abi_version")
 
 
 class EpCfg(ctypes.Structure):
@@ -73,7 +76,8 @@ def lib():
         L.ep_dispatch_fp8.argtypes = [cfg_p, lay_p, P, P, P, P]
         L.ep_indices_to_multihot.argtypes = [cfg_p, P, P, P, P, P]
         L.ep_multihot_to_indices.argtypes = [cfg_p, P, P, P, P, P, P]
-        for name in SYMBOLS[:11]:
+        L.ep_dispatch_layout_noalloc.argtypes = [cfg_p, P, lay_p, P]
+        for name in SYMBOLS[:12]:
             getattr(L, name).restype = I
         L.ep_strerror.argtypes = [I]
         L.ep_strerror.restype = ctypes.c_char_p

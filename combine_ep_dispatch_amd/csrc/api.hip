@@ -9,6 +9,13 @@
 
 #include "epx_device.h"
 
+// Built-in workspace of ep_dispatch_layout_noalloc, for callers that cannot
+// allocate: zero when the code object loads, and each GPU the library runs
+// on holds its own copy for the life of the process.  On the host the name
+// is only a stand-in for the device array; host code uses the address
+// scratch_address() looks up, never the name.
+static __device__ __align__(256) uint8_t scratch[EP_NOALLOC_SCRATCH_BYTES];
+
 namespace {
 
 using namespace epx;
@@ -132,53 +139,28 @@ int zero_pad(const Shape& d, const ep_layout_t* L, void* base, int64_t row_bytes
     return status_of(launch_zero_pad_rows(base, row_bytes, *L, d.S, d.G, d.A, d.C, d.R, st));
 }
 
-}  // namespace
-
-extern "C" {
-
-int ep_abi_version(void) { return EPX_ABI_VERSION; }
-
-const char* ep_strerror(int status) {
-    switch (status) {
-        case EP_OK: return "ok";
-        case EP_EINVAL: return "invalid argument";
-        case EP_ELAUNCH: return "HIP runtime error while enqueueing work";
-        case EP_ENOTSUP: return "device is not gfx950 (MI355X)";
-        default: return "unknown status";
-    }
-}
-
-int ep_query(const ep_cfg_t* cfg, int64_t* min_recv_rows, int64_t* workspace_bytes, int32_t* groups_per_seg) {
-    Shape d;
-    const int rc = derive(cfg, &d);
-    if (rc != EP_OK) return rc;
-    if (min_recv_rows) *min_recv_rows = d.min_rows;
-    if (workspace_bytes) *workspace_bytes = d.ws_bytes;
-    if (groups_per_seg) *groups_per_seg = d.G;
-    return EP_OK;
-}
-
-int ep_dispatch_layout(const ep_cfg_t* cfg, const int32_t* topk_ids, void* workspace, int64_t workspace_bytes,
-                       const ep_layout_t* layout, void* stream) {
-    Shape d;
-    int rc = derive(cfg, &d);
-    if (rc != EP_OK) return rc;
+// Host-side checks shared by both layout entry points (everything but the
+// workspace).
+int layout_check(const Shape& d, const int32_t* topk_ids, const ep_layout_t* L) {
+    int rc;
     if ((rc = check_rows(d)) != EP_OK) return rc;
-    if (layout == nullptr) return EP_EINVAL;
+    if (L == nullptr) return EP_EINVAL;
     if (bad_buffer(topk_ids, (int64_t)d.T * d.K * 4, 4)) return EP_EINVAL;
-    if (workspace == nullptr || misaligned(workspace, 16) || workspace_bytes < d.ws_bytes) return EP_EINVAL;
-    const ep_layout_t* L = layout;
     if (bad_buffer(L->counts, (int64_t)d.NG * 4, 4) || bad_buffer(L->seg_base, (int64_t)(d.S + 1) * 4, 4) ||
         bad_buffer(L->row_offsets, (int64_t)d.S * (d.G + 1) * 4, 4) ||
         bad_buffer(L->scales_offsets, (int64_t)d.S * (d.G + 1) * 4, 4) ||
         bad_buffer(L->token_row, (int64_t)d.T * d.Kp * 4, 4) || bad_buffer(L->expert_ids, d.R * 4, 4) ||
         bad_buffer(L->src_info, d.R * 8, 4) || bad_buffer(L->flags, 4, 4))
         return EP_EINVAL;
-    if ((rc = check_device()) != EP_OK) return rc;
+    return EP_OK;
+}
 
+// Launch of the layout kernels, after layout_check and check_device; `ws`
+// holds at least d.ws_bytes bytes.
+int layout_launch(const Shape& d, const int32_t* topk_ids, void* ws, const ep_layout_t* L, void* stream) {
     LayoutArgs a;
     a.topk_ids = topk_ids;
-    a.desc = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(workspace) + kWorkspaceHeader);
+    a.desc = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(ws) + kWorkspaceHeader);
     a.out = *L;
     a.T = d.T;
     a.K = d.K;
@@ -204,6 +186,79 @@ int ep_dispatch_layout(const ep_cfg_t* cfg, const int32_t* topk_ids, void* works
     a.slots_per_thread = a.mode == kLayoutSmall ? (routed <= 256 ? 1 : (routed <= 512 ? 2 : 4))
                                                 : layout_slots_per_thread(routed, d.NG);
     return status_of(launch_layout(a, static_cast<hipStream_t>(stream)));
+}
+
+constexpr int64_t kScratchBytes = EP_NOALLOC_SCRATCH_BYTES;
+
+// Device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept.
+int scratch_address(void** out) {
+    static std::mutex mu;
+    static void* addr[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return EP_ELAUNCH;
+    if (dev < 0 || dev >= 64) return EP_ENOTSUP;
+    std::lock_guard<std::mutex> lock(mu);
+    if (addr[dev] == nullptr) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return EP_ELAUNCH;
+        addr[dev] = p;
+    }
+    *out = addr[dev];
+    return EP_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ep_abi_version(void) { return EPX_ABI_VERSION; }
+
+const char* ep_strerror(int status) {
+    switch (status) {
+        case EP_OK: return "ok";
+        case EP_EINVAL: return "invalid argument";
+        case EP_ELAUNCH: return "HIP runtime error while enqueueing work";
+        case EP_ENOTSUP: return "device is not gfx950 (MI355X)";
+        case EP_ESCRATCH:
+            return "the layout needs more scratch than the built-in buffer of ep_dispatch_layout_noalloc "
+                   "holds (EP_NOALLOC_SCRATCH_BYTES); use ep_dispatch_layout with a workspace";
+        default: return "unknown status";
+    }
+}
+
+int ep_query(const ep_cfg_t* cfg, int64_t* min_recv_rows, int64_t* workspace_bytes, int32_t* groups_per_seg) {
+    Shape d;
+    const int rc = derive(cfg, &d);
+    if (rc != EP_OK) return rc;
+    if (min_recv_rows) *min_recv_rows = d.min_rows;
+    if (workspace_bytes) *workspace_bytes = d.ws_bytes;
+    if (groups_per_seg) *groups_per_seg = d.G;
+    return EP_OK;
+}
+
+int ep_dispatch_layout(const ep_cfg_t* cfg, const int32_t* topk_ids, void* workspace, int64_t workspace_bytes,
+                       const ep_layout_t* layout, void* stream) {
+    Shape d;
+    int rc = derive(cfg, &d);
+    if (rc != EP_OK) return rc;
+    if ((rc = layout_check(d, topk_ids, layout)) != EP_OK) return rc;
+    if (workspace == nullptr || misaligned(workspace, 16) || workspace_bytes < d.ws_bytes) return EP_EINVAL;
+    if ((rc = check_device()) != EP_OK) return rc;
+    return layout_launch(d, topk_ids, workspace, layout, stream);
+}
+
+int ep_dispatch_layout_noalloc(const ep_cfg_t* cfg, const int32_t* topk_ids, const ep_layout_t* layout,
+                               void* stream) {
+    Shape d;
+    int rc = derive(cfg, &d);
+    if (rc != EP_OK) return rc;
+    if ((rc = layout_check(d, topk_ids, layout)) != EP_OK) return rc;
+    if (d.ws_bytes > kScratchBytes) return EP_ESCRATCH;
+    if ((rc = check_device()) != EP_OK) return rc;
+    void* ws = nullptr;
+    if ((rc = scratch_address(&ws)) != EP_OK) return rc;
+    return layout_launch(d, topk_ids, ws, layout, stream);
 }
 
 int ep_dispatch(const ep_cfg_t* cfg, const ep_layout_t* layout, const uint16_t* x, uint16_t* recv, void* stream) {

@@ -56,6 +56,8 @@ extern "C" {
 #define EP_EINVAL (-1)   /* an argument fails a host-side check                */
 #define EP_ELAUNCH (-2)  /* the HIP runtime reported an error enqueueing work  */
 #define EP_ENOTSUP (-3)  /* the current device is not gfx950                   */
+#define EP_ESCRATCH (-4) /* ep_dispatch_layout_noalloc: the layout needs more
+                            scratch than EP_NOALLOC_SCRATCH_BYTES             */
 /* A HIP grid dimension holds at most 2^32 - 1 work-items.  ep_dispatch,
  * ep_combine, ep_dispatch_bwd and ep_combine_bwd split larger batches into
  * several launches.  The calls that launch one grid per batch return
@@ -304,6 +306,23 @@ int ep_indices_to_multihot(const ep_cfg_t* cfg, const int32_t* topk_ids, const f
  */
 int ep_multihot_to_indices(const ep_cfg_t* cfg, const uint8_t* routing_map, const float* dense_probs,
                            int32_t* topk_ids, float* probs, int32_t* flags, void* stream);
+
+/*
+ * ep_dispatch_layout without a caller workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Same arguments, results and errors as
+ * ep_dispatch_layout, except that the workspace is a buffer built into the
+ * library: EP_NOALLOC_SCRATCH_BYTES bytes per GPU, held from the first call
+ * on that GPU until the process ends.  Returns EP_ESCRATCH, before anything
+ * is enqueued, when ep_query's workspace_bytes for cfg exceeds it.  Every
+ * call on one GPU shares that buffer: two calls that may run at the same
+ * time on one GPU (different streams, no ordering between them) race and
+ * give undefined layouts; calls on one stream are ordered and safe.  Never
+ * allocates, frees or synchronizes.
+ */
+#define EP_NOALLOC_SCRATCH_BYTES (4 << 20)
+int ep_dispatch_layout_noalloc(const ep_cfg_t* cfg, const int32_t* topk_ids, const ep_layout_t* layout,
+                               void* stream);
 
 /* Static description of a status code. */
 const char* ep_strerror(int status);

@@ -71,6 +71,36 @@ def test_exports_every_declared_symbol(L):
     assert L.ep_abi_version() == 1
     assert L.ep_strerror(-1) == b"invalid argument"
     assert L.ep_strerror(0) == b"ok"
+    assert b"ep_dispatch_layout_noalloc" in L.ep_strerror(-4)
+
+
+def test_noalloc_layout_rejects_oversized_problems_before_any_launch(L):
+    """The built-in scratch of ep_dispatch_layout_noalloc holds
+    EP_NOALLOC_SCRATCH_BYTES; a configuration whose workspace_bytes exceeds
+    it gets EP_ESCRATCH (-4) before anything is enqueued, and argument errors
+    keep EP_EINVAL."""
+    from combine_ep_dispatch_amd._lib import EP_NOALLOC_SCRATCH_BYTES, EpLayout
+
+    fake = 0x10000  # never dereferenced: every call below fails validation first
+    lay = EpLayout(*([fake] * 8))
+    big = cfg(num_tokens=1 << 21, num_experts=2048, num_segments=8, top_k=8, align=1)
+    st, rows, ws, _ = query(L, big)
+    assert st == 0 and ws > EP_NOALLOC_SCRATCH_BYTES
+    big.recv_rows = rows
+    cc = big.to_c()
+    assert L.ep_dispatch_layout_noalloc(ctypes.byref(cc), fake, ctypes.byref(lay), None) == -4
+    bad = cfg(num_tokens=-1).to_c()
+    assert L.ep_dispatch_layout_noalloc(ctypes.byref(bad), fake, ctypes.byref(lay), None) == -1
+    small = cfg()
+    st, rows, ws, _ = query(L, small)
+    assert ws <= EP_NOALLOC_SCRATCH_BYTES
+    small.recv_rows = rows - 1
+    cs = small.to_c()
+    assert L.ep_dispatch_layout_noalloc(ctypes.byref(cs), fake, ctypes.byref(lay), None) == -1
+    small.recv_rows = rows
+    cs = small.to_c()
+    assert L.ep_dispatch_layout_noalloc(ctypes.byref(cs), None, ctypes.byref(lay), None) == -1
+    assert L.ep_dispatch_layout_noalloc(ctypes.byref(cs), fake, None, None) == -1
 
 
 def test_header_and_binding_structs_agree():
