@@ -49,6 +49,10 @@ KERNEL_SOURCES = ("combine_ep_dispatch_amd/csrc/move.hip", "combine_ep_dispatch_
                   "combine_ep_dispatch_amd/csrc/epx_device.h")
 
 
+# Each layout path forced (timed beside the default choice; results must agree).
+LAYOUT_PATHS = {"layout_lookback": 2, "layout_barrier": 8, "layout_two_kernel": 4}
+
+
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
@@ -99,9 +103,11 @@ def algorithmic_bytes(w, kept: int, used_rows: int, kept_routed: int = None) -> 
         "combine": row * kept + row * T + 4 * T * K + 4 * T * Kp,
         "combine_bwd": row * T + row * kept + 4 * T * K + 4 * T * Kp,
         "dispatch_bwd": row * kept + row * T + 4 * T * Kp,
-        # not part of the step: the layout on its decoupled look-back path, the
-        # router-probability gradient and FP8 dispatch
+        # not part of the step: each layout path forced, the router-probability
+        # gradient and FP8 dispatch
         "layout_lookback": 4 * T * K + 4 * T * Kp + 12 * used_rows,
+        "layout_barrier": 4 * T * K + 4 * T * Kp + 12 * used_rows,
+        "layout_two_kernel": 4 * T * K + 4 * T * Kp + 12 * used_rows,
         "combine_bwd_probs": row * T + row * kept_routed + 4 * T * Kp + 4 * T * K,
         "dispatch_fp8": row * T + kept * (H + 4 * (H // 128)) + 4 * T * Kp,
     }
@@ -217,10 +223,12 @@ def main() -> int:
     gprobs = torch.empty(T * w.K, dtype=torch.float32, device=dev)
     fp8_codes = torch.empty(R * H, dtype=torch.uint8, device=dev)
     fp8_scales = torch.empty(R * (H // 128), dtype=torch.float32, device=dev)
-    cfg_lb = dataclasses.replace(cfg, flags=cfg.flags | epx.EP_LAYOUT_LOOKBACK)
-    lay_lb = epx.Layout.empty(cfg_lb, dev)
-    ws_lb = epx.workspace_for(cfg_lb, dev)
-    extra_ops = [("layout_lookback", lambda: epx.ep_dispatch_layout(cfg_lb, ids, ws_lb, lay_lb)),
+    # each layout path forced, beside the default choice (results must agree)
+    paths = {n: dataclasses.replace(cfg, flags=cfg.flags | f) for n, f in LAYOUT_PATHS.items()}
+    path_lay = {n: epx.Layout.empty(c, dev) for n, c in paths.items()}
+    path_ws = {n: epx.workspace_for(c, dev) for n, c in paths.items()}
+    extra_ops = [(n, (lambda n=n: epx.ep_dispatch_layout(paths[n], ids, path_ws[n], path_lay[n]))) for n in paths]
+    extra_ops += [
                  ("combine_bwd_probs", lambda: epx.ep_combine_bwd_probs(cfg, lay, gy, out, gprobs)),
                  ("dispatch_fp8", lambda: epx.ep_dispatch_fp8(cfg, lay, x, fp8_codes, fp8_scales))]
 
@@ -324,12 +332,13 @@ def main() -> int:
     used = np.zeros(R, bool)  # rows past a segment's used rows are never written
     for s_ in range(w.S):
         used[seg_base[s_]:seg_base[s_] + rowoff[s_, -1]] = True
-    for k in ("counts", "seg_base", "row_offsets", "token_row", "flags", "expert_ids", "src_info"):
-        a, b = getattr(lay, k).cpu().numpy(), getattr(lay_lb, k).cpu().numpy()
-        if k in ("expert_ids", "src_info"):
-            a, b = a[used], b[used]
-        if not np.array_equal(a, b):
-            raise RuntimeError(f"the look-back layout differs from the direct one in {k}")
+    for path, other in path_lay.items():
+        for k in ("counts", "seg_base", "row_offsets", "token_row", "flags", "expert_ids", "src_info"):
+            a, b = getattr(lay, k).cpu().numpy(), getattr(other, k).cpu().numpy()
+            if k in ("expert_ids", "src_info"):
+                a, b = a[used], b[used]
+            if not np.array_equal(a, b):
+                raise RuntimeError(f"the {path} layout differs from the default one in {k}")
     kept_routed = int((tr[:, :w.K] >= 0).sum())
     nbytes = algorithmic_bytes(w, kept, used_rows, kept_routed)
     per_op = {}
@@ -482,8 +491,12 @@ def latency_sweep(torch, epx, wl, dev, workload: str, token_counts) -> int:
                     ("combine", lambda: epx.ep_combine(cfg, lay, out, probs, y)),
                     ("combine_bwd", lambda: epx.ep_combine_bwd(cfg, lay, gy, probs, gout)),
                     ("dispatch_bwd", lambda: epx.ep_dispatch_bwd(cfg, lay, out, gx))]
-        ops = step_ops + [("dispatch_fp8", lambda: epx.ep_dispatch_fp8(cfg, lay, x, f8c, f8s)),
-                          ("step", lambda: [fn() for _, fn in step_ops])]
+        paths = {n: dataclasses.replace(cfg, flags=cfg.flags | f) for n, f in LAYOUT_PATHS.items()}
+        path_lay = {n: epx.Layout.empty(c, dev) for n, c in paths.items()}
+        path_ws = {n: epx.workspace_for(c, dev) for n, c in paths.items()}
+        ops = step_ops + [("dispatch_fp8", lambda: epx.ep_dispatch_fp8(cfg, lay, x, f8c, f8s))]
+        ops += [(n, (lambda n=n: epx.ep_dispatch_layout(paths[n], ids, path_ws[n], path_lay[n]))) for n in paths]
+        ops += [("step", lambda: [fn() for _, fn in step_ops])]
         step_ops[0][1]()
         torch.cuda.synchronize()
         res = {}

@@ -28,13 +28,14 @@ import torch
 
 from . import _lib
 from ._lib import (EP_FLAG_BAD_ID, EP_FLAG_DROPPED, EP_FLAG_INTERNAL, EP_FLAG_MAP_OVERFLOW,  # noqa: F401
-                   EP_NOALLOC_SCRATCH_BYTES, EP_ZERO_PAD_ROWS, EP_LAYOUT_LOOKBACK, EpCfg, EpLayout)
+                   EP_NOALLOC_SCRATCH_BYTES, EP_ZERO_PAD_ROWS, EP_LAYOUT_LOOKBACK, EP_LAYOUT_DIRECT,
+                   EP_LAYOUT_BARRIER, EpCfg, EpLayout)
 
 __all__ = [
     "EpConfig", "Layout", "QueryResult", "ep_query", "workspace_for", "ep_dispatch_layout",
     "ep_dispatch_layout_noalloc", "EP_NOALLOC_SCRATCH_BYTES",
     "ep_dispatch", "ep_dispatch_nvfp4", "ep_dispatch_fp8", "ep_combine", "ep_dispatch_bwd", "ep_combine_bwd",
-    "ep_combine_bwd_probs", "ep_indices_to_multihot", "ep_multihot_to_indices", "assert_no_overflow", "EpError", "abi_version", "EP_ZERO_PAD_ROWS", "EP_LAYOUT_LOOKBACK", "EP_FLAG_DROPPED",
+    "ep_combine_bwd_probs", "ep_indices_to_multihot", "ep_multihot_to_indices", "assert_no_overflow", "EpError", "abi_version", "EP_ZERO_PAD_ROWS", "EP_LAYOUT_LOOKBACK", "EP_LAYOUT_DIRECT", "EP_LAYOUT_BARRIER", "EP_FLAG_DROPPED",
     "EP_FLAG_BAD_ID", "EP_FLAG_INTERNAL",
 ]
 
@@ -98,8 +99,10 @@ def ep_query(cfg: EpConfig) -> QueryResult:
 
 
 def workspace_for(cfg: EpConfig, device) -> torch.Tensor:
-    """A uint8 device tensor large enough for ep_dispatch_layout's workspace."""
-    return torch.empty(ep_query(cfg).workspace_bytes, dtype=torch.uint8, device=device)
+    """A zero-filled uint8 device tensor large enough for ep_dispatch_layout's
+    workspace.  Keep passing the same tensor to later layout calls: each call
+    leaves it ready for the next (it must only be zero before its first use)."""
+    return torch.zeros(ep_query(cfg).workspace_bytes, dtype=torch.uint8, device=device)
 
 
 @dataclasses.dataclass

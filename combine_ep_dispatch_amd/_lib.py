@@ -19,6 +19,8 @@ EP_ESCRATCH = -4
 EP_NOALLOC_SCRATCH_BYTES = 4 << 20
 EP_ZERO_PAD_ROWS = 1
 EP_LAYOUT_LOOKBACK = 2
+EP_LAYOUT_DIRECT = 4
+EP_LAYOUT_BARRIER = 8
 EP_FLAG_DROPPED = 1
 EP_FLAG_BAD_ID = 2
 EP_FLAG_INTERNAL = 4

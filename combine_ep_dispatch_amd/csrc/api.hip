@@ -22,7 +22,7 @@ using namespace epx;
 
 struct Shape {
     int32_t T, H, E, S, K, Kp, A, C, shared, src, E_loc, G, NG;
-    int64_t R, min_rows, ws_bytes, tiles;
+    int64_t R, min_rows, ws_bytes, tiles, sp_tiles;
     uint32_t flags;
 };
 
@@ -44,7 +44,9 @@ int derive(const ep_cfg_t* c, Shape* d) {
     if (c->shared_expert != 0 && c->shared_expert != 1) return EP_EINVAL;
     if (c->shared_expert && (c->src_segment < 0 || c->src_segment >= c->num_segments)) return EP_EINVAL;
     if (c->reserved0 != 0 || c->reserved1 != 0) return EP_EINVAL;
-    if (c->flags & ~(EP_ZERO_PAD_ROWS | EP_LAYOUT_LOOKBACK)) return EP_EINVAL;
+    constexpr uint32_t kPaths = EP_LAYOUT_LOOKBACK | EP_LAYOUT_DIRECT | EP_LAYOUT_BARRIER;
+    if (c->flags & ~(EP_ZERO_PAD_ROWS | kPaths)) return EP_EINVAL;
+    if (__builtin_popcount(c->flags & kPaths) > 1) return EP_EINVAL;  // at most one path
     d->T = c->num_tokens;
     d->H = c->hidden;
     d->E = c->num_experts;
@@ -63,15 +65,21 @@ int derive(const ep_cfg_t* c, Shape* d) {
     d->NG = (int32_t)ng;
     const int64_t slots = (int64_t)d->T * d->Kp;
     if (slots >= (int64_t(1) << 30)) return EP_EINVAL;  // look-back descriptors hold 30-bit counts
-    if (d->C > 0) {
-        d->min_rows = (int64_t)d->S * d->C;
-    } else {
-        const int64_t groups = (int64_t)d->E + d->shared;
-        d->min_rows = slots + (slots < groups ? slots : groups) * (int64_t)(d->A - 1);
-    }
+    // Every group is padded by at most A - 1 rows, so the used rows of all
+    // segments before any capacity clamp are at most `packed`.  The layout
+    // kernels add up the aligned group sizes in int32 before clamping them to
+    // C, so this bound must fit in int32 in capacity mode too.
+    const int64_t groups = (int64_t)d->E + d->shared;
+    const int64_t packed = slots + (slots < groups ? slots : groups) * (int64_t)(d->A - 1);
+    if (packed >= (int64_t(1) << 31)) return EP_EINVAL;
+    d->min_rows = d->C > 0 ? (int64_t)d->S * d->C : packed;
     if (d->min_rows >= (int64_t(1) << 31)) return EP_EINVAL;  // rows are int32
+    // Workspace: a header, then either path's per-tile tables (32-bit tile
+    // counts of the direct path; two arrays of 64-bit descriptors of the
+    // single pass).
     d->tiles = layout_tiles((int64_t)d->T * d->K, d->NG);
-    d->ws_bytes = kWorkspaceHeader + d->tiles * (int64_t)d->NG * 4;
+    d->sp_tiles = sp_tiles((int64_t)d->T * d->K);
+    d->ws_bytes = kWorkspaceHeader + std::max(d->tiles * (int64_t)d->NG * 4, d->sp_tiles * (int64_t)d->NG * 16);
     d->R = c->recv_rows;
     d->flags = c->flags;
     return EP_OK;
@@ -150,7 +158,7 @@ int layout_check(const Shape& d, const int32_t* topk_ids, const ep_layout_t* L) 
         bad_buffer(L->row_offsets, (int64_t)d.S * (d.G + 1) * 4, 4) ||
         bad_buffer(L->scales_offsets, (int64_t)d.S * (d.G + 1) * 4, 4) ||
         bad_buffer(L->token_row, (int64_t)d.T * d.Kp * 4, 4) || bad_buffer(L->expert_ids, d.R * 4, 4) ||
-        bad_buffer(L->src_info, d.R * 8, 4) || bad_buffer(L->flags, 4, 4))
+        bad_buffer(L->src_info, d.R * 8, 8) || bad_buffer(L->flags, 4, 4))
         return EP_EINVAL;
     return EP_OK;
 }
@@ -175,16 +183,37 @@ int layout_launch(const Shape& d, const int32_t* topk_ids, void* ws, const ep_la
     a.shared = d.shared;
     a.src_seg = d.src;
     a.recv_rows = d.R;
-    a.tiles = (int32_t)d.tiles;
+    a.sp_header = ws;
+    a.sp_desc = reinterpret_cast<uint64_t*>(static_cast<uint8_t*>(ws) + kWorkspaceHeader);
     const int64_t routed = (int64_t)d.T * d.K;
-    if (d.flags & EP_LAYOUT_LOOKBACK) a.mode = kLayoutLookback;
-    else if (routed <= kSmallMaxSlots) a.mode = kLayoutSmall;
-    else if (layout_direct(d.tiles)) a.mode = kLayoutDirect;
-    else a.mode = kLayoutLookback;
-    a.rank_blocks = (int32_t)std::max<int64_t>(d.tiles, std::min<int32_t>(d.NG, 256));
-    // One tile holds every slot in the single-pass mode.
-    a.slots_per_thread = a.mode == kLayoutSmall ? (routed <= 256 ? 1 : (routed <= 512 ? 2 : 4))
-                                                : layout_slots_per_thread(routed, d.NG);
+    a.lookback = 0;
+    if (d.flags & EP_LAYOUT_LOOKBACK) {
+        a.mode = kLayoutSinglePass;
+        a.lookback = 1;
+    } else if (d.flags & EP_LAYOUT_BARRIER) {
+        a.mode = kLayoutSinglePass;
+    } else if (d.flags & EP_LAYOUT_DIRECT) {
+        a.mode = kLayoutDirect;
+    } else if (routed <= kSmallMaxSlots) {
+        a.mode = kLayoutSmall;
+    } else if (layout_direct(d.tiles) || d.sp_tiles > kSpMaxTiles) {
+        a.mode = kLayoutDirect;  // measured fastest wherever its column sums fit one launch
+    } else {
+        a.mode = kLayoutSinglePass;  // past 256 direct-path tiles the column sums grow with the tile count
+    }
+    if (a.mode == kLayoutSinglePass) {
+        a.tiles = (int32_t)d.sp_tiles;
+        a.rank_blocks = (int32_t)sp_blocks(d.sp_tiles, d.NG);
+        a.slots_per_thread = sp_slots_per_thread(routed);
+    } else if (a.mode == kLayoutDirect) {
+        a.tiles = (int32_t)d.tiles;
+        a.rank_blocks = (int32_t)std::max<int64_t>(d.tiles, std::min<int32_t>(d.NG, 256));
+        a.slots_per_thread = layout_slots_per_thread(routed, d.NG);
+    } else {  // one tile holds every slot
+        a.tiles = 1;
+        a.rank_blocks = std::min<int32_t>(d.NG, 256);
+        a.slots_per_thread = routed <= 256 ? 1 : (routed <= 512 ? 2 : 4);
+    }
     return status_of(launch_layout(a, static_cast<hipStream_t>(stream)));
 }
 

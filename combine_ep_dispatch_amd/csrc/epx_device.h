@@ -18,12 +18,12 @@ constexpr int kMaxSlots = EP_MAX_SLOTS;  // K + shared_expert: one slot per lane
 constexpr int kLayoutThreads = 256;                      // 4 waves
 constexpr int kLayoutWaves = kLayoutThreads / kWave;
 constexpr int kWorkspaceHeader = 256;                    // reserved header before the descriptors
-// Up to this many tiles the layout takes the direct path: the histogram
-// launch stores each tile's per-group counts as a row of a [tile][group]
-// table, and every rank workgroup sums each group's whole column (its prefix
-// over earlier tiles and the group total).  Above it, the decoupled
-// look-back over [tile][group] descriptors keeps the work linear in the
-// tile count.
+// Up to this many tiles the layout takes the direct path by default: the
+// histogram launch stores each tile's per-group counts as a row of a
+// [tile][group] table, and every rank workgroup sums each group's whole
+// column (its prefix over earlier tiles and the group total).  Above it the
+// single pass (one kernel) is the default, whose reads grow more slowly with
+// the tile count.
 constexpr int kDirectMaxTiles = 256;
 inline bool layout_direct(int64_t tiles) { return tiles <= kDirectMaxTiles; }
 
@@ -66,12 +66,41 @@ inline int64_t layout_tiles(int64_t routed_slots, int NG) {
 // then takes longer than the second launch.
 constexpr int64_t kSmallMaxSlots = 1024;
 
-// How k_layout_rank resolves a tile's in-group prefix.
-constexpr int kLayoutLookback = 0;  // decoupled look-back over descriptors
-constexpr int kLayoutDirect = 1;    // sums of the [tile][group] count table
-constexpr int kLayoutSmall = 2;     // single pass: the only tile, prefix 0
+// Layout kernel paths.
+constexpr int kLayoutSinglePass = 0;  // k_layout_sp: ticketed tiles, decoupled look-back
+constexpr int kLayoutDirect = 1;      // k_layout_hist + k_layout_rank over a [tile][group] count table
+constexpr int kLayoutSmall = 2;       // k_layout_rank alone: one tile, every workgroup ranks it
 
-// Look-back descriptor: 2 status bits over a 30-bit count.
+// Single-pass layout tiles: 256 x {1, 2, 4, 8} slots, the smallest tile
+// that gives at most kSpTargetTiles tiles (16, 32 and 64 measured within 1
+// us of each other at 8k-32k routed slots).  A workgroup remembers at most
+// kSpMaxTilesPerBlock tiles it took, so the single pass needs
+// tiles <= 32 x the workgroups that can run at once; it is the default only
+// up to kSpMaxTiles tiles (8192 = 32 x one workgroup per CU).
+#ifndef EPX_SP_TILES
+#define EPX_SP_TILES 32
+#endif
+constexpr int kSpTargetTiles = EPX_SP_TILES;
+constexpr int kSpMaxTilesPerBlock = 32;
+constexpr int64_t kSpMaxTiles = 8192;
+inline int sp_slots_per_thread(int64_t routed_slots) {
+    for (int spt = 1; spt < 8; spt *= 2)
+        if (routed_slots <= (int64_t)kLayoutThreads * spt * kSpTargetTiles) return spt;
+    return 8;
+}
+inline int64_t sp_tiles(int64_t routed_slots) {
+    const int64_t tile = (int64_t)kLayoutThreads * sp_slots_per_thread(routed_slots);
+    const int64_t nt = (routed_slots + tile - 1) / tile;
+    return nt < 1 ? 1 : nt;
+}
+// Single-pass workgroups: every tile has one; at least min(groups, 64) so
+// that the groups' metadata runs are spread out.
+inline int64_t sp_blocks(int64_t tiles, int NG) {
+    const int64_t g = NG < 64 ? NG : 64;
+    return tiles > g ? tiles : g;
+}
+
+// Look-back descriptor value word: 2 status bits over a 30-bit count.
 constexpr uint32_t kDescAgg = 1u << 30;   // tile aggregate only
 constexpr uint32_t kDescInc = 2u << 30;   // inclusive prefix through this tile
 constexpr uint32_t kDescValue = (1u << 30) - 1;
@@ -148,13 +177,16 @@ __device__ __forceinline__ T uniform(T v) {
 // ---------------------------------------------------------------------------
 struct LayoutArgs {
     const int32_t* topk_ids;
-    uint32_t* desc;  // [tiles][NG]: tile counts (direct) or look-back descriptors
+    uint32_t* desc;      // direct path: [tiles][NG] tile counts
+    void* sp_header;     // single pass: workspace header (generation, ticket, ...)
+    uint64_t* sp_desc;   // single pass: [tiles][NG] look-back descriptors
     ep_layout_t out;
     int32_t T, K, Kp, E, S, G, NG, E_loc, A, C, shared, src_seg;
     int64_t recv_rows;
-    int32_t tiles;
-    int32_t mode;              // kLayoutLookback, kLayoutDirect or kLayoutSmall
-    int32_t rank_blocks;       // workgroups of the rank pass: max(tiles, min(NG, 256))
+    int32_t tiles;             // tiles of the path that runs
+    int32_t mode;              // kLayoutSinglePass, kLayoutDirect or kLayoutSmall
+    int32_t lookback;          // single pass: tile prefixes by decoupled look-back (else from all aggregates)
+    int32_t rank_blocks;       // workgroups of the rank pass / single pass: max(tiles, min(NG, 256))
     int32_t slots_per_thread;  // 1, 2, 4 or 8 (layout_slots_per_thread)
 };
 hipError_t launch_layout(const LayoutArgs& a, hipStream_t stream);

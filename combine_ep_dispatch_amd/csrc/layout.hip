@@ -13,74 +13,63 @@
 //    row_offsets, expert_ids per received token, src_info, atomic counters
 //    coordinating work across thread blocks.
 //
-// Two launches on the caller's stream (the direct path, up to
-// kDirectMaxTiles tiles; every configuration up to ~500k routed slots):
-//  1. k_layout_hist   per tile of 256 x {2,4,8} routed slots (chosen so that
-//                     there are about 64 tiles), a wave64 match-any over
-//                     the group key (one ballot per key bit); the lowest lane
-//                     of each match set adds the set's popcount into an LDS
-//                     counter, so a hot expert costs one LDS atomic per wave
-//                     instead of one per slot.  Each tile stores its
-//                     per-group counts as one row of a [tile][group]
-//                     table; tile 0 also clears the flags word.
+// Three paths, all with the same results (the host picks one by size or by
+// the EP_LAYOUT_* flag the caller sets):
+//
+// Small (up to 1024 routed slots): k_layout_rank alone; every workgroup
+// ranks the one tile to learn the group totals, workgroup 0 writes the
+// per-slot results and the others spread the groups' metadata runs.
+//
+// Two kernels (default up to 256 tiles, any size with EP_LAYOUT_DIRECT):
+//  1. k_layout_hist   per tile of 256 x {1,2,4,8} routed slots, a wave64
+//                     match-any over the group key (one ballot per key bit);
+//                     the lowest lane of each match set adds the set's
+//                     popcount into an LDS counter, so a hot expert costs one
+//                     LDS atomic per wave instead of one per slot.  Each tile
+//                     stores its per-group counts as one row of a
+//                     [tile][group] table; tile 0 also clears the flags word.
 //  2. k_layout_rank   every workgroup reads, for each group, the group's
-//                     column of tile counts (lanes over groups, so wave
-//                     loads are contiguous; 64 loads in flight per lane, and
-//                     several lanes per group when groups are few) and sums
-//                     it twice: over all tiles (the group total) and over the
-//                     tiles before its own (its in-group prefix).  No workgroup waits on another, and
-//                     there are no atomics on global memory but the flags.
-//                     It then scans the aligned group sizes into group start
-//                     rows, ranks its tile's slots inside their groups
-//                     (per-wave running counters in LDS + match-any), and
-//                     writes counts (tile 0), offsets, token_row and
-//                     src_info.  The fused shared-expert rows, and
-//                     expert_ids of whole groups (pad rows included) as
+//                     column of tile counts (lanes over groups, so wave loads
+//                     are contiguous; 64 loads in flight per lane, and several
+//                     lanes per group when groups are few) and sums it twice:
+//                     over all tiles (the group total) and over the tiles
+//                     before its own (its in-group prefix).  No workgroup
+//                     waits on another, and there are no atomics on global
+//                     memory but the flags.  It then scans the aligned group
+//                     sizes into group start rows, ranks its tile's slots
+//                     inside their groups (per-wave running counters in LDS,
+//                     one 4-byte word per group so neighbouring groups share
+//                     no bank word, touched only by the lowest lane of each
+//                     match set), and writes counts (tile 0), offsets,
+//                     token_row and src_info.  The fused shared-expert rows,
+//                     and expert_ids of whole groups (pad rows included) as
 //                     coalesced runs, are spread over at least
-//                     min(groups, 256) workgroups: the ones past the last
-//                     tile do only this.
-// Above kDirectMaxTiles the per-workgroup row sums would grow with the tile
-// count, so three launches are used instead (also on request, with
-// EP_LAYOUT_LOOKBACK; the results are the same):
-//  0. k_layout_clear  zero the counts (the shared group gets T) and flags.
-//  1. k_layout_hist   publishes each tile's per-group aggregate as a
-//                     look-back descriptor ([tile][group], 2 status bits
-//                     over a 30-bit count; tile 0 publishes its inclusive
-//                     prefix) and adds its nonzero counters into `counts`.
-//  2. k_layout_rank   resolves its per-group prefix by decoupled look-back
-//                     (16 predecessor descriptors per round trip, folded
-//                     nearest-first until an inclusive prefix is met) and
-//                     upgrades its own descriptors to inclusive prefixes.
-//                     Every aggregate is published by the previous launch,
-//                     so no workgroup ever waits on another one.
-// Invalid ids are detected where the slots are ranked (k_layout_rank).
+//                     min(groups, 256) workgroups.
+//
+// Single pass (default past 256 tiles; any size with EP_LAYOUT_LOOKBACK or
+// EP_LAYOUT_BARRIER): k_layout_sp, one kernel with ticketed tiles, described
+// above it.  Measured on MI355X it is slower than the two kernels wherever
+// those apply (DeepSeek-V3 share: 14.8 against 12.0 us per launch; the
+// look-back flavour 19.9): a position needs the totals of all groups, so the
+// single pass waits for the slowest tile's counts through memory-side loads
+// across the XCDs, which costs more than the second launch.
 #include "epx_device.h"
 
 namespace epx {
 namespace {
 
-constexpr int kMaxSpins = 1 << 22;  // look-back gives up (EP_FLAG_INTERNAL) after this
-constexpr int kLookback = 16;       // predecessor descriptors read per round trip
+// A wait on another workgroup gives up (EP_FLAG_INTERNAL) once the
+// workgroup has run this many ticks of the 100 MHz wall clock (about 0.34 s);
+// every later wait of the workgroup then gives up at once, so a call whose
+// waits cannot end still finishes in bounded time.
+constexpr uint64_t kWaitTicks = 1ull << 25;
 
 __device__ __forceinline__ int32_t align_up(int32_t count, int32_t multiple) {
     if ((multiple & (multiple - 1)) == 0) return (count + multiple - 1) & -multiple;  // power of two
     return ((count + multiple - 1) / multiple) * multiple;
 }
 
-__device__ __forceinline__ uint32_t desc_load(const uint32_t* p) {
-    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void desc_store(uint32_t* p, uint32_t v) {
-    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-__global__ __launch_bounds__(256) void k_layout_clear(LayoutArgs a) {
-    const int32_t shared_group = a.shared ? a.src_seg * a.G : -1;
-    for (int g = threadIdx.x; g < a.NG; g += blockDim.x) a.out.counts[g] = (g == shared_group) ? a.T : 0;
-    if (threadIdx.x == 0) a.out.flags[0] = 0;
-}
-
-template <int SPT, bool DIRECT>
+template <int SPT>
 __global__ __launch_bounds__(kLayoutThreads) void k_layout_hist(LayoutArgs a) {
     constexpr int kTileSlots = kLayoutThreads * SPT;
     __shared__ int32_t s_hist[EP_MAX_GROUPS];
@@ -107,24 +96,14 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout_hist(LayoutArgs a) {
             atomicAdd(&s_hist[key], (int32_t)__popcll(m));
     }
     __syncthreads();
-    if (DIRECT) {
-        uint32_t* row = a.desc + (int64_t)blockIdx.x * a.NG;
-        for (int g = tid; g < a.NG; g += kLayoutThreads) row[g] = (uint32_t)s_hist[g];
-        if (blockIdx.x == 0 && tid == 0) a.out.flags[0] = 0;
-    } else {
-        const uint32_t status = blockIdx.x == 0 ? kDescInc : kDescAgg;  // tile 0: prefix 0 + aggregate
-        uint32_t* desc = a.desc + (int64_t)blockIdx.x * a.NG;
-        for (int g = tid; g < a.NG; g += kLayoutThreads) {
-            const int32_t c = s_hist[g];
-            desc_store(&desc[g], status | (uint32_t)c);
-            if (c) atomicAdd(&a.out.counts[g], c);
-        }
-    }
+    uint32_t* row = a.desc + (int64_t)blockIdx.x * a.NG;
+    for (int g = tid; g < a.NG; g += kLayoutThreads) row[g] = (uint32_t)s_hist[g];
+    if (blockIdx.x == 0 && tid == 0) a.out.flags[0] = 0;
 }
 
 template <int SPT, int MODE>
 __global__ __launch_bounds__(kLayoutThreads) void k_layout_rank(LayoutArgs a) {
-    constexpr bool DIRECT = MODE == kLayoutDirect, SMALL = MODE == kLayoutSmall, LOOKBACK = MODE == kLayoutLookback;
+    constexpr bool DIRECT = MODE == kLayoutDirect, SMALL = MODE == kLayoutSmall;
     constexpr int kTileSlots = kLayoutThreads * SPT;
     constexpr int kSlotsPerWave = kWave * SPT;
     __shared__ int32_t s_cnt[EP_MAX_GROUPS];    // group totals
@@ -132,7 +111,7 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout_rank(LayoutArgs a) {
     __shared__ int32_t s_lim[EP_MAX_GROUPS];    // first row past the segment's capacity
     __shared__ int32_t s_pref[EP_MAX_GROUPS];   // slots of the group in earlier tiles
     __shared__ int32_t s_gof[EP_MAX_GROUPS];    // group of each routed expert
-    __shared__ uint16_t s_wcnt[kLayoutWaves][EP_MAX_GROUPS];  // per-wave counts / prefixes
+    __shared__ int32_t s_wcnt[kLayoutWaves][EP_MAX_GROUPS];  // per-wave counts / prefixes (a 4-byte word each)
     __shared__ int32_t s_wsum[kLayoutWaves];
     __shared__ int32_t s_flag;
 
@@ -206,8 +185,6 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout_rank(LayoutArgs a) {
                 s_pref[g] = pre;
             }
         }
-    } else if (LOOKBACK) {
-        for (int g = tid; g < NG; g += kLayoutThreads) s_cnt[g] = a.out.counts[g];
     }
     for (int e = tid; e < a.E; e += kLayoutThreads)
         s_gof[e] = (e / a.E_loc) * G + a.shared + (e % a.E_loc);
@@ -231,12 +208,15 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout_rank(LayoutArgs a) {
             if (e != -1 && (uint32_t)e >= (uint32_t)a.E) flag |= EP_FLAG_BAD_ID;  // -1 = masked slot
             const uint64_t m = match_any(k, nbits);
             const uint32_t r = lanes_below(m);
-            rnk[it] = 0;
-            if (k != (uint32_t)NG) {
-                const uint32_t before = s_wcnt[w][k];
-                rnk[it] = before + r;
-                if (r == 0) s_wcnt[w][k] = (uint16_t)(before + (uint32_t)__popcll(m));
+            // only the lowest lane of each key touches LDS; the others take
+            // its value by a cross-lane read
+            int32_t before = 0;
+            if (k != (uint32_t)NG && r == 0) {
+                before = s_wcnt[w][k];
+                s_wcnt[w][k] = before + (int32_t)__popcll(m);
             }
+            before = __shfl(before, (int)__builtin_ctzll(m), kWave);
+            rnk[it] = k != (uint32_t)NG ? (uint32_t)before + r : 0u;
             key[it] = k;
         }
         __syncthreads();
@@ -251,7 +231,7 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout_rank(LayoutArgs a) {
 #pragma unroll
                 for (int w2 = 0; w2 < kLayoutWaves; ++w2) {
                     const int32_t c = s_wcnt[w2][g];
-                    s_wcnt[w2][g] = (uint16_t)run;
+                    s_wcnt[w2][g] = run;
                     run += c;
                 }
                 agg[j] = run;
@@ -311,8 +291,7 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout_rank(LayoutArgs a) {
     // Counts (direct and single-pass paths), offsets and segment bases: one
     // tile writes them.
     if (tile == 0) {
-        if (!LOOKBACK)
-            for (int g = tid; g < NG; g += kLayoutThreads) a.out.counts[g] = s_cnt[g];
+        for (int g = tid; g < NG; g += kLayoutThreads) a.out.counts[g] = s_cnt[g];
         const int n = a.S * (G + 1);
         for (int idx = tid; idx < n; idx += kLayoutThreads) {
             const int s = idx / (G + 1), gl = idx - s * (G + 1);
@@ -363,51 +342,6 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout_rank(LayoutArgs a) {
 
     if (!SMALL) rank_slots();
 
-    // ---- decoupled look-back over earlier tiles (look-back path only) ----
-#pragma unroll
-    for (int j = 0; j < EP_MAX_GROUPS / kLayoutThreads; ++j) {
-        const int g = tid + j * kLayoutThreads;
-        if (!LOOKBACK || g >= NG) continue;
-        uint32_t pref = 0;
-        if (owns_tile && tile > 0 && s_cnt[g] > 0 && g != shared_group) {
-            // Read a window of kLookback predecessors at once (independent
-            // loads, one round trip), then fold them nearest-first until an
-            // inclusive prefix is found.  Tile 0's descriptor is inclusive
-            // from the start, so the walk ends at or before it.  Every
-            // descriptor was published by the histogram launch; the wait
-            // below is only a guard and gives up after kMaxSpins polls.
-            bool done = false;
-            for (int64_t p = (int64_t)tile - 1; !done && p >= 0; p -= kLookback) {
-                uint32_t d[kLookback];
-#pragma unroll
-                for (int i = 0; i < kLookback; ++i)
-                    d[i] = (p - i >= 0) ? desc_load(&a.desc[(p - i) * NG + g]) : kDescInc;
-#pragma unroll
-                for (int i = 0; i < kLookback; ++i) {
-                    if (done || p - i < 0) {
-                        done = true;
-                        continue;
-                    }
-                    const uint32_t* dp = &a.desc[(p - i) * NG + g];
-                    uint32_t di = d[i];
-                    int spins = 0;
-                    while ((di & ~kDescValue) == 0u) {  // not published yet
-                        if (++spins > kMaxSpins) {
-                            flag |= EP_FLAG_INTERNAL;
-                            di = kDescInc;
-                            break;
-                        }
-                        __builtin_amdgcn_s_sleep(1);
-                        di = desc_load(dp);
-                    }
-                    pref += di & kDescValue;
-                    if (di & kDescInc) done = true;
-                }
-            }
-            desc_store(&a.desc[(int64_t)tile * NG + g], kDescInc | (pref + (uint32_t)agg[j]));
-        }
-        s_pref[g] = (int32_t)pref;
-    }
     __syncthreads();
 
     // ---- write the routed slots of this tile ----
@@ -511,26 +445,594 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout_rank(LayoutArgs a) {
     if (tid == 0 && s_flag) atomicOr(a.out.flags, s_flag);
 }
 
-}  // namespace
-
-template <int SPT, bool DIRECT>
-void launch_passes(const LayoutArgs& a, hipStream_t stream) {
-    constexpr int kMode = DIRECT ? kLayoutDirect : kLayoutLookback;
-    const dim3 block(kLayoutThreads);
-    if (!DIRECT) hipLaunchKernelGGL(k_layout_clear, dim3(1), dim3(256), 0, stream, a);
-    hipLaunchKernelGGL((k_layout_hist<SPT, DIRECT>), dim3((unsigned)a.tiles), block, 0, stream, a);
-    hipLaunchKernelGGL((k_layout_rank<SPT, kMode>), dim3((unsigned)a.rank_blocks), block, 0, stream, a);
+// ---------------------------------------------------------------------------
+// Single-pass layout: one launch at any size.
+//
+// Workgroups whose index is below the tile count are tile workers: each
+// takes tile numbers from an atomic ticket until none are left, so a tile is
+// only ever taken by a running workgroup, and a workgroup only waits on
+// others once every tile has been handed out (and, in the look-back, only on
+// tiles with smaller tickets, taken earlier).  Per tile: rank its slots
+// inside their groups (match-any + per-wave counters) and publish the tile's
+// per-group aggregate.  Every position needs the totals of all groups (a
+// group's first row depends on the sizes of all groups before it), so each
+// workgroup then reads the aggregates of the other tiles.  The tile's
+// in-group prefix over earlier tiles comes either from
+//  - LOOKBACK = true: a decoupled look-back inside the ticket loop
+//    (windows of predecessor descriptors read in one round trip, folded
+//    nearest-first until an inclusive prefix is met; the tile then publishes
+//    its own inclusive prefix), the totals being that prefix plus the
+//    aggregates of the later tiles; or
+//  - LOOKBACK = false: the same read of every tile's aggregate that gives the
+//    totals (the sum over the tiles before this one).
+// Every wait re-polls all the still unpublished entries of its window in one
+// round trip.  The workgroup then scans the aligned group sizes into group
+// start rows and writes its tiles' token_row and src_info; src_info goes
+// through LDS in group-major order, so each wave store covers consecutive
+// receive rows.  expert_ids and pad-row metadata of whole groups are written
+// as coalesced runs by all workgroups.
+//
+// Workspace: a header {generation | ticket, departures, flag bits}, then
+// two arrays of 64-bit descriptors [tile][group] = generation:32 |
+// status:2 | value:30: the look-back descriptors (aggregate, upgraded to the
+// inclusive prefix) and the tiles' aggregates alone (written once).  The
+// generation tells descriptors of this call from stale ones, so they are
+// never cleared.  Every flag bit is known once the totals are (dropped
+// slots and rows past the buffer follow from the group sizes), so each
+// workgroup reports its bits with its departure right then, in one atomic
+// add; the last one out writes the flags word, bumps the generation and
+// resets the ticket and the departure word, which leaves the workspace
+// ready for the next call.
+struct SpHeader {
+    uint64_t ctl;     // generation (high 32 bits) | next tile ticket (low 32 bits)
+    uint64_t depart;  // 16-bit fields: workgroups that have left (bits 0-15), and
+                      // of those, how many saw a dropped slot, a bad id, or gave
+                      // up a wait (bits 16-31, 32-47, 48-63)
+};
+// One workgroup's departure: its count and flag bits in the fields of
+// SpHeader::depart (grids stay below 2^16 workgroups).
+__device__ __forceinline__ uint64_t sp_departure(int32_t f) {
+    return 1ull | ((f & EP_FLAG_DROPPED) ? 1ull << 16 : 0ull) | ((f & EP_FLAG_BAD_ID) ? 1ull << 32 : 0ull) |
+           ((f & EP_FLAG_INTERNAL) ? 1ull << 48 : 0ull);
 }
+__device__ __forceinline__ int32_t sp_flags_of(uint64_t d) {
+    return ((d >> 16) & 0xFFFFu ? EP_FLAG_DROPPED : 0) | ((d >> 32) & 0xFFFFu ? EP_FLAG_BAD_ID : 0) |
+           ((d >> 48) & 0xFFFFu ? EP_FLAG_INTERNAL : 0);
+}
+
+__device__ __forceinline__ uint64_t sp_load(const uint64_t* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void sp_store(uint64_t* p, uint64_t v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ bool sp_published(uint64_t d, uint32_t gen) {
+    return (uint32_t)(d >> 32) == gen && ((uint32_t)d & ~kDescValue) != 0u;
+}
+__device__ __forceinline__ int32_t sp_value(uint64_t d) { return (int32_t)((uint32_t)d & kDescValue); }
+
+// Sum over tiles u in [lo, hi) of the published value src[u * NG + g]
+// (tiles at or after `split` also go to *after`), W loads in flight; the
+// unpublished entries of a window are re-polled together until published or
+// the workgroup's wait budget runs out (then EP_FLAG_INTERNAL).
+template <int W>
+__device__ __forceinline__ int32_t sp_sum(const uint64_t* src, int NG, int g, uint32_t lo, uint32_t hi,
+                                          uint32_t split, int32_t* after, uint32_t gen, uint64_t t_begin,
+                                          int32_t& flag) {
+    const uint64_t zero = ((uint64_t)gen << 32) | kDescAgg;
+    int32_t acc = 0, acc_after = 0;
+    for (uint32_t u = lo; u < hi; u += W) {
+        uint64_t d[W];
+#pragma unroll
+        for (int i = 0; i < W; ++i) d[i] = u + i < hi ? sp_load(&src[(int64_t)(u + i) * NG + g]) : zero;
+        for (;;) {
+            bool pending = false;
+#pragma unroll
+            for (int i = 0; i < W; ++i) pending |= !sp_published(d[i], gen);
+            if (!pending) break;
+            if (wall_clock64() - t_begin > kWaitTicks) {
+                flag |= EP_FLAG_INTERNAL;
+#pragma unroll
+                for (int i = 0; i < W; ++i) d[i] = sp_published(d[i], gen) ? d[i] : zero;
+                break;
+            }
+            __builtin_amdgcn_s_sleep(1);
+#pragma unroll
+            for (int i = 0; i < W; ++i)
+                if (!sp_published(d[i], gen)) d[i] = sp_load(&src[(int64_t)(u + i) * NG + g]);
+        }
+#pragma unroll
+        for (int i = 0; i < W; ++i) {
+            const int32_t v = sp_value(d[i]);
+            acc += v;
+            acc_after += u + i >= split ? v : 0;
+        }
+    }
+    if (after != nullptr) *after = acc_after;
+    return acc;
+}
+
+// Decoupled look-back for tile t > 0 and group g: the sum of the values of
+// descriptors t-1, t-2, ... folded nearest-first up to and including the
+// first inclusive one, W descriptors per round trip; when the nearest
+// unfolded entry is not yet published, the unfolded entries of the window
+// are re-polled together.
+template <int W>
+__device__ __forceinline__ int32_t sp_lookback(const uint64_t* desc, int NG, int g, uint32_t t, uint32_t gen,
+                                               uint64_t t_begin, int32_t& flag) {
+    int32_t acc = 0;
+    bool done = false;
+    for (int64_t p = (int64_t)t - 1; !done; p -= W) {
+        uint64_t d[W];
+#pragma unroll
+        for (int i = 0; i < W; ++i) d[i] = p - i >= 0 ? sp_load(&desc[(p - i) * NG + g]) : 0ull;
+        uint64_t folded = 0;  // bit i: entry i already added
+        for (;;) {
+            bool blocked = false;
+#pragma unroll
+            for (int i = 0; i < W; ++i) {
+                if (done || blocked || ((folded >> i) & 1u)) continue;
+                if (p - i < 0) {  // tile 0 is inclusive from the start: not reached
+                    done = true;
+                    continue;
+                }
+                if (!sp_published(d[i], gen)) {
+                    blocked = true;
+                    continue;
+                }
+                acc += sp_value(d[i]);
+                folded |= 1ull << i;
+                if ((uint32_t)d[i] & kDescInc) done = true;
+            }
+            if (done || !blocked) break;
+            if (wall_clock64() - t_begin > kWaitTicks) {
+                flag |= EP_FLAG_INTERNAL;
+                done = true;
+                break;
+            }
+            __builtin_amdgcn_s_sleep(1);
+#pragma unroll
+            for (int i = 0; i < W; ++i)
+                if (!((folded >> i) & 1u) && p - i >= 0) d[i] = sp_load(&desc[(p - i) * NG + g]);
+        }
+    }
+    return acc;
+}
+
+template <int SPT, int MAXG, bool LOOKBACK>
+__global__ __launch_bounds__(kLayoutThreads) void k_layout_sp(LayoutArgs a) {
+    constexpr int J = MAXG / kLayoutThreads;  // groups per thread, contiguous: tid*J + j
+    constexpr int W = 32 / J;                 // descriptors per group per round trip
+    constexpr int kTileSlots = kLayoutThreads * SPT;
+    constexpr int kSlotsPerWave = kWave * SPT;
+    __shared__ int32_t s_cnt[MAXG];    // group totals
+    __shared__ int32_t s_start[MAXG];  // first row of the group (clamped at capacity)
+    __shared__ int32_t s_lim[MAXG];    // first row past the segment's capacity
+    __shared__ int32_t s_base[MAXG];   // tile: first row of the group's run minus its stage offset
+    __shared__ int32_t s_wcnt[kLayoutWaves][MAXG];  // per-wave counters, then stage offsets
+    __shared__ uint16_t s_gof[MAXG];   // group of each routed expert (E <= NG)
+    __shared__ int2 s_stage[kTileSlots];  // (row, flat slot) in group-major order
+    __shared__ int32_t s_wsum[kLayoutWaves];
+    __shared__ int32_t s_flag, s_ntiles, s_nstage;
+    __shared__ uint32_t s_ticket, s_gen;
+    __shared__ int32_t s_tiles[kSpMaxTilesPerBlock];
+
+    const uint64_t t_begin = wall_clock64();
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), w = tid / kWave;
+    const int NG = a.NG, G = a.G;
+    SpHeader* hdr = reinterpret_cast<SpHeader*>(a.sp_header);
+    const uint32_t NT = (uint32_t)a.tiles;
+    uint64_t* desc = a.sp_desc;                     // [NT][NG] aggregate, then inclusive prefix
+    uint64_t* aggs = a.sp_desc + (int64_t)NT * NG;  // [NT][NG] aggregate only (written once)
+    const bool worker = blockIdx.x < NT;
+    const int64_t routed = (int64_t)a.T * a.K;
+    const int32_t shared_group = a.shared ? a.src_seg * G : -1;
+    const int nbits = 32 - __clz(NG);  // keys live in [0, NG]; NG = "no group"
+
+    // Ticket (workers) or generation (the rest) first; the ids of tile
+    // blockIdx.x are fetched meanwhile, in case the ticket is that tile.
+    if (tid == 0) {
+        if (worker) {
+            const uint64_t c = __hip_atomic_fetch_add(&hdr->ctl, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            s_gen = (uint32_t)(c >> 32);
+            s_ticket = (uint32_t)c;
+        } else {
+            s_gen = (uint32_t)(sp_load(&hdr->ctl) >> 32);
+            s_ticket = NT;
+        }
+        s_flag = 0;
+        s_ntiles = 0;
+    }
+    int32_t eid[SPT];
+    auto load_ids = [&](uint32_t t) {
+        const int64_t f0 = (int64_t)t * kTileSlots + (int64_t)w * kSlotsPerWave + lane;
+#pragma unroll
+        for (int it = 0; it < SPT; ++it) {
+            const int64_t f = f0 + it * kWave;
+            eid[it] = f < routed ? a.topk_ids[f] : -1;
+        }
+    };
+    if (worker) load_ids(blockIdx.x);
+    for (int e = tid; e < a.E; e += kLayoutThreads)
+        s_gof[e] = (uint16_t)((e / a.E_loc) * G + a.shared + (e % a.E_loc));
+    __syncthreads();
+    const uint32_t gen = s_gen;
+
+    uint32_t key[SPT], rnk[SPT];
+    int32_t agg[J], tgo[J];
+    int32_t flag = 0;
+    // Ranks of the tile's slots in their groups: wave w owns slots
+    // [w*64*SPT, (w+1)*64*SPT) of the tile, in SPT rounds of 64, so the
+    // stable order (ascending slot index) is wave, round, lane.  Leaves
+    // s_wcnt[w][g] = this wave's stage offset for group g (the tile's
+    // earlier groups, then earlier waves), agg = the tile's count per owned
+    // group, tgo = the tile's stage offset of each owned group, and the
+    // number of staged (valid) slots in s_nstage.
+    auto rank_tile = [&]() {
+#pragma unroll
+        for (int j = 0; j < J; ++j) {
+            const int g = tid * J + j;
+#pragma unroll
+            for (int w2 = 0; w2 < kLayoutWaves; ++w2)
+                if (g < NG) s_wcnt[w2][g] = 0;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int it = 0; it < SPT; ++it) {
+            const int32_t e = eid[it];
+            const uint32_t k = (uint32_t)e < (uint32_t)a.E ? (uint32_t)s_gof[e] : (uint32_t)NG;
+            if (e != -1 && (uint32_t)e >= (uint32_t)a.E) flag |= EP_FLAG_BAD_ID;  // -1 = masked slot
+            const uint64_t m = match_any(k, nbits);
+            const uint32_t r = lanes_below(m);
+            // only the lowest lane of each key touches LDS; the others take
+            // its value by a cross-lane read
+            int32_t before = 0;
+            if (k != (uint32_t)NG && r == 0) {
+                before = s_wcnt[w][k];
+                s_wcnt[w][k] = before + (int32_t)__popcll(m);
+            }
+            before = __shfl(before, (int)__builtin_ctzll(m), kWave);
+            rnk[it] = (uint32_t)before + r;
+            key[it] = k;
+        }
+        __syncthreads();
+        int32_t tsum = 0;
+#pragma unroll
+        for (int j = 0; j < J; ++j) {
+            const int g = tid * J + j;
+            int32_t run = 0;
+            if (g < NG) {
+#pragma unroll
+                for (int w2 = 0; w2 < kLayoutWaves; ++w2) {
+                    const int32_t c = s_wcnt[w2][g];
+                    s_wcnt[w2][g] = run;
+                    run += c;
+                }
+            }
+            agg[j] = run;
+            tgo[j] = tsum;
+            tsum += run;
+        }
+        // exclusive scan of the per-thread sums: stage offsets of the groups
+        int32_t incl = tsum;
+#pragma unroll
+        for (int o = 1; o < kWave; o <<= 1) {
+            const int32_t n = __shfl_up(incl, o, kWave);
+            if (lane >= o) incl += n;
+        }
+        if (lane == kWave - 1) s_wsum[w] = incl;
+        __syncthreads();
+        int32_t wb = 0, tot = 0;
+#pragma unroll
+        for (int w2 = 0; w2 < kLayoutWaves; ++w2) {
+            wb += w2 < w ? s_wsum[w2] : 0;
+            tot += s_wsum[w2];
+        }
+        const int32_t tbase = wb + incl - tsum;
+#pragma unroll
+        for (int j = 0; j < J; ++j) {
+            const int g = tid * J + j;
+            tgo[j] += tbase;
+            if (g < NG) {
+#pragma unroll
+                for (int w2 = 0; w2 < kLayoutWaves; ++w2) s_wcnt[w2][g] += tgo[j];
+            }
+        }
+        if (tid == 0) s_nstage = tot;
+        __syncthreads();
+    };
+
+    // ---- phase 1: tiles by ticket; publish aggregates (and, with the
+    // look-back, resolve and publish inclusive prefixes) ----
+    int32_t pref[J];
+    uint32_t t = s_ticket;
+    bool live = false;  // key/rnk/s_wcnt/agg/tgo hold the last tile taken
+    while (t < NT) {
+        if (t != blockIdx.x || live) load_ids(t);
+        rank_tile();
+        // The next ticket travels meanwhile (its value is stored only
+        // afterwards, so nothing waits for it here); a workgroup with a full
+        // tile list stops taking tickets.
+        uint32_t next_ticket = NT;
+        if (tid == 0) {
+            s_tiles[s_ntiles] = (int32_t)t;
+            s_ntiles += 1;
+            if (s_ntiles < kSpMaxTilesPerBlock)
+                next_ticket = (uint32_t)__hip_atomic_fetch_add(&hdr->ctl, 1ull, __ATOMIC_RELAXED,
+                                                               __HIP_MEMORY_SCOPE_AGENT);
+        }
+#pragma unroll
+        for (int j = 0; j < J; ++j) {
+            const int g = tid * J + j;
+            pref[j] = 0;
+            if (g < NG) {
+                const uint64_t aggd = ((uint64_t)gen << 32) | kDescAgg | (uint32_t)agg[j];
+                sp_store(&aggs[(int64_t)t * NG + g], aggd);
+                if (LOOKBACK) sp_store(&desc[(int64_t)t * NG + g], t == 0 ? aggd ^ (kDescAgg | kDescInc) : aggd);
+            }
+        }
+        if (LOOKBACK && t > 0) {
+#pragma unroll
+            for (int j = 0; j < J; ++j) {
+                const int g = tid * J + j;
+                if (g < NG) {
+                    pref[j] = sp_lookback<W>(desc, NG, g, t, gen, t_begin, flag);
+                    sp_store(&desc[(int64_t)t * NG + g],
+                             ((uint64_t)gen << 32) | kDescInc | (uint32_t)(pref[j] + agg[j]));
+                }
+            }
+        }
+        if (tid == 0) s_ticket = next_ticket;
+        live = true;
+        __syncthreads();
+        const uint32_t next = s_ticket;
+        if (next < NT) __syncthreads();  // s_wcnt is reused by the next tile
+        else break;
+        t = next;
+    }
+
+    // ---- phase 2: group totals (every tile has been handed to a running
+    // workgroup by now, so the waits end) ----
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+        const int g = tid * J + j;
+        if (g >= NG) continue;
+        int32_t tot;
+        if (LOOKBACK && live) {
+            tot = pref[j] + agg[j] + sp_sum<W>(aggs, NG, g, t + 1, NT, NT, nullptr, gen, t_begin, flag);
+        } else {
+            int32_t from_t = 0;  // tiles >= t
+            tot = sp_sum<W>(aggs, NG, g, 0, NT, live ? t : NT, &from_t, gen, t_begin, flag);
+            if (live) pref[j] = tot - from_t;
+        }
+        s_cnt[g] = tot + (g == shared_group ? a.T : 0);
+    }
+    __syncthreads();
+
+    // ---- aligned exclusive prefix over all groups (segment-major) ----
+    int32_t al[J];
+    int32_t asum = 0;
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+        const int g = tid * J + j;
+        al[j] = g < NG ? align_up(s_cnt[g], a.A) : 0;
+        asum += al[j];
+    }
+    int32_t aincl = asum;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+        const int32_t n = __shfl_up(aincl, o, kWave);
+        if (lane >= o) aincl += n;
+    }
+    if (lane == kWave - 1) s_wsum[w] = aincl;
+    __syncthreads();
+    int32_t awb = 0, total = 0;
+#pragma unroll
+    for (int w2 = 0; w2 < kLayoutWaves; ++w2) {
+        awb += w2 < w ? s_wsum[w2] : 0;
+        total += s_wsum[w2];
+    }
+    {
+        int32_t run = awb + aincl - asum;
+#pragma unroll
+        for (int j = 0; j < J; ++j) {
+            const int g = tid * J + j;
+            if (g < NG) s_start[g] = run;
+            run += al[j];
+        }
+    }
+    __syncthreads();
+    if (blockIdx.x == 0) {
+        for (int g = tid; g < NG; g += kLayoutThreads) a.out.counts[g] = s_cnt[g];
+        const int n = a.S * (G + 1);
+        for (int idx = tid; idx < n; idx += kLayoutThreads) {
+            const int s = idx / (G + 1), gl = idx - s * (G + 1);
+            const int gi = s * G + gl;
+            int32_t off = (gi < NG ? s_start[gi] : total) - s_start[s * G];
+            if (a.C > 0 && off > a.C) off = a.C;
+            a.out.row_offsets[idx] = off;
+            a.out.scales_offsets[idx] = off;
+        }
+        for (int s = tid; s <= a.S; s += kLayoutThreads)
+            a.out.seg_base[s] = a.C > 0 ? s * a.C : (s < a.S ? s_start[s * G] : total);
+    }
+    // absolute first row (clamped at capacity) and capacity limit per group;
+    // workgroup 0 derives the dropped / past-the-buffer bits from them: a
+    // group drops slots iff start + count passes its limit, and reaches
+    // past the buffer iff its used rows (pad included) end beyond R
+    const uint32_t R = (uint32_t)a.recv_rows;
+    int32_t st[J], li[J];
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+        const int g = tid * J + j;
+        st[j] = 0;
+        li[j] = 0;
+        if (g < NG) {
+            const int s = g / G;
+            const int32_t segp = s_start[s * G];
+            int32_t off = s_start[g] - segp;
+            if (a.C > 0) {
+                if (off > a.C) off = a.C;
+                st[j] = s * a.C + off;
+                li[j] = (s + 1) * a.C;
+            } else {
+                st[j] = segp + off;
+                li[j] = 0x7FFFFFFF;
+            }
+            if (blockIdx.x == 0) {
+                const uint32_t c = (uint32_t)s_cnt[g], s0 = (uint32_t)st[j], l0 = (uint32_t)li[j];
+                if (s0 + c > l0) flag |= EP_FLAG_DROPPED;
+                const uint32_t end = min(s0 + (uint32_t)align_up((int32_t)c, a.A), l0);
+                if (end > s0 && end > R) flag |= EP_FLAG_INTERNAL;
+            }
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+        const int g = tid * J + j;
+        if (g < NG) {
+            s_start[g] = st[j];
+            s_lim[g] = li[j];
+        }
+    }
+
+    // ---- flags and departure: one atomic add carries this workgroup's
+    // count and flag bits.  Its result is only looked at at the very end (by
+    // the last workgroup out), so nothing waits for it here; every ticket
+    // this workgroup took was returned before, so the reset below comes
+    // after every ticket of the call. ----
+    if (flag) atomicOr(&s_flag, flag);
+    __syncthreads();
+    uint64_t departed = 0;
+    const uint64_t mine = sp_departure(s_flag);
+    if (tid == 0) departed = __hip_atomic_fetch_add(&hdr->depart, mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+
+    // ---- phase 3: token_row and src_info of this workgroup's tiles ----
+    const int ntiles = worker ? s_ntiles : 0;
+    for (int q = ntiles - 1; q >= 0; --q) {
+        const uint32_t tt = (uint32_t)s_tiles[q];
+        if (q != ntiles - 1) {  // an earlier tile of this workgroup: rank it again
+            __syncthreads();
+            load_ids(tt);
+            rank_tile();
+#pragma unroll
+            for (int j = 0; j < J; ++j) {
+                const int g = tid * J + j;
+                pref[j] = 0;
+                if (g < NG) {
+                    if (LOOKBACK)  // its published inclusive prefix, less its aggregate
+                        pref[j] = sp_value(sp_load(&desc[(int64_t)tt * NG + g])) - agg[j];
+                    else           // every aggregate is published by now
+                        pref[j] = sp_sum<W>(aggs, NG, g, 0, tt, tt, nullptr, gen, t_begin, flag);
+                }
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < J; ++j) {
+            const int g = tid * J + j;
+            if (g < NG) s_base[g] = st[j] + pref[j] - tgo[j];
+        }
+        __syncthreads();
+        const int64_t f0 = (int64_t)tt * kTileSlots + (int64_t)w * kSlotsPerWave + lane;
+#pragma unroll
+        for (int it = 0; it < SPT; ++it) {
+            const int64_t f = f0 + it * kWave;
+            if (f >= routed) continue;
+            const uint32_t tk = (uint32_t)f / (uint32_t)a.K, k = (uint32_t)f - tk * (uint32_t)a.K;
+            int32_t* tr = &a.out.token_row[(int64_t)tk * a.Kp + k];
+            const uint32_t g = key[it];
+            if (g == (uint32_t)NG) {
+                *tr = -1;
+                continue;
+            }
+            const int32_t pos = s_wcnt[w][g] + (int32_t)rnk[it];
+            const uint32_t row = (uint32_t)(s_base[g] + pos);
+            const int32_t out = (row >= (uint32_t)s_lim[g] || row >= R) ? -1 : (int32_t)row;
+            *tr = out;
+            s_stage[pos] = make_int2(out, (int32_t)f);
+        }
+        __syncthreads();
+        const int32_t n = s_nstage;
+        for (int32_t i = tid; i < n; i += kLayoutThreads) {
+            const int2 e = s_stage[i];
+            if (e.x < 0) continue;
+            const uint32_t tk = (uint32_t)e.y / (uint32_t)a.K;
+            *reinterpret_cast<int2*>(&a.out.src_info[2 * (int64_t)e.x]) =
+                make_int2((int32_t)tk, e.y - (int32_t)(tk * (uint32_t)a.K));
+        }
+    }
+
+    // ---- the fused shared expert: token t is rank t of group 0 of src_seg ----
+    __syncthreads();
+    const int32_t nb = (int32_t)gridDim.x;
+    if (a.shared) {
+        const int32_t per = (a.T + nb - 1) / nb;
+        const int32_t t0 = (int32_t)blockIdx.x * per;
+        const int32_t t1 = min(a.T, t0 + per);
+        const uint32_t st0 = (uint32_t)s_start[shared_group], lim0 = (uint32_t)s_lim[shared_group];
+        for (int32_t tk = t0 + tid; tk < t1; tk += kLayoutThreads) {
+            int32_t* tr = &a.out.token_row[(int64_t)tk * a.Kp + a.K];
+            const uint32_t row = st0 + (uint32_t)tk;
+            if (row >= lim0 || row >= R) {
+                *tr = -1;
+            } else {
+                *tr = (int32_t)row;
+                *reinterpret_cast<int2*>(&a.out.src_info[2 * (int64_t)row]) = make_int2(tk, a.K);
+            }
+        }
+    }
+
+    // ---- expert_ids of every used row and pad-row src_info, by group ----
+    for (int g = (int)blockIdx.x; g < NG; g += nb) {
+        const int32_t c = s_cnt[g];
+        const int32_t n = align_up(c, a.A);
+        const int32_t gs = g / G, gl = g - gs * G;
+        const int32_t expert = (a.shared && gl == 0) ? a.E : gs * a.E_loc + (gl - a.shared);
+        for (int32_t r = tid; r < n; r += kLayoutThreads) {
+            const uint32_t row = (uint32_t)s_start[g] + (uint32_t)r;
+            if (row >= (uint32_t)s_lim[g] || row >= R) break;
+            const bool pad = r >= c;
+            a.out.expert_ids[row] = pad ? -1 : expert;
+            if (pad) *reinterpret_cast<int2*>(&a.out.src_info[2 * (int64_t)row]) = make_int2(-1, -1);
+        }
+    }
+
+    // ---- the last workgroup out writes the flags word and resets the
+    // header for the next call (no read of this call touches it later) ----
+    if (tid == 0 && (departed & 0xFFFFu) == gridDim.x - 1u) {
+        const uint64_t all = departed + mine;
+        a.out.flags[0] = sp_flags_of(all);
+        __hip_atomic_store(&hdr->depart, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        sp_store(&hdr->ctl, (uint64_t)(gen + 1u) << 32);
+    }
+}
+
+}  // namespace
 
 template <int SPT>
 void launch_spt(const LayoutArgs& a, hipStream_t stream) {
-    if (a.mode == kLayoutSmall)
-        hipLaunchKernelGGL((k_layout_rank<SPT, kLayoutSmall>), dim3((unsigned)a.rank_blocks), dim3(kLayoutThreads),
-                           0, stream, a);
-    else if (a.mode == kLayoutDirect)
-        launch_passes<SPT, true>(a, stream);
-    else
-        launch_passes<SPT, false>(a, stream);
+    const dim3 block(kLayoutThreads);
+    if (a.mode == kLayoutSmall) {
+        hipLaunchKernelGGL((k_layout_rank<SPT, kLayoutSmall>), dim3((unsigned)a.rank_blocks), block, 0, stream, a);
+    } else if (a.mode == kLayoutDirect) {
+        hipLaunchKernelGGL((k_layout_hist<SPT>), dim3((unsigned)a.tiles), block, 0, stream, a);
+        hipLaunchKernelGGL((k_layout_rank<SPT, kLayoutDirect>), dim3((unsigned)a.rank_blocks), block, 0, stream, a);
+    } else if (a.NG <= kLayoutThreads) {
+        if (a.lookback)
+            hipLaunchKernelGGL((k_layout_sp<SPT, kLayoutThreads, true>), dim3((unsigned)a.rank_blocks), block, 0,
+                               stream, a);
+        else
+            hipLaunchKernelGGL((k_layout_sp<SPT, kLayoutThreads, false>), dim3((unsigned)a.rank_blocks), block, 0,
+                               stream, a);
+    } else {
+        if (a.lookback)
+            hipLaunchKernelGGL((k_layout_sp<SPT, EP_MAX_GROUPS, true>), dim3((unsigned)a.rank_blocks), block, 0,
+                               stream, a);
+        else
+            hipLaunchKernelGGL((k_layout_sp<SPT, EP_MAX_GROUPS, false>), dim3((unsigned)a.rank_blocks), block, 0,
+                               stream, a);
+    }
 }
 
 hipError_t launch_layout(const LayoutArgs& a, hipStream_t stream) {

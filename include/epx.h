@@ -68,15 +68,19 @@ extern "C" {
 
 /* Bits of ep_cfg_t.flags. */
 #define EP_ZERO_PAD_ROWS 1u    /* also write zeros into the payload of pad rows */
-#define EP_LAYOUT_LOOKBACK 2u  /* ep_dispatch_layout: resolve tile prefixes by
-                                  decoupled look-back even where the direct
-                                  tile-count sums apply (same results; selects
-                                  the kernel path) */
+/* ep_dispatch_layout path selection: at most one of the next three bits;
+   every path gives the same results, they differ only in speed. */
+#define EP_LAYOUT_LOOKBACK 2u  /* one kernel: ticketed tiles, each tile's prefix
+                                  by decoupled look-back */
+#define EP_LAYOUT_DIRECT 4u    /* two kernels: tile-count table, then ranks */
+#define EP_LAYOUT_BARRIER 8u   /* one kernel: ticketed tiles, each tile's prefix
+                                  from one read of every tile's counts */
 
 /* Bits of the device flags word (ep_layout_t.flags[0]). */
 #define EP_FLAG_DROPPED 1      /* a slot was dropped at segment capacity [TD]  */
 #define EP_FLAG_BAD_ID 2       /* an expert id outside [-1, E) (slot masked)   */
-#define EP_FLAG_INTERNAL 4     /* the layout scan gave up waiting (never seen) */
+#define EP_FLAG_INTERNAL 4     /* a layout row past recv_rows, or a single-pass
+                                  wait gave up (neither happens in valid use) */
 #define EP_FLAG_MAP_OVERFLOW 8 /* a routing-map row marked more than top_k experts */
 
 /* Largest number of groups S * (E/S + shared_expert) a layout may have. */
@@ -111,7 +115,7 @@ typedef struct ep_cfg_t {
                               src_info, recv, codes, ...); R >= ep_query's
                               min_recv_rows and R < 2^31.  A host integer, so no
                               call ever reads a count back from the device [FA]. */
-    uint32_t flags;        /* EP_ZERO_PAD_ROWS | EP_LAYOUT_LOOKBACK, or 0         */
+    uint32_t flags;        /* EP_ZERO_PAD_ROWS, at most one EP_LAYOUT_* bit, or 0 */
     uint32_t reserved1;    /* must be 0                                           */
 } ep_cfg_t;
 
@@ -166,21 +170,26 @@ int ep_query(const ep_cfg_t* cfg, int64_t* min_recv_rows, int64_t* workspace_byt
  * routing-metadata preprocessing; [TD] dispatch_postprocess counts;
  * [MX] row_offsets, expert_ids, src_info).
  *   topk_ids   int32 [T*K], row-major; -1 = unused slot ([FA] topk_idx)
- *   workspace  >= workspace_bytes from ep_query, 16-byte aligned; its
- *              contents on entry do not matter and are clobbered
- *   layout     the arrays above, all written here
- * Steps: a per-tile wavefront ballot/popcount histogram, then one pass
- * that resolves each tile's in-group prefix, scans the aligned group sizes,
- * ranks every slot inside its group and writes token_row, expert_ids and
- * src_info.  The prefix over earlier tiles comes from one of three paths,
- * all with identical results:
- *  - up to 1024 routed slots (one tile): a single launch in which every
- *    workgroup ranks all slots itself;
- *  - up to 256 tiles: direct sums of a [tile][group] table of tile counts
- *    (two kernels);
- *  - otherwise, or when cfg->flags has EP_LAYOUT_LOOKBACK: a single-pass
- *    decoupled look-back over per-tile descriptors (three kernels: the
- *    counters are cleared first).
+ *   workspace  >= workspace_bytes from ep_query, 16-byte aligned, zero-filled
+ *              before its first use; every call leaves it ready for the
+ *              next one (reuse it: the single-pass kernels keep a generation
+ *              count and a ticket in it).  Not shared by calls that may run
+ *              at the same time.
+ *   layout     the arrays above, all written here (src_info 8-byte aligned)
+ * Steps: per tile of routed slots, a wavefront ballot/popcount histogram
+ * and in-group ranks (stable, ascending slot index); each tile's prefix
+ * over earlier tiles; the aligned group sizes scanned into group start rows;
+ * token_row, expert_ids and src_info written.  Paths (same results):
+ *  - up to 1024 routed slots: one kernel in which every workgroup ranks
+ *    all slots itself;
+ *  - otherwise up to 256 tiles (by default; EP_LAYOUT_DIRECT at any size):
+ *    two kernels, a [tile][group] count table then the ranks;
+ *  - beyond that (by default; EP_LAYOUT_LOOKBACK / EP_LAYOUT_BARRIER at any
+ *    size): one kernel, tiles taken from an atomic ticket, each tile's
+ *    prefix by decoupled look-back (or from one read of every tile's
+ *    counts), the group totals from every tile's published counts.
+ * Data errors go to layout->flags; a single-pass wait that cannot end gives
+ * up after about 0.3 s and sets EP_FLAG_INTERNAL.
  */
 int ep_dispatch_layout(const ep_cfg_t* cfg, const int32_t* topk_ids, void* workspace,
                        int64_t workspace_bytes, const ep_layout_t* layout, void* stream);

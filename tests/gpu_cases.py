@@ -50,14 +50,27 @@ def sentinel_layout(cfg: epx.EpConfig) -> epx.Layout:
     return epx.Layout(f(S, G), f(S + 1), f(S, G + 1), f(S, G + 1), f(T, cfg.kp), f(R), f(R, 2), f(1))
 
 
-def gpu_layout(cfg: epx.EpConfig, ids: np.ndarray, garbage_ws=True) -> epx.Layout:
-    lay = sentinel_layout(cfg)
-    ws = epx.workspace_for(cfg, DEV)
-    if garbage_ws:
-        ws.fill_(0xCD)  # the call must not depend on the workspace's contents
-    ids_t = torch.from_numpy(np.ascontiguousarray(ids, np.int32).reshape(-1)).to(DEV)
-    epx.ep_dispatch_layout(cfg, ids_t, ws, lay)
-    torch.cuda.synchronize()
+# The layout paths a test can force (cfg.flags bits); 0 = the default choice.
+LAYOUT_PATHS = {"single-pass": epx.EP_LAYOUT_LOOKBACK, "single-pass-barrier": epx.EP_LAYOUT_BARRIER,
+                "two-kernel": epx.EP_LAYOUT_DIRECT, "default": 0}
+PATH_FLAGS = epx.EP_LAYOUT_LOOKBACK | epx.EP_LAYOUT_DIRECT | epx.EP_LAYOUT_BARRIER
+
+
+def gpu_layout(cfg: epx.EpConfig, ids: np.ndarray, ws=None, path=None) -> epx.Layout:
+    """Layout into sentinel-filled arrays; a fresh zeroed workspace unless one
+    is given; `path` (a LAYOUT_PATHS key) overrides cfg's path bits."""
+    saved = cfg.flags
+    if path is not None:
+        cfg.flags = (saved & ~PATH_FLAGS) | LAYOUT_PATHS[path]
+    try:
+        lay = sentinel_layout(cfg)
+        if ws is None:
+            ws = epx.workspace_for(cfg, DEV)
+        ids_t = torch.from_numpy(np.ascontiguousarray(ids, np.int32).reshape(-1)).to(DEV)
+        epx.ep_dispatch_layout(cfg, ids_t, ws, lay)
+        torch.cuda.synchronize()
+    finally:
+        cfg.flags = saved
     return lay
 
 
@@ -189,14 +202,11 @@ def check_layout(c: Case, name: str) -> epx.Layout:
     say(f"[gpu] layout {name}: T={c.cfg.num_tokens} E={c.cfg.num_experts} S={c.cfg.num_segments} "
         f"K={c.cfg.top_k} A={c.cfg.align} C={c.cfg.seg_capacity} shared={c.cfg.shared_expert} "
         f"R={c.cfg.recv_rows}")
-    # Both prefix paths (direct tile-count sums, decoupled look-back) must
-    # give the oracle's layout; the direct (default) one is returned.
-    saved = c.cfg.flags
-    try:
-        c.cfg.flags = saved | epx.EP_LAYOUT_LOOKBACK
-        assert_layout_equal(layout_np(gpu_layout(c.cfg, c.ids)), c.L, name + " (look-back)")
-    finally:
-        c.cfg.flags = saved
+    # Every layout path (single pass, two kernels, and whichever the size
+    # selects by default) must give the oracle's layout; the default one is
+    # returned.
+    for path in ("single-pass", "single-pass-barrier", "two-kernel"):
+        assert_layout_equal(layout_np(gpu_layout(c.cfg, c.ids, path=path)), c.L, f"{name} ({path})")
     lay = gpu_layout(c.cfg, c.ids)
     assert_layout_equal(layout_np(lay), c.L, name)
     return lay

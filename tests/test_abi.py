@@ -34,6 +34,22 @@ def layout_tiles(routed, ng):
     return tiles_at(8)
 
 
+def sp_tiles(routed):
+    """Single-pass layout tiles: 256 x spt slots, spt the smallest of 1, 2,
+    4, 8 giving at most 32 tiles (else 8)."""
+    for spt in (1, 2, 4):
+        if routed <= 256 * spt * 32:
+            return max(1, -(-routed // (256 * spt)))
+    return max(1, -(-routed // (256 * 8)))
+
+
+def workspace_bytes(routed, ng):
+    """A 256-byte header, then the larger of the two paths' per-tile tables:
+    32-bit tile counts (two-kernel path) or two arrays of 64-bit descriptors
+    (single pass)."""
+    return 256 + max(layout_tiles(routed, ng) * ng * 4, sp_tiles(routed) * ng * 16)
+
+
 def test_layout_tiles_rule():
     # DeepSeek-V3 share (256 groups): one lane per group, 64 tiles per batch
     assert layout_tiles(4096 * 8, 256) == 64          # 2 slots per thread (1 would need 2 batches)
@@ -143,7 +159,7 @@ def test_query_sizes(L, orc):
         assert g == c.num_experts // c.num_segments + c.shared_expert
         routed = c.num_tokens * c.top_k
         ng = c.num_segments * g
-        assert ws == 256 + layout_tiles(routed, ng) * ng * 4
+        assert ws == workspace_bytes(routed, ng)
     # the bound is reached by some routing and never exceeded (oracle layout)
     rng = np.random.default_rng(0)
     c = cfg(num_tokens=9, num_experts=12, num_segments=3, top_k=3, align=5, shared_expert=1)
@@ -158,8 +174,13 @@ INVALID = [
     dict(num_tokens=-1), dict(hidden=0), dict(hidden=12), dict(num_experts=0), dict(num_segments=0),
     dict(num_experts=9), dict(top_k=0), dict(top_k=9), dict(align=0), dict(seg_capacity=-1),
     dict(shared_expert=2), dict(shared_expert=1, src_segment=2), dict(shared_expert=1, src_segment=-1),
-    dict(flags=4), dict(flags=8), dict(num_experts=4096, num_segments=2),  # > EP_MAX_GROUPS groups
+    dict(flags=6), dict(flags=7), dict(flags=10), dict(flags=12), dict(flags=14), dict(flags=16),
+    dict(num_experts=4096, num_segments=2),  # > EP_MAX_GROUPS groups
     dict(num_tokens=1 << 28, top_k=4),  # 2^30 slots
+    # capacity mode: the unclamped aligned offsets (summed in int32 before the
+    # clamp to C) would reach 2^31 although S * C is small
+    dict(num_tokens=4, num_experts=4, num_segments=1, top_k=4, align=1 << 30, seg_capacity=100),
+    dict(num_tokens=64, num_experts=8, num_segments=2, top_k=2, align=1 << 28, seg_capacity=1000),
 ]
 
 
@@ -168,12 +189,13 @@ def test_query_rejects_invalid_config(L, kw):
     assert query(L, cfg(**kw))[0] == -1
 
 
-@pytest.mark.parametrize("flags", [0, 1, 2, 3])
+@pytest.mark.parametrize("flags", [0, 1, 2, 3, 4, 5, 8, 9])
 def test_query_accepts_documented_flags(L, flags):
-    """EP_ZERO_PAD_ROWS (1) and EP_LAYOUT_LOOKBACK (2), alone or together."""
-    from combine_ep_dispatch_amd import EP_LAYOUT_LOOKBACK, EP_ZERO_PAD_ROWS
+    """EP_ZERO_PAD_ROWS (1) with at most one of the layout path bits
+    EP_LAYOUT_LOOKBACK (2), EP_LAYOUT_DIRECT (4), EP_LAYOUT_BARRIER (8)."""
+    from combine_ep_dispatch_amd import EP_LAYOUT_BARRIER, EP_LAYOUT_DIRECT, EP_LAYOUT_LOOKBACK, EP_ZERO_PAD_ROWS
 
-    assert (EP_ZERO_PAD_ROWS, EP_LAYOUT_LOOKBACK) == (1, 2)
+    assert (EP_ZERO_PAD_ROWS, EP_LAYOUT_LOOKBACK, EP_LAYOUT_DIRECT, EP_LAYOUT_BARRIER) == (1, 2, 4, 8)
     assert query(L, cfg(flags=flags))[0] == 0
 
 

@@ -73,8 +73,13 @@ def test_guards_and_determinism(G, case):
 
     def run_all():
         outs = {}
+        # the single-pass layout first, with its workspace between guards too
+        wsg = Guarded(G.epx.ep_query(cfg).workspace_bytes, torch.uint8)
+        wsg.view.zero_()
+        sp = G.gpu_layout(cfg, c.ids, ws=wsg.view, path="single-pass")
+        wsg.check("workspace")
+        G.assert_layout_equal(G.layout_np(sp), c.L, f"guards case {case} single-pass")
         ws = G.epx.workspace_for(cfg, G.DEV)
-        ws.fill_(0xCD)
         shapes = {"counts": (S, Gs), "seg_base": (S + 1,), "row_offsets": (S, Gs + 1),
                   "scales_offsets": (S, Gs + 1), "token_row": (T, cfg.kp), "expert_ids": (R,),
                   "src_info": (R, 2), "flags": (1,)}

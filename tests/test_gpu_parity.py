@@ -238,13 +238,46 @@ def test_fp8_special_rows(G):
     G.check_fp8(c, lay, "fp8_special")
 
 
-def test_determinism_and_garbage_workspace(G):
+def sp_header(ws):
+    """(generation, ticket, departure word) of a single-pass workspace."""
+    h = ws[:16].cpu().numpy().view(np.uint64)
+    return int(h[0]) >> 32, int(h[0]) & 0xFFFFFFFF, int(h[1])
+
+
+def test_single_pass_workspace_reuse(G):
+    """One zeroed workspace serves a sequence of single-pass layouts of
+    different shapes (more tiles, fewer, more groups, capacity drops, bad
+    ids): every call matches the oracle, and each leaves the header with the
+    ticket and the departure word reset and the generation one higher, so stale descriptors of earlier calls are never taken for
+    current ones."""
+    seq = [G.workload_case("dsv3"), G.random_case(5, T=300, S=2, E_loc=3, K=2, A=4),
+           G.workload_case("skewed", T=5000), G.random_case(6, T=2000, S=8, E_loc=256, K=6, A=1, shared=0),
+           G.workload_case("capacity", T=3000), G.random_case(7, T=4000, S=4, E_loc=8, K=4, bad_p=0.05),
+           G.workload_case("dsv3")]
+    nbytes = max(G.epx.ep_query(c.cfg).workspace_bytes for c in seq)
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device=G.DEV)
+    gen0 = sp_header(ws)[0]
+    for i, c in enumerate(seq + seq):
+        path = "single-pass" if i < len(seq) else "single-pass-barrier"
+        lay = G.gpu_layout(c.cfg, c.ids, ws=ws, path=path)
+        G.assert_layout_equal(G.layout_np(lay), c.L, f"reuse call {i} ({path})")
+        gen, ticket, depart = sp_header(ws)
+        assert (gen, ticket, depart) == (gen0 + i + 1, 0, 0), (i, gen, ticket, depart)
+    # two-kernel calls in between write tile counts into the same workspace:
+    # the next single-pass call must not take them for descriptors
     c = G.workload_case("skewed", T=3000)
-    a = G.layout_np(G.gpu_layout(c.cfg, c.ids, garbage_ws=True))
-    b = G.layout_np(G.gpu_layout(c.cfg, c.ids, garbage_ws=False))
-    for k in a:
-        assert np.array_equal(a[k], b[k]), k
-    G.assert_layout_equal(a, c.L, "skewed3000")
+    G.gpu_layout(c.cfg, c.ids, ws=ws, path="two-kernel")
+    G.assert_layout_equal(G.layout_np(G.gpu_layout(c.cfg, c.ids, ws=ws, path="single-pass")), c.L, "after 2k")
+
+
+def test_determinism(G):
+    c = G.workload_case("skewed", T=3000)
+    for path in G.LAYOUT_PATHS:
+        a = G.layout_np(G.gpu_layout(c.cfg, c.ids, path=path))
+        b = G.layout_np(G.gpu_layout(c.cfg, c.ids, path=path))
+        for k in a:
+            assert np.array_equal(a[k], b[k]), (path, k)
+        G.assert_layout_equal(a, c.L, f"skewed3000 {path}")
 
 
 def test_zero_pad_rows_flag(G):
