@@ -76,6 +76,8 @@ def _load():
             getattr(lib, name).argtypes = [P] * 5
         lib.orc_combine_bwd_probs.restype = None
         lib.orc_combine_bwd_probs.argtypes = [P] * 5
+        lib.orc_combine_nvfp4.restype = None
+        lib.orc_combine_nvfp4.argtypes = [P] * 7
         lib.orc_indices_to_multihot.restype = None
         lib.orc_indices_to_multihot.argtypes = [P] * 5
         lib.orc_multihot_to_indices.restype = ctypes.c_int32
@@ -253,6 +255,21 @@ def combine(cfg: Cfg, token_row: np.ndarray, out: np.ndarray, probs: Optional[np
     oo = np.ascontiguousarray(out, np.uint16)
     pp = None if probs is None else np.ascontiguousarray(probs, np.float32)
     lib.orc_combine(ctypes.byref(cfg._c()), _ptr(tr), _ptr(oo), _ptr(pp), _ptr(y))
+    return y
+
+
+def combine_nvfp4(cfg: Cfg, token_row: np.ndarray, codes: np.ndarray, scales: np.ndarray,
+                  rowscale: np.ndarray, probs: Optional[np.ndarray]) -> np.ndarray:
+    """Combine over NVFP4 expert-output rows (codes [R, H/2], E4M3 scales
+    [R, H/16], bf16 rowscale bits [R]) -> y bf16 bits [T, H]."""
+    lib = _load()
+    y = np.full((cfg.T, cfg.H), SENTINEL_U16, np.uint16)
+    tr = np.ascontiguousarray(token_row, np.int32)
+    cc = np.ascontiguousarray(codes, np.uint8)
+    ss = np.ascontiguousarray(scales, np.uint8)
+    rs = np.ascontiguousarray(rowscale, np.uint16)
+    pp = None if probs is None else np.ascontiguousarray(probs, np.float32)
+    lib.orc_combine_nvfp4(ctypes.byref(cfg._c()), _ptr(tr), _ptr(cc), _ptr(ss), _ptr(rs), _ptr(pp), _ptr(y))
     return y
 
 

@@ -363,6 +363,45 @@ void orc_combine_bwd_probs(const orc_cfg* c, const int32_t* token_row, const uin
 }
 
 /* ------------------------------------------------------------------ */
+/* Combine over NVFP4 expert outputs                                   */
+/* ------------------------------------------------------------------ */
+
+/* Combine whose expert outputs arrive as NVFP4 rows: codes [rows, H/2]
+ * (element 2j in the low nibble of byte j), E4M3 block scales [rows, H/16]
+ * and a bf16 rowscale per row, the layout the MAX
+ * DistributedEPDispatchBlockScaledNVDynGlobalScales page's execute
+ * produces (output_scales, output_rowwise_scales: the BF16 inverse of the
+ * per-token global scale).  Element h of row r dequantizes as
+ *     xhat = e2m1(code) * (e4m3(scale[h/16]) * float(rowscale))
+ * (reading: the block's combined scale first, then the element, each an
+ * IEEE fp32 multiply rounded to nearest-even; both products are exact
+ * unless they fall below the fp32 normal range), and combine sums
+ * w_k * xhat over the kept slots in ascending k in fp32, exactly as
+ * orc_combine does with bf16 rows. */
+void orc_combine_nvfp4(const orc_cfg* c, const int32_t* token_row, const uint8_t* codes,
+                       const uint8_t* scales, const uint16_t* rowscale, const float* probs, uint16_t* y)
+{
+    const int32_t Kp = c->K + c->shared, H = c->H;
+    for (int32_t t = 0; t < c->T; ++t)
+        for (int32_t h = 0; h < H; ++h) {
+            float acc = 0.0f;
+            for (int32_t k = 0; k < Kp; ++k) {
+                int32_t row = token_row[(int64_t)t * Kp + k];
+                if (row < 0) continue;
+                float w = slot_weight(c, probs, t, k);
+                uint8_t byte = codes[(int64_t)row * (H / 2) + h / 2];
+                uint8_t code = (h % 2 == 0) ? (uint8_t)(byte & 0x0F) : (uint8_t)(byte >> 4);
+                float block_scale = orc_e4m3_decode(scales[(int64_t)row * (H / 16) + h / 16]) *
+                                    orc_bf16_to_f32(rowscale[row]);
+                float xhat = orc_e2m1_decode(code) * block_scale;
+                float prod = w * xhat;
+                acc = acc + prod;
+            }
+            y[(int64_t)t * H + h] = orc_bf16_rne(acc);
+        }
+}
+
+/* ------------------------------------------------------------------ */
 /* Compact top-k <-> dense routing map                                  */
 /* ------------------------------------------------------------------ */
 

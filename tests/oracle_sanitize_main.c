@@ -20,6 +20,8 @@ void orc_combine(const orc_cfg*, const int32_t*, const uint16_t*, const float*, 
 void orc_dispatch_bwd(const orc_cfg*, const int32_t*, const uint16_t*, uint16_t*);
 void orc_combine_bwd(const orc_cfg*, const int32_t*, const uint16_t*, const float*, uint16_t*);
 void orc_combine_bwd_probs(const orc_cfg*, const int32_t*, const uint16_t*, const uint16_t*, double*);
+void orc_combine_nvfp4(const orc_cfg*, const int32_t*, const uint8_t*, const uint8_t*, const uint16_t*,
+                       const float*, uint16_t*);
 void orc_indices_to_multihot(const orc_cfg*, const int32_t*, const float*, uint8_t*, float*);
 int32_t orc_multihot_to_indices(const orc_cfg*, const uint8_t*, const float*, int32_t*, float*);
 
@@ -67,6 +69,10 @@ static void run(orc_cfg c)
         uint8_t *codes = calloc((size_t)(R * c.H / 2 + 1), 1), *sc = calloc((size_t)(R * c.H / 16 + 1), 1);
         uint16_t* rs = calloc((size_t)(R + 1), 2);
         orc_dispatch_nvfp4(&c, tr, x, codes, sc, rs);
+        uint16_t* yq = malloc(sizeof(uint16_t) * (size_t)(c.T * c.H + 1));
+        orc_combine_nvfp4(&c, tr, codes, sc, rs, probs, yq);
+        orc_combine_nvfp4(&c, tr, codes, sc, rs, NULL, yq);
+        free(yq);
         free(codes);
         free(sc);
         free(rs);

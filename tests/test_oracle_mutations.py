@@ -20,7 +20,7 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 PINS = ["tests/test_oracle_formats.py", "tests/test_oracle_layout.py",
         "tests/test_oracle_payload.py", "tests/test_oracle_nvfp4.py", "tests/test_oracle_fp8.py",
-        "tests/test_oracle_routing_map.py"]
+        "tests/test_oracle_routing_map.py", "tests/test_oracle_combine_nvfp4.py"]
 
 MUTANTS = {
     "global_scale_448": ("2688.0f / rowmax", "448.0f / rowmax"),
@@ -66,6 +66,16 @@ MUTANTS = {
     "map_overflow_unflagged": ("                flags |= 8;\n", ""),
     "bf16_truncates": ("if (rem > 0x8000u) return (uint16_t)(lo + 1);",
                        "if (rem > 0x8000u) return (uint16_t)(lo);"),
+    "nvfp4_combine_nibble_order": ("(h % 2 == 0) ? (uint8_t)(byte & 0x0F) : (uint8_t)(byte >> 4)",
+                                   "(h % 2 == 1) ? (uint8_t)(byte & 0x0F) : (uint8_t)(byte >> 4)"),
+    "nvfp4_combine_no_rowscale": ("float block_scale = orc_e4m3_decode(scales[(int64_t)row * (H / 16) + h / 16]) *\n"
+                                  "                                    orc_bf16_to_f32(rowscale[row]);",
+                                  "float block_scale = orc_e4m3_decode(scales[(int64_t)row * (H / 16) + h / 16]);"),
+    "nvfp4_combine_scale_index": ("scales[(int64_t)row * (H / 16) + h / 16]", "scales[(int64_t)row * (H / 16) + h / 8]"),
+    "nvfp4_combine_unweighted": ("float w = slot_weight(c, probs, t, k);\n                uint8_t byte",
+                                 "float w = 1.0f;\n                uint8_t byte"),
+    "nvfp4_combine_sign_dropped": ("float xhat = orc_e2m1_decode(code) * block_scale;",
+                                   "float xhat = orc_e2m1_decode(code & 7) * block_scale;"),
 }
 
 
