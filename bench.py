@@ -110,6 +110,7 @@ def algorithmic_bytes(w, kept: int, used_rows: int, kept_routed: int = None) -> 
         "layout_two_kernel": 4 * T * K + 4 * T * Kp + 12 * used_rows,
         "combine_bwd_probs": row * T + row * kept_routed + 4 * T * Kp + 4 * T * K,
         "dispatch_fp8": row * T + kept * (H + 4 * (H // 128)) + 4 * T * Kp,
+        "combine_nvfp4": kept * (H // 2 + H // 16 + 2) + row * T + 4 * T * K + 4 * T * Kp,
     }
 
 
@@ -228,9 +229,12 @@ def main() -> int:
     path_lay = {n: epx.Layout.empty(c, dev) for n, c in paths.items()}
     path_ws = {n: epx.workspace_for(c, dev) for n, c in paths.items()}
     extra_ops = [(n, (lambda n=n: epx.ep_dispatch_layout(paths[n], ids, path_ws[n], path_lay[n]))) for n in paths]
-    extra_ops += [
-                 ("combine_bwd_probs", lambda: epx.ep_combine_bwd_probs(cfg, lay, gy, out, gprobs)),
-                 ("dispatch_fp8", lambda: epx.ep_dispatch_fp8(cfg, lay, x, fp8_codes, fp8_scales))]
+    # combine over NVFP4 rows: the step's own NVFP4 dispatch output stands in
+    # for NVFP4 expert outputs (same format and size)
+    cq_y = torch.empty(T * H, dtype=torch.bfloat16, device=dev)
+    extra_ops += [("combine_bwd_probs", lambda: epx.ep_combine_bwd_probs(cfg, lay, gy, out, gprobs)),
+                  ("dispatch_fp8", lambda: epx.ep_dispatch_fp8(cfg, lay, x, fp8_codes, fp8_scales)),
+                  ("combine_nvfp4", lambda: epx.ep_combine_nvfp4(cfg, lay, codes, scales, rowscale, probs, cq_y))]
 
     def step():
         for _, fn in ops:
@@ -494,7 +498,10 @@ def latency_sweep(torch, epx, wl, dev, workload: str, token_counts) -> int:
         paths = {n: dataclasses.replace(cfg, flags=cfg.flags | f) for n, f in LAYOUT_PATHS.items()}
         path_lay = {n: epx.Layout.empty(c, dev) for n, c in paths.items()}
         path_ws = {n: epx.workspace_for(c, dev) for n, c in paths.items()}
-        ops = step_ops + [("dispatch_fp8", lambda: epx.ep_dispatch_fp8(cfg, lay, x, f8c, f8s))]
+        cq_y = torch.empty(T * H, dtype=torch.bfloat16, device=dev)
+        ops = step_ops + [("dispatch_fp8", lambda: epx.ep_dispatch_fp8(cfg, lay, x, f8c, f8s)),
+                          ("combine_nvfp4", lambda: epx.ep_combine_nvfp4(cfg, lay, codes, scales, rowscale, probs,
+                                                                         cq_y))]
         ops += [(n, (lambda n=n: epx.ep_dispatch_layout(paths[n], ids, path_ws[n], path_lay[n]))) for n in paths]
         ops += [("step", lambda: [fn() for _, fn in step_ops])]
         step_ops[0][1]()

@@ -33,7 +33,7 @@ from ._lib import (EP_FLAG_BAD_ID, EP_FLAG_DROPPED, EP_FLAG_INTERNAL, EP_FLAG_MA
 
 __all__ = [
     "EpConfig", "Layout", "QueryResult", "ep_query", "workspace_for", "ep_dispatch_layout",
-    "ep_dispatch_layout_noalloc", "EP_NOALLOC_SCRATCH_BYTES",
+    "ep_dispatch_layout_noalloc", "EP_NOALLOC_SCRATCH_BYTES", "ep_combine_nvfp4",
     "ep_dispatch", "ep_dispatch_nvfp4", "ep_dispatch_fp8", "ep_combine", "ep_dispatch_bwd", "ep_combine_bwd",
     "ep_combine_bwd_probs", "ep_indices_to_multihot", "ep_multihot_to_indices", "assert_no_overflow", "EpError", "abi_version", "EP_ZERO_PAD_ROWS", "EP_LAYOUT_LOOKBACK", "EP_LAYOUT_DIRECT", "EP_LAYOUT_BARRIER", "EP_FLAG_DROPPED",
     "EP_FLAG_BAD_ID", "EP_FLAG_INTERNAL",
@@ -240,6 +240,25 @@ def ep_combine(cfg: EpConfig, layout: Layout, expert_out: torch.Tensor, probs: O
     _check(_lib.lib().ep_combine(ctypes.byref(c), ctypes.byref(L), expert_out.data_ptr(),
                                  None if probs is None else probs.data_ptr(), y.data_ptr(),
                                  _stream(stream, dev)), "ep_combine")
+
+
+def ep_combine_nvfp4(cfg: EpConfig, layout: Layout, codes: torch.Tensor, scales: torch.Tensor,
+                     rowscale: torch.Tensor, probs: Optional[torch.Tensor], y: torch.Tensor, stream=None) -> None:
+    """Combine over NVFP4 expert-output rows: codes uint8 [R, H/2], E4M3
+    scales uint8 [R, H/16], rowscale bf16 [R] -> y bf16 [T, H]."""
+    dev = codes.device
+    T, H, R = cfg.num_tokens, cfg.hidden, cfg.recv_rows
+    _tensor(codes, "codes", torch.uint8, R * (H // 2))
+    _tensor(scales, "scales", torch.uint8, R * (H // 16), dev)
+    _tensor(rowscale, "rowscale", torch.bfloat16, R, dev)
+    if probs is not None:
+        _tensor(probs, "probs", torch.float32, T * cfg.top_k, dev)
+    _tensor(y, "y", torch.bfloat16, T * H, dev)
+    layout.check(cfg, dev)
+    c, L = cfg.to_c(), layout.to_c()
+    _check(_lib.lib().ep_combine_nvfp4(ctypes.byref(c), ctypes.byref(L), codes.data_ptr(), scales.data_ptr(),
+                                       rowscale.data_ptr(), None if probs is None else probs.data_ptr(),
+                                       y.data_ptr(), _stream(stream, dev)), "ep_combine_nvfp4")
 
 
 def ep_dispatch_bwd(cfg: EpConfig, layout: Layout, grad_recv: torch.Tensor, grad_x: torch.Tensor,

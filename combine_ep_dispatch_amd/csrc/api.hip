@@ -372,6 +372,34 @@ int ep_combine(const ep_cfg_t* cfg, const ep_layout_t* layout, const uint16_t* e
     return status_of(launch_gather_reduce(move_args(d, layout, expert_out, y, probs), static_cast<hipStream_t>(stream)));
 }
 
+int ep_combine_nvfp4(const ep_cfg_t* cfg, const ep_layout_t* layout, const uint8_t* codes, const uint8_t* scales,
+                     const uint16_t* rowscale, const float* probs, uint16_t* y, void* stream) {
+    Shape d;
+    int rc = derive(cfg, &d);
+    if (rc != EP_OK) return rc;
+    if ((rc = check_rows(d)) != EP_OK) return rc;
+    if (d.H % 16 != 0 || grid_too_big(d, (int64_t)kWave * combine_nvfp4_pieces(d.H))) return EP_EINVAL;
+    if (layout == nullptr || bad_buffer(layout->token_row, (int64_t)d.T * d.Kp * 4, 4)) return EP_EINVAL;
+    if (bad_buffer(codes, d.R * (d.H / 2), 8) || bad_buffer(scales, d.R * (d.H / 16), 1) ||
+        bad_buffer(rowscale, d.R * 2, 2) || bad_buffer(y, (int64_t)d.T * d.H * 2, 16))
+        return EP_EINVAL;
+    if (probs != nullptr && misaligned(probs, 4)) return EP_EINVAL;
+    if ((rc = check_device()) != EP_OK) return rc;
+    CombineNvfp4Args a;
+    a.codes = codes;
+    a.scales = scales;
+    a.rowscale = rowscale;
+    a.token_row = layout->token_row;
+    a.probs = probs;
+    a.y = y;
+    a.T = d.T;
+    a.K = d.K;
+    a.Kp = d.Kp;
+    a.H = d.H;
+    a.R = d.R;
+    return status_of(launch_combine_nvfp4(a, static_cast<hipStream_t>(stream)));
+}
+
 int ep_dispatch_bwd(const ep_cfg_t* cfg, const ep_layout_t* layout, const uint16_t* grad_recv, uint16_t* grad_x,
                     void* stream) {
     Shape d;

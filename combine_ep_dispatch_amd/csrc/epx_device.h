@@ -114,9 +114,9 @@ __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w 
 
 // float -> bf16 bits, round to nearest-even; NaN keeps sign and payload top
 // bits and is made quiet (bit 6 of the bf16 set).  This is gfx950's
-// v_cvt_pk_bf16_f32, two values per instruction: over all 2^32 float
-// patterns it equals (u + 0x7FFF + ((u >> 16) & 1)) >> 16 for non-NaN u and
-// (u >> 16) | 0x40 for NaN, denormals included.
+// v_cvt_pk_bf16_f32, two values per instruction: on all 2^32 float
+// patterns it equals bf16_rne_bits below, denormals and NaN included
+// (tests/test_gpu_conversions.py).
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
@@ -146,6 +146,44 @@ __device__ __forceinline__ float e4m3_decode(uint32_t c) {
     const uint32_t e = c >> 3, m = c & 7u;
     if (e == 0u) return (float)m * 0.001953125f;  // m * 2^-9, exact
     return __uint_as_float(((e + 120u) << 23) | (m << 20));
+}
+
+// Signed E4M3 encode: RNE, saturating to +-448, sign bit of v kept (-0 and
+// tiny negatives give 0x80).  Finite v only.
+__device__ __forceinline__ uint32_t e4m3_signed(float v) {
+    return e4m3_encode(__builtin_fabsf(v)) | ((__float_as_uint(v) >> 24) & 0x80u);
+}
+
+// E4M3 code with its sign bit -> value (finite codes).
+__device__ __forceinline__ float e4m3_decode_signed(uint32_t c) {
+    return __uint_as_float(__float_as_uint(e4m3_decode(c & 0x7Fu)) | ((c & 0x80u) << 24));
+}
+
+// v -> E2M1 code (OCP MX: magnitudes 0, .5, 1, 1.5, 2, 3, 4, 6).  The
+// thresholds are the midpoints between magnitudes; at a midpoint the even
+// code wins (the comparison is strict toward the odd neighbour); past 5
+// it saturates at 6; the sign bit of v is kept.
+__device__ __forceinline__ uint32_t e2m1_encode(float v) {
+    const float a = __builtin_fabsf(v);
+    uint32_t c = (a > 0.25f) + (a >= 0.75f) + (a > 1.25f) + (a >= 1.75f) + (a > 2.5f) + (a >= 3.5f) +
+                 (a > 5.0f);
+    return c | ((__float_as_uint(v) >> 28) & 8u);
+}
+
+// E2M1 code -> value, from its bit fields: exponent e = bits 2..1 (bias 1),
+// mantissa m = bit 0; e = 0 is subnormal (m * 0.5).
+__device__ __forceinline__ float e2m1_decode(uint32_t c) {
+    const uint32_t e = (c >> 1) & 3u, m = c & 1u;
+    const uint32_t mag = e == 0u ? (m ? 0x3F000000u : 0u) : (((e + 126u) << 23) | (m << 22));
+    return __uint_as_float(mag | ((c & 8u) << 28));
+}
+
+// float -> bf16 bits by the bit formula: round to nearest-even on the
+// dropped 16 bits; NaN keeps sign and payload top bits and is made quiet.
+__device__ __forceinline__ uint32_t bf16_rne_bits(float f) {
+    const uint32_t u = __float_as_uint(f);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (u >> 16) | 0x40u;
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
 // Count of set bits of `m` in lanes below this one (the in-wave rank).
@@ -227,6 +265,19 @@ struct Fp8Args {
 };
 hipError_t launch_fp8(const Fp8Args& a, hipStream_t stream);
 int fp8_max_hidden();
+
+struct CombineNvfp4Args {
+    const uint8_t* codes;      // [R, H/2]
+    const uint8_t* scales;     // [R, H/16]
+    const uint16_t* rowscale;  // [R] bf16 bits
+    const int32_t* token_row;  // [T, K']
+    const float* probs;        // [T, K] or nullptr: weight 1
+    uint16_t* y;               // [T, H] bf16 bits
+    int32_t T, K, Kp, H;
+    int64_t R;                 // receive rows; a token_row entry outside [0, R) is skipped
+};
+hipError_t launch_combine_nvfp4(const CombineNvfp4Args& a, hipStream_t stream);
+int combine_nvfp4_pieces(int32_t H);
 
 struct RouteArgs {
     int32_t* ids;         // [T, K]

@@ -29,9 +29,10 @@
 // inside the 8-lane group.
 // IEEE division and no contraction keep the result bit-identical to the
 // plain definition.  The encode is gfx950's v_cvt_pk_fp8_f32 (OCP E4M3,
-// RNE), two elements per instruction: for |v| <= 464 it equals the RNE,
-// saturating, sign-kept encode (checked over all 2^32 float patterns), and
-// here |v| <= 448 up to one rounding.  Past 464 it gives the NaN code, so a
+// RNE), two elements per instruction: for |v| <= 464 it equals e4m3_signed,
+// the RNE, saturating, sign-kept encode (tests/test_gpu_conversions.py runs
+// both over all 2^32 float patterns), and here |v| <= 448 up to one
+// rounding.  Past 464 it gives the NaN code, so a
 // block whose factor 448 / amax overflowed (amax below 448/FLT_MAX) takes
 // the software encoder instead.
 #include "epx_device.h"
@@ -46,10 +47,6 @@ constexpr int kFp8MaxIters = 16;  // H <= 1024 * 16
 #define EPX_FP8_SMALL_BATCH 4096
 #endif
 constexpr int kSmallBatchTokens = EPX_FP8_SMALL_BATCH;  // below this, 4 waves per token
-
-__device__ __forceinline__ uint32_t e4m3_signed(float v) {
-    return e4m3_encode(__builtin_fabsf(v)) | ((__float_as_uint(v) >> 24) & 0x80u);
-}
 
 __device__ __forceinline__ uint32_t absmax16(const uint4& p, const uint4& q) {
     const uint32_t w[8] = {p.x, p.y, p.z, p.w, q.x, q.y, q.z, q.w};

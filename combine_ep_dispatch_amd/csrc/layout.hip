@@ -537,9 +537,11 @@ __device__ __forceinline__ int32_t sp_sum(const uint64_t* src, int NG, int g, ui
                 break;
             }
             __builtin_amdgcn_s_sleep(1);
-#pragma unroll
-            for (int i = 0; i < W; ++i)
-                if (!sp_published(d[i], gen)) d[i] = sp_load(&src[(int64_t)(u + i) * NG + g]);
+            // the whole window again; published entries are kept
+            for (int i = 0; i < W; ++i) {
+                const uint64_t n = u + i < hi ? sp_load(&src[(int64_t)(u + i) * NG + g]) : zero;
+                d[i] = sp_published(d[i], gen) ? d[i] : n;
+            }
         }
 #pragma unroll
         for (int i = 0; i < W; ++i) {
@@ -772,7 +774,6 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout_sp(LayoutArgs a) {
             }
         }
         if (LOOKBACK && t > 0) {
-#pragma unroll
             for (int j = 0; j < J; ++j) {
                 const int g = tid * J + j;
                 if (g < NG) {
@@ -793,7 +794,6 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout_sp(LayoutArgs a) {
 
     // ---- phase 2: group totals (every tile has been handed to a running
     // workgroup by now, so the waits end) ----
-#pragma unroll
     for (int j = 0; j < J; ++j) {
         const int g = tid * J + j;
         if (g >= NG) continue;
@@ -916,7 +916,6 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout_sp(LayoutArgs a) {
             __syncthreads();
             load_ids(tt);
             rank_tile();
-#pragma unroll
             for (int j = 0; j < J; ++j) {
                 const int g = tid * J + j;
                 pref[j] = 0;

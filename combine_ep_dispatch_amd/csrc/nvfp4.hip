@@ -23,9 +23,11 @@
 // library is built with correctly rounded division and without FMA
 // contraction, so the results are bit-identical to the plain definition.
 // The E2M1 encode is gfx950's v_cvt_scalef32_pk_fp4_f32 with scale 1, two
-// elements per instruction: on every finite and infinite input it is the
-// RNE, ties-to-even, saturating, sign-kept encode below (checked over all
-// 2^32 float patterns).  It turns NaN into code 7, so a block whose
+// elements per instruction: on every finite and infinite input it equals
+// e2m1_encode, the RNE, ties-to-even, saturating, sign-kept encode
+// (tests/test_gpu_conversions.py runs both over all 2^32 float patterns,
+// and e2m1_encode against the oracle at every rounding boundary).  It
+// differs only on NaN, so a block whose
 // per-element factor g / e4m3(s) overflowed (a row max below 2688/FLT_MAX,
 // where 0 * inf can occur) takes the threshold encoder instead:
 //   s = (bmax / 6) * g            -> E4M3, RNE, saturating to 448
@@ -45,16 +47,6 @@ constexpr int kMaxBlocksPerLane = 16;  // H <= 16 * 64 * 16 = 16384
 #define EPX_NVFP4_SMALL_BATCH 4096
 #endif
 constexpr int kSmallBatchTokens = EPX_NVFP4_SMALL_BATCH;  // below this, 4 waves per token
-
-// v -> E2M1 code.  Thresholds are the midpoints between the magnitudes
-// {0, .5, 1, 1.5, 2, 3, 4, 6}; at a midpoint the even code wins (the
-// comparison is strict toward the odd neighbour).
-__device__ __forceinline__ uint32_t e2m1_encode(float v) {
-    const float a = __builtin_fabsf(v);
-    uint32_t c = (a > 0.25f) + (a >= 0.75f) + (a > 1.25f) + (a >= 1.75f) + (a > 2.5f) + (a >= 3.5f) +
-                 (a > 5.0f);
-    return c | ((__float_as_uint(v) >> 28) & 8u);
-}
 
 __device__ __forceinline__ uint32_t absmax_bf16x2(uint32_t acc, uint32_t w) {
     const uint32_t lo = w & 0x7FFFu, hi = (w >> 16) & 0x7FFFu;

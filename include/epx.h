@@ -256,6 +256,26 @@ int ep_combine(const ep_cfg_t* cfg, const ep_layout_t* layout, const uint16_t* e
                const float* probs, uint16_t* y, void* stream);
 
 /*
+ * Combine over NVFP4 expert-output rows ([MX] execute: the NVFP4 row format,
+ * output_scales, output_rowwise_scales; [TD] moe_router_dtype fp32): the
+ * expert outputs come back in the dispatch's NVFP4 format and are
+ * dequantized as they are read:
+ *   xhat = e2m1(code) * (e4m3(scale[h/16]) * float(rowscale[row]))
+ *   y[t, h] = bf16_rne( sum_{k, token_row[t,k] >= 0} w_k * xhat(token_row[t,k], h) )
+ * each product an fp32 multiply, accumulated in fp32 in ascending k from +0
+ * with no fused multiply-add; w_k as in ep_combine.
+ *   codes     uint8 [R, H/2]   element 2j in the low nibble of byte j (8-byte aligned)
+ *   scales    uint8 [R, H/16]  E4M3 block scales, sign bit decoded; the NaN
+ *                              codes 0x7F / 0xFF are outside the contract
+ *   rowscale  bf16  [R]
+ *   probs     float [T, K] or NULL;  y  bf16 [T, H]  (H % 16 == 0)
+ * Pad and dropped rows are never read.  Returns EP_EINVAL past one grid:
+ * T * ceil(H/1024) waves of 64 work-items must stay below 2^32.
+ */
+int ep_combine_nvfp4(const ep_cfg_t* cfg, const ep_layout_t* layout, const uint8_t* codes, const uint8_t* scales,
+                     const uint16_t* rowscale, const float* probs, uint16_t* y, void* stream);
+
+/*
  * Dispatch backward ([FA] HybridEPDispatch.backward: combine the
  * gradients): grad_x[t] = bf16_rne( sum_k float(grad_recv[token_row[t,k]]) ),
  * fp32, ascending k, unweighted (dispatch is a copy); 0 if no slot is kept.

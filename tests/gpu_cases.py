@@ -328,3 +328,41 @@ def check_fp8(c: Case, lay: epx.Layout, name: str, x=None):
     wc, wsc = orc.dispatch_fp8(c.oc, c.L["token_row"], x)
     assert_bits_equal(codes.cpu().numpy(), wc, f"{name}: fp8 codes")
     assert_bits_equal(scales.view(torch.int32).cpu().numpy(), wsc.view(np.int32), f"{name}: fp8 scales")
+
+
+def nvfp4_rows(c: Case, seed_offset: int):
+    """Stand-in NVFP4 expert outputs for every receive row: random codes,
+    E4M3 scales (some negative) and bf16 rowscales over 2^-40..2^40.  Rows no
+    kept slot uses are poisoned (codes 0x77, scale 0x7E, rowscale 2^100), so
+    a read of them shows up in the result."""
+    rng = np.random.default_rng(c.seed * 1000 + seed_offset)
+    R, H = c.cfg.recv_rows, c.cfg.hidden
+    codes = rng.integers(0, 256, (R, H // 2), dtype=np.uint8)
+    scales = rng.integers(0, 0x7F, (R, H // 16), dtype=np.uint8)
+    scales[rng.random((R, H // 16)) < 0.05] |= 0x80
+    rs = wl.bf16_bits(np.exp2(rng.uniform(-40, 40, R)).astype(np.float32))
+    used = np.zeros(R, bool)
+    tr = c.L["token_row"]
+    used[tr[tr >= 0]] = True
+    codes[~used] = 0x77
+    scales[~used] = 0x7E
+    rs[~used] = wl.bf16_bits(np.array([2.0 ** 100], np.float32))[0]
+    return codes, scales, rs
+
+
+def check_combine_nvfp4(c: Case, lay: epx.Layout, name: str, weighted=True, rows=None):
+    """ep_combine_nvfp4 against the oracle, bit for bit (same op order, no
+    contraction); `rows` = (codes, scales, rowscale bits), random by default."""
+    say(f"[gpu] combine_nvfp4 {name}: weighted={weighted}")
+    cfg = c.cfg
+    codes, scales, rs = nvfp4_rows(c, 4) if rows is None else rows
+    probs = c.probs if weighted else None
+    y = bf16_filled(cfg.num_tokens, cfg.hidden, orc.SENTINEL_U16)
+    pt = None if probs is None else torch.from_numpy(probs.reshape(-1)).to(DEV)
+    epx.ep_combine_nvfp4(cfg, lay, torch.from_numpy(codes.reshape(-1)).to(DEV),
+                         torch.from_numpy(scales.reshape(-1)).to(DEV), u16_tensor(rs.reshape(-1)), pt, y)
+    torch.cuda.synchronize()
+    want = orc.combine_nvfp4(c.oc, c.L["token_row"], codes, scales, rs, probs)
+    got = bits_of(y)
+    assert_close_bf16(got, want, f"{name}: combine_nvfp4")
+    assert_bits_equal(got, want, f"{name}: combine_nvfp4 (bitwise)")

@@ -307,6 +307,18 @@ def test_new_entry_points_reject_bad_arguments(L):
     cs = short.to_c()
     assert L.ep_dispatch_fp8(ctypes.byref(cs), ctypes.byref(lay), fake, fake, fake, None) == -1
     assert L.ep_combine_bwd_probs(ctypes.byref(cs), ctypes.byref(lay), fake, fake, fake, None) == -1
+    # combine over NVFP4 rows: H % 16, 8-byte aligned codes, buffers present, enough rows
+    assert L.ep_combine_nvfp4(ctypes.byref(cc), ctypes.byref(lay), fake + 4, fake, fake, None, fake, None) == -1
+    assert L.ep_combine_nvfp4(ctypes.byref(cc), ctypes.byref(lay), fake, None, fake, None, fake, None) == -1
+    assert L.ep_combine_nvfp4(ctypes.byref(cc), ctypes.byref(lay), fake, fake, fake + 1, None, fake, None) == -1
+    assert L.ep_combine_nvfp4(ctypes.byref(cc), ctypes.byref(lay), fake, fake, fake, fake + 2, fake, None) == -1
+    assert L.ep_combine_nvfp4(ctypes.byref(cc), ctypes.byref(lay), fake, fake, fake, None, fake + 8, None) == -1
+    assert L.ep_combine_nvfp4(ctypes.byref(cc), None, fake, fake, fake, None, fake, None) == -1
+    assert L.ep_combine_nvfp4(ctypes.byref(cs), ctypes.byref(lay), fake, fake, fake, None, fake, None) == -1
+    c24 = cfg(hidden=24)
+    c24.recv_rows = rows
+    cc24 = c24.to_c()
+    assert L.ep_combine_nvfp4(ctypes.byref(cc24), ctypes.byref(lay), fake, fake, fake, None, fake, None) == -1
     # routing-map conversions: dense probabilities need compact ones and vice versa
     assert L.ep_indices_to_multihot(ctypes.byref(cc), None, None, fake, None, None) == -1
     assert L.ep_indices_to_multihot(ctypes.byref(cc), fake, None, None, None, None) == -1

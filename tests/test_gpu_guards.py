@@ -68,6 +68,10 @@ def test_guards_and_determinism(G, case):
     out = G.u16_tensor(c.rows(1)).view(-1)
     gy = G.u16_tensor(G.wl.make_tensor_like_rows(T, H, c.seed * 1000 + 3)).view(-1)
     rm_np, dp_np = G.orc.indices_to_multihot(c.oc, c.ids, c.probs)
+    cq_np, sq_np, rq_np = G.nvfp4_rows(c, 4)
+    cq = torch.from_numpy(cq_np.reshape(-1)).to(G.DEV)
+    sq = torch.from_numpy(sq_np.reshape(-1)).to(G.DEV)
+    rq = G.u16_tensor(rq_np.reshape(-1))
     rm = torch.from_numpy(rm_np.reshape(-1)).to(G.DEV)
     dp = torch.from_numpy(dp_np.reshape(-1)).to(G.DEV)
 
@@ -107,6 +111,7 @@ def test_guards_and_determinism(G, case):
         op("dispatch_bwd", lambda o: G.epx.ep_dispatch_bwd(cfg, lay, out, o), (T * H, torch.bfloat16))
         op("combine_bwd", lambda o: G.epx.ep_combine_bwd(cfg, lay, gy, probs, o), (R * H, torch.bfloat16))
         op("probs_grad", lambda o: G.epx.ep_combine_bwd_probs(cfg, lay, gy, out, o), (T * K, torch.float32))
+        op("combine_nvfp4", lambda o: G.epx.ep_combine_nvfp4(cfg, lay, cq, sq, rq, probs, o), (T * H, torch.bfloat16))
         op("to_multihot", lambda m, d: G.epx.ep_indices_to_multihot(cfg, ids, probs, m, d),
            (T * E, torch.uint8), (T * E, torch.float32))
         op("to_indices", lambda i, p, f: G.epx.ep_multihot_to_indices(cfg, rm, dp, i, p, f),

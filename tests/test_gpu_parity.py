@@ -50,6 +50,11 @@ def test_named_workload_full_size(G, name):
     G.check_dispatch_bwd(c, lay, name)
     G.check_combine_bwd(c, lay, name, weighted=True)
     G.check_probs_grad(c, lay, name)
+    G.check_combine_nvfp4(c, lay, name, weighted=True)
+    if name == "nvfp4":  # the dispatch's own NVFP4 rows, combined back
+        tr = c.L["token_row"]
+        G.check_combine_nvfp4(c, lay, name + " round trip", weighted=True,
+                              rows=G.orc.dispatch_nvfp4(c.oc, tr, c.x))
     if name == "capacity":
         assert f == 1  # overflow flag raised, nothing else
     else:
@@ -86,6 +91,8 @@ def test_random_shapes(G, seed):
     G.check_dispatch_bwd(c, lay, name)
     G.check_combine_bwd(c, lay, name, weighted=seed % 3 != 0)
     G.check_probs_grad(c, lay, name)
+    if c.cfg.hidden % 16 == 0:
+        G.check_combine_nvfp4(c, lay, name, weighted=seed % 2 == 1)
 
 
 @pytest.mark.parametrize("seed", range(LARGE_SEEDS))
@@ -118,6 +125,7 @@ def test_large_random_shapes(G, seed):
     G.check_dispatch_bwd(c, lay, name)
     G.check_combine_bwd(c, lay, name, weighted=seed % 3 != 0)
     G.check_probs_grad(c, lay, name)
+    G.check_combine_nvfp4(c, lay, name, weighted=seed % 2 == 0)
 
 
 EDGE = {
@@ -173,6 +181,8 @@ def test_edge_cases(G, edge):
     G.check_dispatch_bwd(c, lay, edge)
     G.check_combine_bwd(c, lay, edge)
     G.check_probs_grad(c, lay, edge)
+    if c.cfg.hidden % 16 == 0:
+        G.check_combine_nvfp4(c, lay, edge)
 
 
 @pytest.mark.parametrize("C", [1, 2, 7, 64])
