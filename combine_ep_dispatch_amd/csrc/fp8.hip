@@ -12,15 +12,16 @@
 // codes and scales to the rows of slots w, w + 8, ...  Short store runs per
 // wave rather than one wave storing all K' copies: at DeepSeek-V3 size the
 // kernel went from 51.0 to 48.0 us, and from 5.8 to 4.8 us at T = 128.
-// Outputs larger than half the MALL take nontemporal code stores (skewed
-// workload: 65.6 against 51.8 us; at DeepSeek-V3 size within 1%).  Rows
-// of fewer than 4 iterations (H < 3584) keep one wave per token.  After a
-// cache flush (cold input) the kernel is slower than the one-wave form at
-// DeepSeek-V3 size (61 against 48 us), whose plain stores then land in an
-// empty MALL; with the caches in the state that back-to-back launches leave,
-// and at small batches, it is the faster (T = 128 cold: 7.7 against
-// 9.3 us).  4 and 2 waves per token were slower than 8 warm and no better
-// cold.  Batches
+// Outputs larger than the 256 MiB MALL take nontemporal code stores; smaller
+// ones are stored plainly and stay in it.  Measured on MI355X, launches
+// back to back / after a cache flush: DeepSeek-V3 size (231 MiB out) 47.8 /
+// 49.2 us with plain stores against 48.0 / 63.3 us nontemporal; the skewed
+// workload (258 MiB) 51.9 / 66.9 nontemporal against 66.1 / 55.6 plain,
+// the plain stores' cold figure leaving the write-back of the MALL's dirty
+// lines to whatever runs next.  One wave per token: 51.1 / 48.2 and
+// 66.8 / 54.7 us; at T = 128 4.8 / 7.7 against 5.8 / 9.3 us.  Rows of
+// fewer than 4 iterations (H < 3584) keep one wave per token.  4 and 2
+// waves per token were slower than 8 warm and no better cold.  Batches
 // past that kernel's grid (2^23 tokens) take one wave per token (four under
 // kSmallBatchTokens, taking alternate iterations).  In an iteration, lanes
 // form 8 groups of 8; group j owns block 8*it + j and each lane 16 of its
@@ -147,10 +148,16 @@ typedef uint32_t v4u __attribute__((ext_vector_type(4)));
 #ifndef EPX_FP8_WPT
 #define EPX_FP8_WPT 8  // waves per token (one workgroup per token)
 #endif
-// Outputs larger than this (half the 256 MB MALL) take nontemporal code
-// stores: written straight through, they no longer evict the inputs and
-// other outputs from the MALL.  Smaller ones stay in it for their consumer.
-constexpr int64_t kFp8StreamBytes = int64_t(128) << 20;
+// Outputs larger than this (the MALL) take nontemporal code stores: they
+// could not stay in it anyway, and written straight through they no longer
+// evict the inputs from it.  Smaller ones stay in it for their consumer.
+#ifndef EPX_FP8_STREAM_MB
+#define EPX_FP8_STREAM_MB 256
+#endif
+constexpr int64_t kFp8StreamBytes = int64_t(EPX_FP8_STREAM_MB) << 20;
+#ifndef EPX_FP8_WG_MIN_ITERS
+#define EPX_FP8_WG_MIN_ITERS 4
+#endif
 
 // One workgroup of WPT waves per token: the waves quantize the row's
 // iterations into LDS once, then wave w stores the codes and scales of the
@@ -214,7 +221,7 @@ hipError_t launch_fp8(const Fp8Args& a, hipStream_t stream) {
     // blocks (H >= 3584).  With 2 (H = 2048, capacity workload) 6 of its 8
     // waves idle while the row is quantized, and the kernel took 32.9 against
     // 26.6 us with one wave per token.
-    if (nit >= 4 && (int64_t)a.T * WPT * kWave <= 0xFFFFFFFFll) {
+    if (nit >= EPX_FP8_WG_MIN_ITERS && (int64_t)a.T * WPT * kWave <= 0xFFFFFFFFll) {
         const size_t lds = (size_t)nit * kWave * sizeof(uint4) + (size_t)nit * 8 * sizeof(float);
         const int64_t out_bytes = (int64_t)a.T * a.Kp * (a.H + a.H / 128 * 4);
         if (out_bytes > kFp8StreamBytes)
