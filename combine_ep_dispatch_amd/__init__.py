@@ -29,13 +29,13 @@ import torch
 from . import _lib
 from ._lib import (EP_FLAG_BAD_ID, EP_FLAG_DROPPED, EP_FLAG_INTERNAL, EP_FLAG_MAP_OVERFLOW,  # noqa: F401
                    EP_NOALLOC_SCRATCH_BYTES, EP_ZERO_PAD_ROWS, EP_LAYOUT_LOOKBACK, EP_LAYOUT_DIRECT,
-                   EP_LAYOUT_BARRIER, EpCfg, EpLayout)
+                   EP_LAYOUT_BARRIER, EP_LAYOUT_COUNT, EpCfg, EpLayout)
 
 __all__ = [
     "EpConfig", "Layout", "QueryResult", "ep_query", "workspace_for", "ep_dispatch_layout",
     "ep_dispatch_layout_noalloc", "EP_NOALLOC_SCRATCH_BYTES", "ep_combine_nvfp4",
     "ep_dispatch", "ep_dispatch_nvfp4", "ep_dispatch_fp8", "ep_combine", "ep_dispatch_bwd", "ep_combine_bwd",
-    "ep_combine_bwd_probs", "ep_indices_to_multihot", "ep_multihot_to_indices", "assert_no_overflow", "EpError", "abi_version", "EP_ZERO_PAD_ROWS", "EP_LAYOUT_LOOKBACK", "EP_LAYOUT_DIRECT", "EP_LAYOUT_BARRIER", "EP_FLAG_DROPPED",
+    "ep_combine_bwd_probs", "ep_indices_to_multihot", "ep_multihot_to_indices", "assert_no_overflow", "EpError", "abi_version", "EP_ZERO_PAD_ROWS", "EP_LAYOUT_LOOKBACK", "EP_LAYOUT_DIRECT", "EP_LAYOUT_BARRIER", "EP_LAYOUT_COUNT", "EP_FLAG_DROPPED",
     "EP_FLAG_BAD_ID", "EP_FLAG_INTERNAL",
 ]
 

@@ -21,6 +21,7 @@ EP_ZERO_PAD_ROWS = 1
 EP_LAYOUT_LOOKBACK = 2
 EP_LAYOUT_DIRECT = 4
 EP_LAYOUT_BARRIER = 8
+EP_LAYOUT_COUNT = 16
 EP_FLAG_DROPPED = 1
 EP_FLAG_BAD_ID = 2
 EP_FLAG_INTERNAL = 4

@@ -44,7 +44,7 @@ int derive(const ep_cfg_t* c, Shape* d) {
     if (c->shared_expert != 0 && c->shared_expert != 1) return EP_EINVAL;
     if (c->shared_expert && (c->src_segment < 0 || c->src_segment >= c->num_segments)) return EP_EINVAL;
     if (c->reserved0 != 0 || c->reserved1 != 0) return EP_EINVAL;
-    constexpr uint32_t kPaths = EP_LAYOUT_LOOKBACK | EP_LAYOUT_DIRECT | EP_LAYOUT_BARRIER;
+    constexpr uint32_t kPaths = EP_LAYOUT_LOOKBACK | EP_LAYOUT_DIRECT | EP_LAYOUT_BARRIER | EP_LAYOUT_COUNT;
     if (c->flags & ~(EP_ZERO_PAD_ROWS | kPaths)) return EP_EINVAL;
     if (__builtin_popcount(c->flags & kPaths) > 1) return EP_EINVAL;  // at most one path
     d->T = c->num_tokens;
@@ -194,8 +194,12 @@ int layout_launch(const Shape& d, const int32_t* topk_ids, void* ws, const ep_la
         a.mode = kLayoutSinglePass;
     } else if (d.flags & EP_LAYOUT_DIRECT) {
         a.mode = kLayoutDirect;
+    } else if (d.flags & EP_LAYOUT_COUNT) {
+        a.mode = kLayoutCount;
     } else if (routed <= kSmallMaxSlots) {
         a.mode = kLayoutSmall;
+    } else if (routed <= kCountMaxSlots) {
+        a.mode = kLayoutCount;
     } else if (layout_direct(d.tiles) || d.sp_tiles > kSpMaxTiles) {
         a.mode = kLayoutDirect;  // measured fastest wherever its column sums fit one launch
     } else {
@@ -205,6 +209,10 @@ int layout_launch(const Shape& d, const int32_t* topk_ids, void* ws, const ep_la
         a.tiles = (int32_t)d.sp_tiles;
         a.rank_blocks = (int32_t)sp_blocks(d.sp_tiles, d.NG);
         a.slots_per_thread = sp_slots_per_thread(routed);
+    } else if (a.mode == kLayoutCount) {
+        a.slots_per_thread = 1;
+        a.tiles = (int32_t)std::max<int64_t>(1, (routed + kLayoutThreads - 1) / kLayoutThreads);
+        a.rank_blocks = (int32_t)std::max<int64_t>(a.tiles, std::min<int32_t>(d.NG, 256));
     } else if (a.mode == kLayoutDirect) {
         a.tiles = (int32_t)d.tiles;
         a.rank_blocks = (int32_t)std::max<int64_t>(d.tiles, std::min<int32_t>(d.NG, 256));

@@ -58,18 +58,33 @@ inline int64_t layout_tiles(int64_t routed_slots, int NG) {
     return nt < 1 ? 1 : nt;
 }
 
-// Up to this many routed slots (one tile of 256 x 4) the layout is one
-// launch: every workgroup ranks all slots in LDS to learn the group totals.
-// Measured on MI355X, the one launch beats the histogram + rank pair up to
-// 1024 slots (8.8 against 10.4 us at 1024); at 1280 and above the pair wins
-// (10.4 against 11.7 us), as every workgroup's ranking of the whole tile
-// then takes longer than the second launch.
-constexpr int64_t kSmallMaxSlots = 1024;
+// Up to this many routed slots (two slots per thread of one tile) the
+// layout is one launch in which every workgroup ranks all slots in LDS to
+// learn the group totals.  Measured on MI355X (DeepSeek-V3 shape), against
+// the count path below: 5.0 against 5.8 us at 8 slots, 5.2 against 6.1 at
+// 128, 6.0 against 6.2 at 512, 7.4 against 6.2 at 1024 (the serial
+// match-any rounds of the whole tile then cost more than the count).
+#ifndef EPX_SMALL_MAX_SLOTS
+#define EPX_SMALL_MAX_SLOTS 512
+#endif
+constexpr int64_t kSmallMaxSlots = EPX_SMALL_MAX_SLOTS;
+
+// Up to this many routed slots the layout is one launch in which every
+// workgroup counts every slot into per-group LDS counters (split at its own
+// tile: the counts before it are its in-group prefix), then ranks its tile
+// of 256 slots.  Nothing is read that another workgroup wrote.  Measured on
+// MI355X (DeepSeek-V3 shape, uniform and Zipf-1.2 routing), against the two
+// kernels: 6.5 against 9.4 us at 1280-2048 slots, 7.0 against 9.4 at 4096,
+// 8.2 against 9.5 at 8192, 10.3 against 9.5 at 16384 (every workgroup's
+// count of all slots then costs more than the second launch), 16.3 against
+// 11.5 at 32768.
+constexpr int64_t kCountMaxSlots = 8192;
 
 // Layout kernel paths.
 constexpr int kLayoutSinglePass = 0;  // k_layout_sp: ticketed tiles, decoupled look-back
 constexpr int kLayoutDirect = 1;      // k_layout_hist + k_layout_rank over a [tile][group] count table
 constexpr int kLayoutSmall = 2;       // k_layout_rank alone: one tile, every workgroup ranks it
+constexpr int kLayoutCount = 3;       // k_layout_rank alone: every workgroup counts every slot
 
 // Single-pass layout tiles: 256 x {1, 2, 4, 8} slots, the smallest tile
 // that gives at most kSpTargetTiles tiles (16, 32 and 64 measured within 1
@@ -222,7 +237,7 @@ struct LayoutArgs {
     int32_t T, K, Kp, E, S, G, NG, E_loc, A, C, shared, src_seg;
     int64_t recv_rows;
     int32_t tiles;             // tiles of the path that runs
-    int32_t mode;              // kLayoutSinglePass, kLayoutDirect or kLayoutSmall
+    int32_t mode;              // kLayoutSinglePass, kLayoutDirect, kLayoutSmall or kLayoutCount
     int32_t lookback;          // single pass: tile prefixes by decoupled look-back (else from all aggregates)
     int32_t rank_blocks;       // workgroups of the rank pass / single pass: max(tiles, min(NG, 256))
     int32_t slots_per_thread;  // 1, 2, 4 or 8 (layout_slots_per_thread)

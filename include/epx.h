@@ -68,13 +68,15 @@ extern "C" {
 
 /* Bits of ep_cfg_t.flags. */
 #define EP_ZERO_PAD_ROWS 1u    /* also write zeros into the payload of pad rows */
-/* ep_dispatch_layout path selection: at most one of the next three bits;
+/* ep_dispatch_layout path selection: at most one of the next four bits;
    every path gives the same results, they differ only in speed. */
 #define EP_LAYOUT_LOOKBACK 2u  /* one kernel: ticketed tiles, each tile's prefix
                                   by decoupled look-back */
 #define EP_LAYOUT_DIRECT 4u    /* two kernels: tile-count table, then ranks */
 #define EP_LAYOUT_BARRIER 8u   /* one kernel: ticketed tiles, each tile's prefix
                                   from one read of every tile's counts */
+#define EP_LAYOUT_COUNT 16u    /* one kernel: every workgroup counts every
+                                  routed slot (no workspace traffic) */
 
 /* Bits of the device flags word (ep_layout_t.flags[0]). */
 #define EP_FLAG_DROPPED 1      /* a slot was dropped at segment capacity [TD]  */
@@ -180,8 +182,11 @@ int ep_query(const ep_cfg_t* cfg, int64_t* min_recv_rows, int64_t* workspace_byt
  * and in-group ranks (stable, ascending slot index); each tile's prefix
  * over earlier tiles; the aligned group sizes scanned into group start rows;
  * token_row, expert_ids and src_info written.  Paths (same results):
- *  - up to 1024 routed slots: one kernel in which every workgroup ranks
+ *  - up to 512 routed slots: one kernel in which every workgroup ranks
  *    all slots itself;
+ *  - up to 8192 routed slots (by default; EP_LAYOUT_COUNT at any size): one
+ *    kernel in which every workgroup counts all slots per group in LDS,
+ *    then ranks its own tile;
  *  - otherwise up to 256 tiles (by default; EP_LAYOUT_DIRECT at any size):
  *    two kernels, a [tile][group] count table then the ranks;
  *  - beyond that (by default; EP_LAYOUT_LOOKBACK / EP_LAYOUT_BARRIER at any

@@ -52,8 +52,8 @@ def sentinel_layout(cfg: epx.EpConfig) -> epx.Layout:
 
 # The layout paths a test can force (cfg.flags bits); 0 = the default choice.
 LAYOUT_PATHS = {"single-pass": epx.EP_LAYOUT_LOOKBACK, "single-pass-barrier": epx.EP_LAYOUT_BARRIER,
-                "two-kernel": epx.EP_LAYOUT_DIRECT, "default": 0}
-PATH_FLAGS = epx.EP_LAYOUT_LOOKBACK | epx.EP_LAYOUT_DIRECT | epx.EP_LAYOUT_BARRIER
+                "two-kernel": epx.EP_LAYOUT_DIRECT, "count": epx.EP_LAYOUT_COUNT, "default": 0}
+PATH_FLAGS = epx.EP_LAYOUT_LOOKBACK | epx.EP_LAYOUT_DIRECT | epx.EP_LAYOUT_BARRIER | epx.EP_LAYOUT_COUNT
 
 
 def gpu_layout(cfg: epx.EpConfig, ids: np.ndarray, ws=None, path=None) -> epx.Layout:

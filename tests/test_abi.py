@@ -174,7 +174,8 @@ INVALID = [
     dict(num_tokens=-1), dict(hidden=0), dict(hidden=12), dict(num_experts=0), dict(num_segments=0),
     dict(num_experts=9), dict(top_k=0), dict(top_k=9), dict(align=0), dict(seg_capacity=-1),
     dict(shared_expert=2), dict(shared_expert=1, src_segment=2), dict(shared_expert=1, src_segment=-1),
-    dict(flags=6), dict(flags=7), dict(flags=10), dict(flags=12), dict(flags=14), dict(flags=16),
+    dict(flags=6), dict(flags=7), dict(flags=10), dict(flags=12), dict(flags=14), dict(flags=18), dict(flags=20),
+    dict(flags=24), dict(flags=32),
     dict(num_experts=4096, num_segments=2),  # > EP_MAX_GROUPS groups
     dict(num_tokens=1 << 28, top_k=4),  # 2^30 slots
     # capacity mode: the unclamped aligned offsets (summed in int32 before the
@@ -189,13 +190,15 @@ def test_query_rejects_invalid_config(L, kw):
     assert query(L, cfg(**kw))[0] == -1
 
 
-@pytest.mark.parametrize("flags", [0, 1, 2, 3, 4, 5, 8, 9])
+@pytest.mark.parametrize("flags", [0, 1, 2, 3, 4, 5, 8, 9, 16, 17])
 def test_query_accepts_documented_flags(L, flags):
     """EP_ZERO_PAD_ROWS (1) with at most one of the layout path bits
-    EP_LAYOUT_LOOKBACK (2), EP_LAYOUT_DIRECT (4), EP_LAYOUT_BARRIER (8)."""
-    from combine_ep_dispatch_amd import EP_LAYOUT_BARRIER, EP_LAYOUT_DIRECT, EP_LAYOUT_LOOKBACK, EP_ZERO_PAD_ROWS
+    EP_LAYOUT_LOOKBACK (2), EP_LAYOUT_DIRECT (4), EP_LAYOUT_BARRIER (8),
+    EP_LAYOUT_COUNT (16)."""
+    from combine_ep_dispatch_amd import (EP_LAYOUT_BARRIER, EP_LAYOUT_COUNT, EP_LAYOUT_DIRECT, EP_LAYOUT_LOOKBACK,
+                                         EP_ZERO_PAD_ROWS)
 
-    assert (EP_ZERO_PAD_ROWS, EP_LAYOUT_LOOKBACK, EP_LAYOUT_DIRECT, EP_LAYOUT_BARRIER) == (1, 2, 4, 8)
+    assert (EP_ZERO_PAD_ROWS, EP_LAYOUT_LOOKBACK, EP_LAYOUT_DIRECT, EP_LAYOUT_BARRIER, EP_LAYOUT_COUNT) == (1, 2, 4, 8, 16)
     assert query(L, cfg(flags=flags))[0] == 0
 
 
