@@ -41,7 +41,16 @@
 //    stores its lines stayed dirty in L2 and the MALL, and the next kernel
 //    paid for their write-back while reading its own cold input.  At
 //    DeepSeek-V3 size the whole six-kernel step went from ~455 to ~417 us,
-//    and combine alone from 91 to 88 us.
+//    and combine alone from 91 to 88 us.  Stores through a buffer
+//    descriptor with device scope (sc1) ran the gathers 2% faster back to
+//    back (86.2 against 87.9 us) and made the step slower (451 against
+//    413 us): their lines wait in the MALL and the next kernel writes them
+//    back.  The same holds for the scatters (step 434 us).
+//  - Both movers sit at the ceiling of their memory pattern on MI355X: a
+//    probe that issues the gathers' loads and stores at DeepSeek-V3 size
+//    (the same rows, 8 nontemporal 1 KiB reads and one nontemporal 1 KiB
+//    write per wave) with no arithmetic took 87.2 us, combine 88.0 us; the
+//    same probe without the writes took 69 us (6.8 TB/s of reads).
 #include "epx_device.h"
 
 #ifndef EPX_SCATTER_VPL
@@ -64,6 +73,17 @@
 #endif
 #ifndef EPX_SCATTER_NT_STORES
 #define EPX_SCATTER_NT_STORES 1
+#endif
+// Cache-policy bits for the output stores (1 = sc0, 2 = nt, 16 = sc1), -1
+// for the plain global forms above.
+#ifndef EPX_GATHER_STORE_AUX
+#define EPX_GATHER_STORE_AUX -1
+#endif
+#ifndef EPX_GATHER_LOAD_AUX
+#define EPX_GATHER_LOAD_AUX -1
+#endif
+#ifndef EPX_SCATTER_STORE_AUX
+#define EPX_SCATTER_STORE_AUX -1
 #endif
 
 namespace epx {
@@ -99,6 +119,21 @@ __device__ __forceinline__ v4u load_scatter_src(const v4u* p) {
 #else
     return *p;
 #endif
+}
+
+// 16-byte store to vector v of a wave-uniform row base through a buffer
+// descriptor carrying the cache-policy bits AUX.
+template <int AUX>
+__device__ __forceinline__ void store_policy(v4u* row, int32_t v, int32_t row_bytes, v4u val) {
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(row, (short)0, row_bytes, 0x00020000);
+    __builtin_amdgcn_raw_buffer_store_b128(val, rs, v * 16, 0, AUX);
+}
+
+template <int AUX>
+__device__ __forceinline__ v4u load_policy(const v4u* row, int32_t v, int32_t row_bytes) {
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<v4u*>(row), (short)0, row_bytes, 0x00020000);
+    return __builtin_amdgcn_raw_buffer_load_b128(rs, v * 16, 0, AUX);
 }
 
 __device__ __forceinline__ void store_scatter_dst(v4u* p, v4u v) {
@@ -212,7 +247,13 @@ __global__ __launch_bounds__(EPX_SCATTER_WAVES * kWave) void k_scatter(MoveArgs 
 #pragma unroll
     for (int i = 0; i < VPL; ++i) {
         const int32_t v = (p * VPL + i) * kWave + lane;
-        if (FULL || v < Hv) store_scatter_dst(dst + v, SCALED ? scale_bf16x8(buf[i], w) : buf[i]);
+        if (FULL || v < Hv) {
+            const v4u val = SCALED ? scale_bf16x8(buf[i], w) : buf[i];
+            if constexpr (EPX_SCATTER_STORE_AUX >= 0)
+                store_policy<EPX_SCATTER_STORE_AUX>(dst, v, Hv * 16, val);
+            else
+                store_scatter_dst(dst + v, val);
+        }
     }
 }
 
@@ -270,7 +311,11 @@ __global__ __launch_bounds__(kGatherThreads) void k_gather(MoveArgs a, int32_t H
 #pragma unroll
             for (int i = 0; i < VPL; ++i) {
                 const int32_t v = v0 + i * kWave;
-                buf[kk][i] = (rows[kk] >= 0 && (FULL || v < Hv)) ? load_stream(r + v) : v4u{0, 0, 0, 0};
+                if constexpr (EPX_GATHER_LOAD_AUX >= 0)
+                    buf[kk][i] = (rows[kk] >= 0 && (FULL || v < Hv)) ? load_policy<EPX_GATHER_LOAD_AUX>(r, v, Hv * 16)
+                                                                      : v4u{0, 0, 0, 0};
+                else
+                    buf[kk][i] = (rows[kk] >= 0 && (FULL || v < Hv)) ? load_stream(r + v) : v4u{0, 0, 0, 0};
             }
         }
 #pragma unroll
@@ -292,7 +337,10 @@ __global__ __launch_bounds__(kGatherThreads) void k_gather(MoveArgs a, int32_t H
             o.y = pack_bf16x2(acc[i][2], acc[i][3]);
             o.z = pack_bf16x2(acc[i][4], acc[i][5]);
             o.w = pack_bf16x2(acc[i][6], acc[i][7]);
-            store_stream(dst + v, o);
+            if constexpr (EPX_GATHER_STORE_AUX >= 0)
+                store_policy<EPX_GATHER_STORE_AUX>(dst, v, Hv * 16, o);
+            else
+                store_stream(dst + v, o);
         }
     }
 }
