@@ -42,7 +42,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, published
-COLD_REPS = 10
+COLD_REPS = 20
+MIN_OP_REPS = 50        # timed repetitions per op, whatever --steps is
 METRIC = "dispatch+combine tokens/s and effective HBM GB/s (% of peak), 1 MI355X"
 KERNEL_SOURCES = ("combine_ep_dispatch_amd/csrc/move.hip", "combine_ep_dispatch_amd/csrc/nvfp4.hip",
                   "combine_ep_dispatch_amd/csrc/layout.hip", "combine_ep_dispatch_amd/csrc/fp8.hip",
@@ -50,7 +51,7 @@ KERNEL_SOURCES = ("combine_ep_dispatch_amd/csrc/move.hip", "combine_ep_dispatch_
 
 
 # Each layout path forced (timed beside the default choice; results must agree).
-LAYOUT_PATHS = {"layout_lookback": 2, "layout_barrier": 8, "layout_two_kernel": 4}
+LAYOUT_PATHS = {"layout_lookback": 2, "layout_barrier": 8, "layout_two_kernel": 4, "layout_count": 16}
 
 
 def log(*a):
@@ -108,6 +109,7 @@ def algorithmic_bytes(w, kept: int, used_rows: int, kept_routed: int = None) -> 
         "layout_lookback": 4 * T * K + 4 * T * Kp + 12 * used_rows,
         "layout_barrier": 4 * T * K + 4 * T * Kp + 12 * used_rows,
         "layout_two_kernel": 4 * T * K + 4 * T * Kp + 12 * used_rows,
+        "layout_count": 4 * T * K + 4 * T * Kp + 12 * used_rows,
         "combine_bwd_probs": row * T + row * kept_routed + 4 * T * Kp + 4 * T * K,
         "dispatch_fp8": row * T + kept * (H + 4 * (H // 128)) + 4 * T * Kp,
         "combine_nvfp4": kept * (H // 2 + H // 16 + 2) + row * T + 4 * T * K + 4 * T * Kp,
@@ -275,7 +277,7 @@ def main() -> int:
 
     # per-op kernel durations: a graph of LAUNCHES back-to-back launches per op,
     # bracketed by HIP events on the stream the kernels run on
-    LAUNCHES, REPS, OP_WARMUP = 8, max(10, args.steps // 2), 5
+    LAUNCHES, REPS, OP_WARMUP = 8, max(MIN_OP_REPS, args.steps), 5
     op_us = {}
     for n, fn in ops + extra_ops:
         def many(fn=fn):
@@ -295,6 +297,21 @@ def main() -> int:
         torch.cuda.synchronize()
         op_us[n] = [a.elapsed_time(b) * 1e3 / LAUNCHES for a, b in times]
         del g
+    # in-step per-op durations: eager steps enqueued back to back (the queue
+    # stays ahead of the GPU), an event between consecutive ops, so each op
+    # runs after its predecessors as in the timed step
+    IN_STEP_STEPS = max(MIN_OP_REPS // 2, 20)
+    marks = []
+    for _ in range(IN_STEP_STEPS):
+        evs = [torch.cuda.Event(enable_timing=True)]
+        evs[0].record(stream)
+        for _, fn in ops:
+            fn()
+            evs.append(torch.cuda.Event(enable_timing=True))
+            evs[-1].record(stream)
+        marks.append(evs)
+    torch.cuda.synchronize()
+    in_step_us = {n: [m[i].elapsed_time(m[i + 1]) * 1e3 for m in marks[2:]] for i, n in enumerate(names)}
     # cold per-op durations: one launch after an untimed read of 1 GiB that
     # evicts L2 and the 256 MB MALL.  A read leaves no dirty lines behind
     # (a fill would, and the timed launch would pay for writing them back),
@@ -345,30 +362,40 @@ def main() -> int:
                 raise RuntimeError(f"the {path} layout differs from the default one in {k}")
     kept_routed = int((tr[:, :w.K] >= 0).sum())
     nbytes = algorithmic_bytes(w, kept, used_rows, kept_routed)
+    def rate(n, us):
+        gbps = nbytes[n] / (us * 1e-6) / 1e9
+        return {"us_median": round(us, 2), "GBps": round(gbps, 1), "frac": round(gbps / HBM_PEAK_GBPS, 4)}
+
     per_op = {}
     for n in names + [n for n, _ in extra_ops]:
-        us = statistics.mean(op_us[n])
         med = statistics.median(op_us[n])
         dec = statistics.quantiles(op_us[n], n=10)
         cdec = statistics.quantiles(cold_us[n], n=10)
-        cmed = statistics.median(cold_us[n])
-        gbps = nbytes[n] / (us * 1e-6) / 1e9
-        per_op[n] = {"us": round(us, 2), "us_median": round(med, 2), "us_p10": round(dec[0], 2),
-                     "us_p90": round(dec[-1], 2), "bytes": nbytes[n],
+        gbps = nbytes[n] / (med * 1e-6) / 1e9
+        per_op[n] = {"us": round(med, 2), "us_mean": round(statistics.mean(op_us[n]), 2), "us_p10": round(dec[0], 2),
+                     "us_p90": round(dec[-1], 2), "reps": len(op_us[n]), "bytes": nbytes[n],
                      "GBps": round(gbps, 1), "frac": round(gbps / HBM_PEAK_GBPS, 4),
                      "frac_of_copy": round(gbps / copy_gbps, 4),
-                     "cold": {"us_median": round(cmed, 2), "us_p10": round(cdec[0], 2), "us_p90": round(cdec[-1], 2),
-                              "GBps": round(nbytes[n] / (cmed * 1e-6) / 1e9, 1),
-                              "frac": round(nbytes[n] / (cmed * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)}}
-        log(f"[bench] {n:17s} {us:8.2f} us  {nbytes[n] / 1e6:8.2f} MB  {gbps:7.1f} GB/s  "
-            f"{100 * gbps / HBM_PEAK_GBPS:5.1f}% of 8 TB/s   cold {cmed:8.2f} us "
-            f"{100 * per_op[n]['cold']['frac']:5.1f}%")
+                     "cold": dict(rate(n, statistics.median(cold_us[n])), us_p10=round(cdec[0], 2),
+                                  us_p90=round(cdec[-1], 2), reps=len(cold_us[n]))}
+        if n in in_step_us:
+            per_op[n]["in_step"] = dict(rate(n, statistics.median(in_step_us[n])), reps=len(in_step_us[n]))
+        log(f"[bench] {n:18s} {med:8.2f} us  {nbytes[n] / 1e6:8.2f} MB  {gbps:7.1f} GB/s  "
+            f"{100 * gbps / HBM_PEAK_GBPS:5.1f}% of 8 TB/s   cold {per_op[n]['cold']['us_median']:8.2f} us "
+            f"{100 * per_op[n]['cold']['frac']:5.1f}%" +
+            (f"   in step {per_op[n]['in_step']['us_median']:8.2f} us {100 * per_op[n]['in_step']['frac']:5.1f}%"
+             if n in in_step_us else ""))
     step_bytes = sum(nbytes[n] for n in names)
     dom = max((n for n in names if n != "layout"), key=lambda n: per_op[n]["us"])
     fwd_us = per_op["layout"]["us"] + per_op["dispatch"]["us"] + per_op["combine"]["us"]
     roof = {"bound": "hbm", "kernel": dom, "achieved": per_op[dom]["GBps"], "peak": HBM_PEAK_GBPS,
             "unit": "GB/s", "frac": per_op[dom]["frac"], "traffic": traffic_for(dom, args.workload),
-            "algorithmic_bytes_per_launch": nbytes[dom], "avg_launch_us": per_op[dom]["us"]}
+            "algorithmic_bytes_per_launch": nbytes[dom], "avg_launch_us": per_op[dom]["us"],
+            "in_step_frac": per_op[dom]["in_step"]["frac"], "in_step_launch_us": per_op[dom]["in_step"]["us_median"],
+            "cold_frac": per_op[dom]["cold"]["frac"], "cold_launch_us": per_op[dom]["cold"]["us_median"],
+            "note": ("frac: median launch of graphs of 8 back-to-back launches (warm); in_step_frac: the kernel "
+                     "inside eager steps enqueued back to back; cold_frac: one launch after a 1 GiB read that "
+                     "evicts L2 and MALL")}
 
     result = {
         "metric": METRIC,
@@ -393,10 +420,12 @@ def main() -> int:
         "hbm_frac": round(step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
         "fwd_dispatch_combine_tokens_per_s": round(T / (fwd_us * 1e-6), 1),
         "ops": per_op,
-        "ops_note": ("us/us_median/us_p10/us_p90: warm, graphs of 8 back-to-back launches, "
-                     f"{OP_WARMUP} untimed replays then {REPS} timed; cold: one launch "
-                     f"after an untimed read of 1 GiB that evicts L2 and MALL ({COLD_REPS} reps); frac_of_copy: "
-                     "against torch's 1 GiB device copy"),
+        "ops_note": ("us (median), us_mean, us_p10, us_p90, GBps, frac: warm, graphs of 8 back-to-back launches, "
+                     f"{OP_WARMUP} untimed replays then {REPS} timed; in_step: the op inside eager steps "
+                     f"enqueued back to back ({IN_STEP_STEPS} steps, the first 2 dropped), an event between "
+                     f"consecutive ops; cold: one launch after an untimed read of 1 GiB that evicts L2 and MALL "
+                     f"({COLD_REPS} reps); frac_of_copy: against torch's 1 GiB device copy; GBps and frac use "
+                     "the medians"),
         "copy_context_GBps": round(copy_gbps, 1),
         "overflow_flags": flags,
         "roofline": roof,
@@ -527,9 +556,12 @@ def latency_sweep(torch, epx, wl, dev, workload: str, token_counts) -> int:
 
 
 def copy_calibration(torch, epx, dev) -> int:
-    """A plain copy of known size (1 GiB read + 1 GiB written) through the
-    dispatch kernel with identity routing: rocprofv3 FETCH_SIZE / WRITE_SIZE
-    of this launch give the counter-to-bytes scale."""
+    """Plain copies of known size (1 GiB read + 1 GiB written) through two
+    kernels with identity routing: rocprofv3 FETCH_SIZE / WRITE_SIZE of these
+    launches give the counter-to-bytes scale for each load pattern.
+      - k_scatter (ep_dispatch): plain 16-byte loads of x, streaming stores;
+      - k_gather (ep_dispatch_bwd, K = 1): nontemporal 16-byte loads of the
+        receive rows, nontemporal stores."""
     T, H = 65536, 8192  # 65536 rows x 16 KiB = 1 GiB
     cfg = epx.EpConfig(num_tokens=T, hidden=H, num_experts=1, num_segments=1, top_k=1)
     cfg.recv_rows = epx.ep_query(cfg).min_recv_rows
@@ -544,8 +576,13 @@ def copy_calibration(torch, epx, dev) -> int:
     for _ in range(3):
         epx.ep_dispatch(cfg, lay, x, recv)
     torch.cuda.synchronize()
-    print(json.dumps({"copy_calibration": {"bytes_read": T * H * 2 + T * 4, "bytes_written": T * H * 2,
-                                           "launches": 3}}), flush=True)
+    for _ in range(3):
+        epx.ep_dispatch_bwd(cfg, lay, recv, x)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration": {
+        "scatter": {"kernel": "k_scatter", "bytes_read": T * H * 2 + T * 4, "bytes_written": T * H * 2, "launches": 3},
+        "gather": {"kernel": "k_gather", "bytes_read": T * H * 2 + T * 4, "bytes_written": T * H * 2,
+                   "launches": 3}}}), flush=True)
     return 0
 
 
