@@ -11,13 +11,21 @@
 //
 // One wave per (token, piece of 64 blocks = 1024 elements).  Lane l owns
 // block b = 64*piece + l: per slot row it loads the block's 8 code bytes
-// and its scale byte (wave loads of 512 and 64 contiguous bytes) and the
-// row's rowscale (wave-uniform); the loads of up to 8 slots are issued
-// before any is used.  The E2M1 values come from gfx950's
-// v_cvt_scalef32_pk_f32_fp4 with scale 1.0 (two exact values per
-// instruction); the block scale and the element product are ordinary fp32
-// multiplies in the order above.  A row is 4034 bytes instead of 14336 for
-// bf16 at H = 7168, so the kernel reads 3.6x fewer bytes than ep_combine.
+// and its scale byte (wave loads of 512 and 64 contiguous bytes) through
+// buffer descriptors whose base is the row (wave-uniform), and the row's
+// rowscale; the loads of up to 8 slots are issued before any is used.  A
+// masked or dropped slot gets an empty descriptor (its loads return 0) and
+// weight 0, so it adds +0 to every sum, which leaves the sum unchanged: a
+// sum that starts at +0 never becomes -0 in round-to-nearest.  That keeps
+// the slot loop free of per-slot branches.  The E2M1 values come from
+// gfx950's v_cvt_scalef32_pk_f32_fp4 with scale 1.0 (two exact values per
+// instruction), the E4M3 scale from v_cvt_f32_fp8 (exact; NaN for the
+// codes 0x7F and 0xFF); tests/test_gpu_conversions.py checks both against
+// the software decodes on every byte.  The block scale and the element
+// product are ordinary fp32 multiplies in the order above.  A row is 4034
+// bytes instead of 14336 for bf16 at H = 7168, so the kernel reads 3.6x
+// fewer bytes than ep_combine; it is bound by the VALU: three fp32
+// operations per element and slot (packed fp32 math stays off).
 #include "epx_device.h"
 
 namespace epx {
@@ -28,10 +36,12 @@ constexpr int kCqWaves = kCqThreads / kWave;
 constexpr int kCqBatch = 8;      // slots whose loads are in flight together
 
 typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+typedef uint32_t v2u __attribute__((ext_vector_type(2)));
+constexpr int kBufferFlags = 0x00020000;  // buffer descriptor word 3: 32-bit data, raw addressing
 
 // The 16 E2M1 values of one block: 8 code bytes, element 2j in the low
 // nibble of byte j.
-__device__ __forceinline__ void e2m1_block(uint2 c, float (&v)[16]) {
+__device__ __forceinline__ void e2m1_block(v2u c, float (&v)[16]) {
     f32x2_t p;
     p = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c.x, 1.0f, 0);
     v[0] = p.x, v[1] = p.y;
@@ -59,39 +69,42 @@ __global__ __launch_bounds__(kCqThreads) void k_combine_nvfp4(CombineNvfp4Args a
     const int32_t piece = wave - t * pieces;
     const int lane = threadIdx.x & (kWave - 1);
     const int32_t nblk = a.H / 16;
-    const int32_t b = piece * kWave + lane;
-    const bool active = b < nblk;
+    const int32_t b = piece * kWave + lane;  // lanes past the last block read past their descriptors: 0
 
     // Slot row and weight of slot `lane` (both loads issued before either is
-    // tested); rows outside [0, R) read as -1.
+    // tested); rows outside [0, R) read as -1 and get weight 0.
     const int32_t r_raw = a.token_row[(int64_t)t * a.Kp + min(lane, a.Kp - 1)];
     float w_lane = 1.0f;
     if (WEIGHTED) w_lane = a.probs[(int64_t)t * a.K + min(lane, a.K - 1)];
-    const int32_t my_row = (lane < a.Kp && r_raw < a.R) ? r_raw : -1;
-    const float my_w = lane < a.K ? w_lane : 1.0f;
+    const int32_t my_row = (lane < a.Kp && r_raw >= 0 && r_raw < a.R) ? r_raw : -1;
+    const float my_w = my_row < 0 ? 0.0f : (lane < a.K ? w_lane : 1.0f);
 
     float acc[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[i] = 0.0f;
-    const int64_t cstride = a.H / 2;
+    const int32_t cstride = a.H / 2;
     for (int32_t k0 = 0; k0 < a.Kp; k0 += kCqBatch) {
-        int32_t rows[kCqBatch];
-        uint2 cw[kCqBatch];
+        v2u cw[kCqBatch];
         uint32_t sc[kCqBatch], rs[kCqBatch];
 #pragma unroll
         for (int kk = 0; kk < kCqBatch; ++kk) {
-            rows[kk] = k0 + kk < a.Kp ? __builtin_amdgcn_readlane(my_row, k0 + kk) : -1;
-            const int64_t r = rows[kk] < 0 ? 0 : rows[kk];
-            const bool ld = rows[kk] >= 0 && active;
-            cw[kk] = ld ? *reinterpret_cast<const uint2*>(a.codes + r * cstride + 8 * (int64_t)b) : make_uint2(0, 0);
-            sc[kk] = ld ? (uint32_t)a.scales[r * nblk + b] : 0u;
-            rs[kk] = rows[kk] >= 0 ? (uint32_t)a.rowscale[r] : 0u;
+            const int32_t row = k0 + kk < a.Kp ? __builtin_amdgcn_readlane(my_row, k0 + kk) : -1;
+            const bool valid = row >= 0;
+            const int64_t r = valid ? row : 0;
+            const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(
+                const_cast<uint8_t*>(a.codes + r * cstride), (short)0, valid ? cstride : 0, kBufferFlags);
+            const __amdgpu_buffer_rsrc_t rsc = __builtin_amdgcn_make_buffer_rsrc(
+                const_cast<uint8_t*>(a.scales + r * nblk), (short)0, valid ? nblk : 0, kBufferFlags);
+            cw[kk] = __builtin_amdgcn_raw_buffer_load_b64(rc, 8 * b, 0, 0);
+            sc[kk] = __builtin_amdgcn_raw_buffer_load_b8(rsc, b, 0, 0);
+            rs[kk] = valid ? (uint32_t)a.rowscale[r] : 0u;
         }
 #pragma unroll
         for (int kk = 0; kk < kCqBatch; ++kk) {
-            if (rows[kk] < 0) continue;  // masked or dropped: contributes nothing
+            if (k0 + kk >= a.Kp) break;
             const float w = WEIGHTED ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_w), k0 + kk)) : 1.0f;
-            const float bs = e4m3_decode_signed(sc[kk]) * bf16_lo(rs[kk]);  // block scale * float(rowscale)
+            // block scale * float(rowscale)
+            const float bs = __builtin_amdgcn_cvt_f32_fp8((int)sc[kk], 0) * bf16_lo(rs[kk]);
             float v[16];
             e2m1_block(cw[kk], v);
 #pragma unroll
@@ -106,7 +119,7 @@ __global__ __launch_bounds__(kCqThreads) void k_combine_nvfp4(CombineNvfp4Args a
             }
         }
     }
-    if (!active) return;
+    if (b >= nblk) return;
     v4u* dst = reinterpret_cast<v4u*>(a.y + (int64_t)t * a.H + 16 * (int64_t)b);
     v4u o0, o1;
     o0.x = pack_bf16x2(acc[0], acc[1]);

@@ -116,6 +116,14 @@ __global__ void k_e2m1_decode(uint32_t* out, uint32_t* ref) {
     decode_sel<3>(byte, out, ref);
 }
 
+// E4M3 decode (v_cvt_f32_fp8, byte 0) of every byte: out[c] = float bits of
+// the hardware value, ref[c] = e4m3_decode_signed(c).
+__global__ void k_e4m3_decode(uint32_t* out, uint32_t* ref) {
+    const uint32_t c = threadIdx.x;  // 256 threads
+    out[c] = __float_as_uint(__builtin_amdgcn_cvt_f32_fp8((int)c, 0));
+    ref[c] = __float_as_uint(e4m3_decode_signed(c));
+}
+
 // The same conversion with the scale operand set to a block scale
 // bs = e4m3(sc) * float(rowscale), against e2m1_decode(code) * bs, for
 // every code, every finite E4M3 scale byte and every finite bf16 rowscale.
@@ -175,6 +183,13 @@ int conv_check_encode(int kind, uint64_t begin, uint64_t n, void* counts, void* 
 // out, ref: u32 [256 * 4 * 2] device memory.
 int conv_check_e2m1_decode(void* out, void* ref, void* stream) {
     hipLaunchKernelGGL(k_e2m1_decode, dim3(1), dim3(256), 0, static_cast<hipStream_t>(stream),
+                       static_cast<uint32_t*>(out), static_cast<uint32_t*>(ref));
+    return hipGetLastError() == hipSuccess ? 0 : -2;
+}
+
+// out, ref: u32 [256] device memory.
+int conv_check_e4m3_decode(void* out, void* ref, void* stream) {
+    hipLaunchKernelGGL(k_e4m3_decode, dim3(1), dim3(256), 0, static_cast<hipStream_t>(stream),
                        static_cast<uint32_t*>(out), static_cast<uint32_t*>(ref));
     return hipGetLastError() == hipSuccess ? 0 : -2;
 }

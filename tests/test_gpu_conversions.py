@@ -15,6 +15,9 @@ those definitions against the CPU oracle at every rounding boundary.
     equal to the bit-field decode for every byte in every byte position
     (with another scale it is not an exact multiply, so the kernel does not
     use one).
+  * E4M3 decode, v_cvt_f32_fp8 (NVFP4 combine's block scales): equal to the
+    software decode and to the oracle's on every finite code, NaN for the
+    two NaN codes 0x7F and 0xFF as in the oracle.
 
 The software encoders and the oracle (oracle/oracle.c: brute-force nearest
 value, ties to the even code) are both monotone step functions of the
@@ -109,6 +112,25 @@ def test_e2m1_decode_every_byte(C):
             for half, nib in ((0, byte & 15), (1, byte >> 4)):
                 want[(byte * 4 + sel) * 2 + half] = -mags[nib & 7] if nib & 8 else mags[nib & 7]
     assert np.array_equal(r, want.view(np.uint32))  # -0 for code 8 included
+
+
+def test_e4m3_decode_every_byte(C, orc):
+    out = torch.zeros(256, dtype=torch.int32, device=DEV)
+    ref = torch.zeros(256, dtype=torch.int32, device=DEV)
+    assert C.conv_check_e4m3_decode(ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(ref.data_ptr()), stream()) == 0
+    torch.cuda.synchronize()
+    o, r = out.cpu().numpy().view(np.uint32), ref.cpu().numpy().view(np.uint32)
+    lib = orc._load()
+    dec = lib.orc_e4m3_decode
+    dec.restype, dec.argtypes = ctypes.c_float, [ctypes.c_uint8]
+    nan_codes = (0x7F, 0xFF)
+    for c in range(256):
+        want = np.float32(dec(c))
+        hw = o[c:c + 1].view(np.float32)[0]
+        if c in nan_codes:
+            assert np.isnan(hw) and np.isnan(want), (c, hw, want)
+        else:
+            assert o[c] == r[c] == want.view(np.uint32), (hex(c), hex(o[c]), hex(r[c]), want)
 
 
 def test_e2m1_decode_with_block_scale(C):

@@ -229,6 +229,40 @@ def test_nvfp4_special_rows(G, H):
         G.check_fp8(c, lay, "fp8_special")
 
 
+@pytest.mark.parametrize("H", [1040, 4096])
+def test_combine_nvfp4_special_rows(G, H):
+    """NVFP4 combine over rows with every E4M3 scale byte (the NaN codes 0x7F
+    and 0xFF included), every code byte, and rowscales 0, -0, bf16
+    subnormals, the largest finite bf16, infinity and NaN.  Outputs that are
+    NaN must be NaN in both; all others equal bit for bit.  H = 1040: 65
+    blocks, the second piece of a token holds one block."""
+    rng = np.random.default_rng(5)
+    T = 64
+    c = G.random_case(12, T=T, H=H, S=2, E_loc=4, K=3, A=4, shared=1, src=0, mask_p=0.1)
+    lay = G.check_layout(c, "nvfp4_combine_special")
+    R = c.cfg.recv_rows
+    codes = rng.integers(0, 256, (R, H // 2), dtype=np.uint8)
+    scales = (np.arange(R * (H // 16)) % 256).astype(np.uint8).reshape(R, H // 16)
+    rng.shuffle(scales, axis=1)
+    specials = np.array([0x0000, 0x8000, 0x0001, 0x8001, 0x007F, 0x7F7F, 0xFF7F, 0x7F80, 0xFF80, 0x7FC0],
+                        np.uint16)
+    rs = G.wl.bf16_bits(np.exp2(rng.uniform(-20, 20, R)).astype(np.float32))
+    rs[: specials.size] = specials
+    rng.shuffle(rs)
+    probs = c.probs
+    y = G.bf16_filled(T, H, G.orc.SENTINEL_U16)
+    G.epx.ep_combine_nvfp4(c.cfg, lay, torch.from_numpy(codes.reshape(-1)).to(G.DEV),
+                           torch.from_numpy(scales.reshape(-1)).to(G.DEV), G.u16_tensor(rs),
+                           torch.from_numpy(probs.reshape(-1)).to(G.DEV), y)
+    torch.cuda.synchronize()
+    got = G.bits_of(y).reshape(-1)
+    want = G.orc.combine_nvfp4(c.oc, c.L["token_row"], codes, scales, rs, probs).reshape(-1)
+    nan = lambda b: ((b & 0x7F80) == 0x7F80) & ((b & 0x7F) != 0)
+    assert np.array_equal(nan(got), nan(want)), np.nonzero(nan(got) != nan(want))[0][:8]
+    assert nan(want).any() and (~nan(want)).any()
+    G.assert_bits_equal(got[~nan(want)], want[~nan(want)], "combine_nvfp4 special rows")
+
+
 def test_fp8_special_rows(G):
     """FP8 blocks with zeros, -0, bf16 subnormals, huge and tiny magnitudes,
     ties at E4M3 midpoints, and a ragged last block group (H/128 = 9)."""
