@@ -47,6 +47,7 @@ MIN_OP_REPS = 50        # timed repetitions per op, whatever --steps is
 METRIC = "dispatch+combine tokens/s and effective HBM GB/s (% of peak), 1 MI355X"
 KERNEL_SOURCES = ("combine_ep_dispatch_amd/csrc/move.hip", "combine_ep_dispatch_amd/csrc/nvfp4.hip",
                   "combine_ep_dispatch_amd/csrc/layout.hip", "combine_ep_dispatch_amd/csrc/fp8.hip",
+                  "combine_ep_dispatch_amd/csrc/nvfp4_combine.hip", "combine_ep_dispatch_amd/csrc/api.hip",
                   "combine_ep_dispatch_amd/csrc/epx_device.h")
 
 
@@ -89,6 +90,20 @@ def traffic_for(op: str, workload: str):
         return None
     entry = doc.get("ops", {}).get(op)
     return None if entry is None else entry.get("bytes_per_launch")
+
+
+def in_step_for(workload: str):
+    """Per-op durations inside graph-replayed steps, from the rocprofv3
+    kernel trace of `workload` (see profiles/), or None when missing, taken
+    on another workload or on different kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"kernel_trace_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        doc = json.load(f)
+    if doc.get("workload") != workload or doc.get("source_digest") != source_digest():
+        return None
+    return doc
 
 
 def algorithmic_bytes(w, kept: int, used_rows: int, kept_routed: int = None) -> dict:
@@ -367,6 +382,7 @@ def main() -> int:
         return {"us_median": round(us, 2), "GBps": round(gbps, 1), "frac": round(gbps / HBM_PEAK_GBPS, 4)}
 
     per_op = {}
+    trace = in_step_for(args.workload)
     for n in names + [n for n, _ in extra_ops]:
         med = statistics.median(op_us[n])
         dec = statistics.quantiles(op_us[n], n=10)
@@ -379,23 +395,30 @@ def main() -> int:
                      "cold": dict(rate(n, statistics.median(cold_us[n])), us_p10=round(cdec[0], 2),
                                   us_p90=round(cdec[-1], 2), reps=len(cold_us[n]))}
         if n in in_step_us:
-            per_op[n]["in_step"] = dict(rate(n, statistics.median(in_step_us[n])), reps=len(in_step_us[n]))
+            per_op[n]["in_step_eager"] = dict(rate(n, statistics.median(in_step_us[n])), reps=len(in_step_us[n]))
+        if trace is not None and n in trace["in_step_us"]:
+            per_op[n]["in_step"] = dict(rate(n, trace["in_step_us"][n]), steps=trace["graph_steps"])
         log(f"[bench] {n:18s} {med:8.2f} us  {nbytes[n] / 1e6:8.2f} MB  {gbps:7.1f} GB/s  "
             f"{100 * gbps / HBM_PEAK_GBPS:5.1f}% of 8 TB/s   cold {per_op[n]['cold']['us_median']:8.2f} us "
             f"{100 * per_op[n]['cold']['frac']:5.1f}%" +
             (f"   in step {per_op[n]['in_step']['us_median']:8.2f} us {100 * per_op[n]['in_step']['frac']:5.1f}%"
-             if n in in_step_us else ""))
+             if "in_step" in per_op[n] else "") +
+            (f"   eager+event {per_op[n]['in_step_eager']['us_median']:8.2f} us" if n in in_step_us else ""))
     step_bytes = sum(nbytes[n] for n in names)
     dom = max((n for n in names if n != "layout"), key=lambda n: per_op[n]["us"])
     fwd_us = per_op["layout"]["us"] + per_op["dispatch"]["us"] + per_op["combine"]["us"]
     roof = {"bound": "hbm", "kernel": dom, "achieved": per_op[dom]["GBps"], "peak": HBM_PEAK_GBPS,
             "unit": "GB/s", "frac": per_op[dom]["frac"], "traffic": traffic_for(dom, args.workload),
             "algorithmic_bytes_per_launch": nbytes[dom], "avg_launch_us": per_op[dom]["us"],
-            "in_step_frac": per_op[dom]["in_step"]["frac"], "in_step_launch_us": per_op[dom]["in_step"]["us_median"],
+            "in_step_frac": per_op[dom]["in_step"]["frac"] if "in_step" in per_op[dom] else None,
+            "in_step_launch_us": per_op[dom]["in_step"]["us_median"] if "in_step" in per_op[dom] else None,
+            "in_step_eager_frac": per_op[dom]["in_step_eager"]["frac"],
             "cold_frac": per_op[dom]["cold"]["frac"], "cold_launch_us": per_op[dom]["cold"]["us_median"],
             "note": ("frac: median launch of graphs of 8 back-to-back launches (warm); in_step_frac: the kernel "
-                     "inside eager steps enqueued back to back; cold_frac: one launch after a 1 GiB read that "
-                     "evicts L2 and MALL")}
+                     "inside graph-replayed steps, from the rocprofv3 trace in profiles/kernel_trace_<workload>.json "
+                     "(null when the kernel sources differ from the traced ones); in_step_eager_frac: the op inside "
+                     "eager steps with an event between consecutive ops, the event packet's gap included; "
+                     "cold_frac: one launch after a 1 GiB read that evicts L2 and MALL")}
 
     result = {
         "metric": METRIC,
@@ -421,10 +444,12 @@ def main() -> int:
         "fwd_dispatch_combine_tokens_per_s": round(T / (fwd_us * 1e-6), 1),
         "ops": per_op,
         "ops_note": ("us (median), us_mean, us_p10, us_p90, GBps, frac: warm, graphs of 8 back-to-back launches, "
-                     f"{OP_WARMUP} untimed replays then {REPS} timed; in_step: the op inside eager steps "
-                     f"enqueued back to back ({IN_STEP_STEPS} steps, the first 2 dropped), an event between "
-                     f"consecutive ops; cold: one launch after an untimed read of 1 GiB that evicts L2 and MALL "
-                     f"({COLD_REPS} reps); frac_of_copy: against torch's 1 GiB device copy; GBps and frac use "
+                     f"{OP_WARMUP} untimed replays then {REPS} timed; in_step: the op's kernels inside graph-replayed "
+                     "steps, from the rocprofv3 kernel trace committed under profiles/ (only while the kernel "
+                     "sources match it); in_step_eager: the op inside eager steps enqueued back to back "
+                     f"({IN_STEP_STEPS} steps, the first 2 dropped), an event between consecutive ops, whose packet "
+                     "adds a gap of about 5.6 us to each op; cold: one launch after an untimed read of 1 GiB "
+                     f"that evicts L2 and MALL ({COLD_REPS} reps); frac_of_copy: against torch's 1 GiB device copy; GBps and frac use "
                      "the medians"),
         "copy_context_GBps": round(copy_gbps, 1),
         "overflow_flags": flags,
