@@ -14,7 +14,16 @@
 // The token is quantized once (VALU only: there is no contraction here for
 // MFMA), then its bytes are written to each of the token's K' rows: 8 code
 // bytes per block per lane (512 contiguous bytes per wave store), one scale
-// byte per block.  Small batches of wide rows instead take one workgroup
+// byte per block.  The code stores are nontemporal, as the bf16 dispatch's:
+// with plain ones the 117 MB of codes at DeepSeek-V3 size waited dirty in
+// the MALL and the next kernels wrote them back.  Measured on MI355X
+// (graphs of the whole step, interleaved builds): DeepSeek-V3 step 413.4 ->
+// 410.2 us, skewed 465.0 -> 452.0, NVFP4 workload 454.9 -> 451.9, capacity
+// 204.8 -> 202.9 us, while the kernel alone got slower (29.6 -> 32.8 us
+// back to back, 34.0 -> 36.7 us after a cache flush).  A consumer that
+// read the codes right away would find them in the MALL with plain stores.
+// Nontemporal scale stores as well cost more than they gave (step 412.5).
+// Small batches of wide rows instead take one workgroup
 // of 8 waves per token (k_nvfp4_wg): the row is quantized into LDS once and
 // each wave stores whole slot rows with 16-byte code and 4-byte scale
 // stores.
@@ -43,6 +52,12 @@ namespace {
 constexpr int kQuantThreads = 256;
 constexpr int kQuantWaves = kQuantThreads / kWave;
 constexpr int kMaxBlocksPerLane = 16;  // H <= 16 * 64 * 16 = 16384
+#ifndef EPX_NVFP4_NT_CODES
+#define EPX_NVFP4_NT_CODES 1
+#endif
+#ifndef EPX_NVFP4_NT_SCALES
+#define EPX_NVFP4_NT_SCALES 0
+#endif
 #ifndef EPX_NVFP4_SMALL_BATCH
 #define EPX_NVFP4_SMALL_BATCH 4096
 #endif
@@ -184,8 +199,17 @@ __global__ __launch_bounds__(kQuantThreads) void k_nvfp4(Nvfp4Args a) {
         for (int i = 0; i < NBL; ++i) {
             const int32_t b = b0 + i * kWave * W;
             if (b < nblk) {
+#if EPX_NVFP4_NT_CODES
+                typedef uint32_t v2u_t __attribute__((ext_vector_type(2)));
+                __builtin_nontemporal_store(v2u_t{code[i].x, code[i].y}, reinterpret_cast<v2u_t*>(crow + 8 * (int64_t)b));
+#else
                 *reinterpret_cast<uint2*>(crow + 8 * (int64_t)b) = code[i];
+#endif
+#if EPX_NVFP4_NT_SCALES
+                __builtin_nontemporal_store((uint8_t)sc[i], srow + b);
+#else
                 srow[b] = (uint8_t)sc[i];
+#endif
             }
         }
         if (part == 0 && lane == 0) a.rowscale[row] = (uint16_t)rs;
