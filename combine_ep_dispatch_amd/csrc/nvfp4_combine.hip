@@ -76,6 +76,9 @@ __global__ __launch_bounds__(kCqThreads) void k_combine_nvfp4(CombineNvfp4Args a
     const int32_t r_raw = a.token_row[(int64_t)t * a.Kp + min(lane, a.Kp - 1)];
     float w_lane = 1.0f;
     if (WEIGHTED) w_lane = a.probs[(int64_t)t * a.K + min(lane, a.K - 1)];
+    // Left to itself the scheduler tests the row before it sends the weight
+    // load: two round trips before the payload loads can start.
+    __builtin_amdgcn_sched_barrier(0);
     const int32_t my_row = (lane < a.Kp && r_raw >= 0 && r_raw < a.R) ? r_raw : -1;
     const float my_w = my_row < 0 ? 0.0f : (lane < a.K ? w_lane : 1.0f);
 
@@ -95,9 +98,14 @@ __global__ __launch_bounds__(kCqThreads) void k_combine_nvfp4(CombineNvfp4Args a
                 const_cast<uint8_t*>(a.codes + r * cstride), (short)0, valid ? cstride : 0, kBufferFlags);
             const __amdgpu_buffer_rsrc_t rsc = __builtin_amdgcn_make_buffer_rsrc(
                 const_cast<uint8_t*>(a.scales + r * nblk), (short)0, valid ? nblk : 0, kBufferFlags);
+            // the row's rowscale through an empty descriptor as well: a
+            // conditional load here would be waited on at once, with the
+            // loads of the earlier slots, one round trip per slot
+            const __amdgpu_buffer_rsrc_t rrs = __builtin_amdgcn_make_buffer_rsrc(
+                const_cast<uint16_t*>(a.rowscale + r), (short)0, valid ? 2 : 0, kBufferFlags);
             cw[kk] = __builtin_amdgcn_raw_buffer_load_b64(rc, 8 * b, 0, 0);
             sc[kk] = __builtin_amdgcn_raw_buffer_load_b8(rsc, b, 0, 0);
-            rs[kk] = valid ? (uint32_t)a.rowscale[r] : 0u;
+            rs[kk] = __builtin_amdgcn_raw_buffer_load_b16(rrs, 0, 0, 0);
         }
 #pragma unroll
         for (int kk = 0; kk < kCqBatch; ++kk) {

@@ -151,14 +151,16 @@ EDGE = {
     "direct_254_tiles": dict(T=65000, S=4, E_loc=16, K=8, H=16, A=2, bad_p=0.01),  # direct path, near its tile limit
     "lookback_274_tiles": dict(T=70001, S=4, E_loc=16, K=8, H=16, A=2, shared=1, src=3, bad_p=0.01),  # look-back path
     "single_pass_max_groups": dict(T=128, S=8, E_loc=255, K=8, shared=1, A=4, H=32),  # 2048 groups, one launch
-    "single_pass_1024": dict(T=128, S=8, E_loc=32, K=8, H=64, A=128, shared=1, src=5),  # largest one-launch layout
-    "single_pass_1023": dict(T=1023, S=4, E_loc=8, K=1, H=16, A=4),                   # one slot under it
-    "direct_1025": dict(T=1025, S=4, E_loc=8, K=1, H=16, A=4, bad_p=0.01),            # one slot past it: two launches
-    "direct_2048": dict(T=256, S=8, E_loc=32, K=8, H=64, A=128, shared=1, src=5),     # decode batch, two launches
+    "single_pass_1024": dict(T=128, S=8, E_loc=32, K=8, H=64, A=128, shared=1, src=5),  # 1024 slots: count path
+    "single_pass_1023": dict(T=1023, S=4, E_loc=8, K=1, H=16, A=4),                   # count path, ragged tile
+    "direct_1025": dict(T=1025, S=4, E_loc=8, K=1, H=16, A=4, bad_p=0.01),            # count path, 5 tiles
+    "direct_2048": dict(T=256, S=8, E_loc=32, K=8, H=64, A=128, shared=1, src=5),     # decode batch, count path
     "single_pass_256": dict(T=64, S=2, E_loc=16, K=4, H=32, A=8, mask_p=0.1),         # 1 slot/thread bound
     "single_pass_257": dict(T=257, S=4, E_loc=4, K=1, H=32, A=2),                     # 2 slots/thread
-    "single_pass_512": dict(T=128, S=2, E_loc=16, K=4, H=32, A=8, bad_p=0.02),        # 2 slots/thread bound
-    "single_pass_513": dict(T=171, S=3, E_loc=5, K=3, H=32, A=2, mask_p=0.2),         # 4 slots/thread
+    "single_pass_512": dict(T=128, S=2, E_loc=16, K=4, H=32, A=8, bad_p=0.02),        # small path bound
+    "single_pass_513": dict(T=171, S=3, E_loc=5, K=3, H=32, A=2, mask_p=0.2),         # one past it: count path
+    "count_8192": dict(T=1024, S=8, E_loc=32, K=8, H=64, A=128, mask_p=0.05),        # count path bound
+    "direct_8193": dict(T=8193, S=4, E_loc=8, K=1, H=16, A=4, bad_p=0.01),            # one past it: two kernels
     "slots_64": dict(T=300, S=1, E_loc=64, K=63, shared=1, src=0, H=64, A=4),  # K' = 64: 16 scatter slot blocks
     "hidden_8": dict(T=500, S=2, E_loc=4, K=3, H=8),                          # one ragged piece per row
     "hidden_16k": dict(T=300, S=2, E_loc=4, K=4, H=16384, A=8),               # 8 full pieces, 16 NVFP4 blocks per lane
