@@ -121,18 +121,21 @@ __device__ __forceinline__ v4u load_scatter_src(const v4u* p) {
 #endif
 }
 
+constexpr int kBufferWord3 = 0x00020000;  // buffer descriptor word 3: 32-bit data, raw addressing
+constexpr int kCachePolicyNt = 2;         // buffer load/store cache-policy bit: nontemporal
+
 // 16-byte store to vector v of a wave-uniform row base through a buffer
 // descriptor carrying the cache-policy bits AUX.
 template <int AUX>
 __device__ __forceinline__ void store_policy(v4u* row, int32_t v, int32_t row_bytes, v4u val) {
-    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(row, (short)0, row_bytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(row, (short)0, row_bytes, kBufferWord3);
     __builtin_amdgcn_raw_buffer_store_b128(val, rs, v * 16, 0, AUX);
 }
 
 template <int AUX>
 __device__ __forceinline__ v4u load_policy(const v4u* row, int32_t v, int32_t row_bytes) {
     const __amdgpu_buffer_rsrc_t rs =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<v4u*>(row), (short)0, row_bytes, 0x00020000);
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<v4u*>(row), (short)0, row_bytes, kBufferWord3);
     return __builtin_amdgcn_raw_buffer_load_b128(rs, v * 16, 0, AUX);
 }
 
@@ -372,10 +375,24 @@ __global__ __launch_bounds__(kMoveThreads) void k_probs_grad(MoveArgs a, int32_t
         for (int32_t v = threadIdx.x; v < Hv; v += kMoveThreads) {
             const v4u g = gy[v];
             const uint32_t gq[4] = {g.x, g.y, g.z, g.w};
+            // Every slot's load goes out before any is used: under a
+            // per-slot branch the compiler waited on each load in turn.  A
+            // masked or dropped slot loads through an empty descriptor (no
+            // memory access, zeros) and is skipped below.
+            v4u ov[kSlotBatch];
+#pragma unroll
+            for (int kk = 0; kk < kSlotBatch; ++kk) {
+                const bool valid = rows[kk] >= 0;
+                const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+                    const_cast<v4u*>(out + (int64_t)(valid ? rows[kk] : 0) * Hv), (short)0, valid ? Hv * 16 : 0,
+                    kBufferWord3);
+                ov[kk] = __builtin_amdgcn_raw_buffer_load_b128(rs, v * 16, 0, kCachePolicyNt);
+            }
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int kk = 0; kk < kSlotBatch; ++kk) {
                 if (rows[kk] < 0) continue;
-                const v4u o = load_stream(out + (int64_t)rows[kk] * Hv + v);
+                const v4u o = ov[kk];
                 const uint32_t oq[4] = {o.x, o.y, o.z, o.w};
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
