@@ -73,16 +73,22 @@ __device__ __forceinline__ uint32_t codes4_hw(uint32_t w0, uint32_t w1, float in
 }
 
 // Iteration `it` of a row: 8 blocks of 128 elements, block it*8 + lane/8
-// in lanes 8j..8j+7, 16 elements per lane (one 2 KiB wave load).  Gives this
-// lane's 16 codes and its block's scale (the same in all 8 lanes).
-__device__ __forceinline__ void quantize_iteration(const uint4* xr, int32_t it, int lane, int32_t nblk, uint4& code,
-                                                   float& scale) {
+// in lanes 8j..8j+7, 16 elements per lane (one 2 KiB wave load).
+// load_iteration fetches this lane's 16 elements (zeros past the last
+// block); quantize_loaded gives its 16 codes and its block's scale (the
+// same in all 8 lanes).
+__device__ __forceinline__ void load_iteration(const uint4* xr, int32_t it, int lane, int32_t nblk, uint4& p,
+                                               uint4& q) {
     const int32_t b = it * 8 + lane / 8;  // this lane's block
-    uint4 p = make_uint4(0, 0, 0, 0), q = make_uint4(0, 0, 0, 0);
+    p = make_uint4(0, 0, 0, 0);
+    q = make_uint4(0, 0, 0, 0);
     if (b < nblk) {
         p = xr[128 * it + 2 * lane];
         q = xr[128 * it + 2 * lane + 1];
     }
+}
+
+__device__ __forceinline__ void quantize_loaded(uint4 p, uint4 q, uint4& code, float& scale) {
     uint32_t m = absmax16(p, q);
     m = max(m, (uint32_t)__shfl_xor((int)m, 4, kWave));
     m = max(m, (uint32_t)__shfl_xor((int)m, 2, kWave));
@@ -108,6 +114,13 @@ __device__ __forceinline__ void quantize_iteration(const uint4* xr, int32_t it, 
     scale = amax / 448.0f;
 }
 
+__device__ __forceinline__ void quantize_iteration(const uint4* xr, int32_t it, int lane, int32_t nblk, uint4& code,
+                                                   float& scale) {
+    uint4 p, q;
+    load_iteration(xr, it, lane, nblk, p, q);
+    quantize_loaded(p, q, code, scale);
+}
+
 // W waves per token (1, or 4 for small batches): wave `part` takes the
 // iterations part, part + W, ...  A 128-element block lives in 8 lanes of
 // one wave, so the waves of a token never exchange anything.
@@ -120,15 +133,24 @@ __global__ __launch_bounds__(kFp8Threads) void k_fp8(Fp8Args a) {
     const int lane = threadIdx.x & (kWave - 1);
     const int32_t nblk = a.H / 128;
     const uint4* xr = reinterpret_cast<const uint4*>(a.x + (int64_t)t * a.H);
+    // The token's K' rows, lane k holding slot k, loaded before the row is
+    // quantized so that the store loop issues no load (a load there is
+    // waited on together with the previous slot's stores).
+    const int32_t my_row = lane < a.Kp ? a.token_row[(int64_t)t * a.Kp + lane] : -1;
 
+    // every iteration's loads go out before the first is quantized (one
+    // round trip per token, not one per iteration)
+    uint4 p[NIT], q[NIT];
+#pragma unroll
+    for (int j = 0; j < NIT; ++j) load_iteration(xr, part + j * W, lane, nblk, p[j], q[j]);
+    __builtin_amdgcn_sched_barrier(0);
     uint4 code[NIT];
     float scale[NIT];
 #pragma unroll
-    for (int j = 0; j < NIT; ++j) quantize_iteration(xr, part + j * W, lane, nblk, code[j], scale[j]);
+    for (int j = 0; j < NIT; ++j) quantize_loaded(p[j], q[j], code[j], scale[j]);
 
-    const int32_t* tr = a.token_row + (int64_t)t * a.Kp;
     for (int32_t k = 0; k < a.Kp; ++k) {
-        const int32_t row = tr[k];
+        const int32_t row = __builtin_amdgcn_readlane(my_row, k);
         if (row < 0 || row >= a.R) continue;
         uint4* crow = reinterpret_cast<uint4*>(a.codes + (int64_t)row * a.H);
         float* srow = a.scales + (int64_t)row * nblk;

@@ -144,6 +144,10 @@ __global__ __launch_bounds__(kQuantThreads) void k_nvfp4(Nvfp4Args a) {
     const int32_t nblk = a.H / 16;
     const uint4* xr = reinterpret_cast<const uint4*>(a.x + (int64_t)t * a.H);
     const int32_t b0 = part * kWave + lane;  // this lane's first block
+    // The token's K' rows, lane k holding slot k, loaded with the row so
+    // that the store loop below issues no load: a load there is waited on
+    // together with the previous slot's stores (one round trip per slot).
+    const int32_t my_row = lane < a.Kp ? a.token_row[(int64_t)t * a.Kp + lane] : -1;
 
     uint4 q[NBL][2];
     uint32_t bmax[NBL];
@@ -189,9 +193,8 @@ __global__ __launch_bounds__(kQuantThreads) void k_nvfp4(Nvfp4Args a) {
     }
 
     const int64_t cstride = a.H / 2, sstride = nblk;
-    const int32_t* tr = a.token_row + (int64_t)t * a.Kp;
     for (int32_t k = 0; k < a.Kp; ++k) {
-        const int32_t row = tr[k];
+        const int32_t row = __builtin_amdgcn_readlane(my_row, k);
         if (row < 0 || row >= a.R) continue;
         uint8_t* crow = a.codes + (int64_t)row * cstride;
         uint8_t* srow = a.scales + (int64_t)row * sstride;
