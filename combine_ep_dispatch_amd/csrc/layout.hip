@@ -80,22 +80,28 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout_hist(LayoutArgs a) {
     __shared__ int32_t s_hist[EP_MAX_GROUPS];
     __shared__ int32_t s_gof[EP_MAX_GROUPS];  // group of each routed expert
     const int tid = threadIdx.x;
+    const int64_t routed = (int64_t)a.T * a.K;
+    const int nbits = 32 - __clz(a.NG);  // keys live in [0, NG]; NG = "no group"
+    const int64_t base = (int64_t)blockIdx.x * kTileSlots;
+    // All of the tile's ids are loaded first, so that their latency hides
+    // behind the LDS set-up and they cost one round trip, not one per slot
+    // per thread.
+    int32_t eid[SPT];
+#pragma unroll
+    for (int it = 0; it < SPT; ++it) {
+        const int64_t f = base + it * kLayoutThreads + tid;
+        eid[it] = f < routed ? a.topk_ids[f] : -1;
+    }
     for (int g = tid; g < a.NG; g += kLayoutThreads) s_hist[g] = 0;
     for (int e = tid; e < a.E; e += kLayoutThreads)
         s_gof[e] = (e / a.E_loc) * a.G + a.shared + (e % a.E_loc);
     __syncthreads();
 
-    const int64_t routed = (int64_t)a.T * a.K;
-    const int nbits = 32 - __clz(a.NG);  // keys live in [0, NG]; NG = "no group"
-    const int64_t base = (int64_t)blockIdx.x * kTileSlots;
 #pragma unroll
     for (int it = 0; it < SPT; ++it) {
-        const int64_t f = base + it * kLayoutThreads + tid;
+        const int32_t e = eid[it];
         uint32_t key = (uint32_t)a.NG;
-        if (f < routed) {
-            const int32_t e = a.topk_ids[f];
-            if ((uint32_t)e < (uint32_t)a.E) key = (uint32_t)s_gof[e];
-        }
+        if ((uint32_t)e < (uint32_t)a.E) key = (uint32_t)s_gof[e];
         const uint64_t m = match_any(key, nbits);
         if (key != (uint32_t)a.NG && lanes_below(m) == 0)
             atomicAdd(&s_hist[key], (int32_t)__popcll(m));
