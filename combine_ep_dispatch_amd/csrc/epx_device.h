@@ -79,6 +79,11 @@ constexpr int64_t kSmallMaxSlots = EPX_SMALL_MAX_SLOTS;
 // count of all slots then costs more than the second launch), 16.3 against
 // 11.5 at 32768.
 constexpr int64_t kCountMaxSlots = 8192;
+// Forced with EP_LAYOUT_COUNT the path takes at most this many routed slots:
+// every one of its (slots / 256) workgroups counts every slot, so its cost
+// grows with the square of the batch (262 144 slots: 1024 workgroups of
+// 262 144 LDS additions each).
+constexpr int64_t kCountForcedMaxSlots = int64_t(1) << 18;
 
 // Layout kernel paths.
 constexpr int kLayoutSinglePass = 0;  // k_layout_sp: ticketed tiles, decoupled look-back

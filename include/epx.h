@@ -76,7 +76,10 @@ extern "C" {
 #define EP_LAYOUT_BARRIER 8u   /* one kernel: ticketed tiles, each tile's prefix
                                   from one read of every tile's counts */
 #define EP_LAYOUT_COUNT 16u    /* one kernel: every workgroup counts every
-                                  routed slot (no workspace traffic) */
+                                  routed slot (no workspace traffic); at
+                                  most 2^18 routed slots (T*K), else
+                                  EP_EINVAL: its cost grows with the square
+                                  of the batch */
 
 /* Bits of the device flags word (ep_layout_t.flags[0]). */
 #define EP_FLAG_DROPPED 1      /* a slot was dropped at segment capacity [TD]  */

@@ -54,6 +54,7 @@ def sentinel_layout(cfg: epx.EpConfig) -> epx.Layout:
 LAYOUT_PATHS = {"single-pass": epx.EP_LAYOUT_LOOKBACK, "single-pass-barrier": epx.EP_LAYOUT_BARRIER,
                 "two-kernel": epx.EP_LAYOUT_DIRECT, "count": epx.EP_LAYOUT_COUNT, "default": 0}
 PATH_FLAGS = epx.EP_LAYOUT_LOOKBACK | epx.EP_LAYOUT_DIRECT | epx.EP_LAYOUT_BARRIER | epx.EP_LAYOUT_COUNT
+COUNT_FORCED_MAX_SLOTS = 1 << 18  # routed slots EP_LAYOUT_COUNT accepts
 
 
 def gpu_layout(cfg: epx.EpConfig, ids: np.ndarray, ws=None, path=None) -> epx.Layout:
@@ -202,10 +203,13 @@ def check_layout(c: Case, name: str) -> epx.Layout:
     say(f"[gpu] layout {name}: T={c.cfg.num_tokens} E={c.cfg.num_experts} S={c.cfg.num_segments} "
         f"K={c.cfg.top_k} A={c.cfg.align} C={c.cfg.seg_capacity} shared={c.cfg.shared_expert} "
         f"R={c.cfg.recv_rows}")
-    # Every layout path (single pass, two kernels, and whichever the size
-    # selects by default) must give the oracle's layout; the default one is
-    # returned.
-    for path in ("single-pass", "single-pass-barrier", "two-kernel"):
+    # Every layout path (single pass, two kernels, count, and whichever the
+    # size selects by default) must give the oracle's layout; the default
+    # one is returned.  The count path takes at most 2^18 routed slots.
+    paths = ["single-pass", "single-pass-barrier", "two-kernel"]
+    if c.cfg.num_tokens * c.cfg.top_k <= COUNT_FORCED_MAX_SLOTS:
+        paths.append("count")
+    for path in paths:
         assert_layout_equal(layout_np(gpu_layout(c.cfg, c.ids, path=path)), c.L, f"{name} ({path})")
     lay = gpu_layout(c.cfg, c.ids)
     assert_layout_equal(layout_np(lay), c.L, name)

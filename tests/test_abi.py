@@ -176,6 +176,7 @@ INVALID = [
     dict(shared_expert=2), dict(shared_expert=1, src_segment=2), dict(shared_expert=1, src_segment=-1),
     dict(flags=6), dict(flags=7), dict(flags=10), dict(flags=12), dict(flags=14), dict(flags=18), dict(flags=20),
     dict(flags=24), dict(flags=32),
+    dict(flags=16, num_tokens=(1 << 15) + 1, top_k=8),  # forced count path past 2^18 routed slots
     dict(num_experts=4096, num_segments=2),  # > EP_MAX_GROUPS groups
     dict(num_tokens=1 << 28, top_k=4),  # 2^30 slots
     # capacity mode: the unclamped aligned offsets (summed in int32 before the
@@ -200,6 +201,14 @@ def test_query_accepts_documented_flags(L, flags):
 
     assert (EP_ZERO_PAD_ROWS, EP_LAYOUT_LOOKBACK, EP_LAYOUT_DIRECT, EP_LAYOUT_BARRIER, EP_LAYOUT_COUNT) == (1, 2, 4, 8, 16)
     assert query(L, cfg(flags=flags))[0] == 0
+
+
+def test_forced_count_path_bound(L):
+    """EP_LAYOUT_COUNT takes at most 2^18 routed slots (its cost grows with
+    the square of the batch); the default choice has no such bound."""
+    assert query(L, cfg(flags=16, num_tokens=1 << 15, top_k=8))[0] == 0
+    assert query(L, cfg(flags=16, num_tokens=(1 << 15) + 1, top_k=8))[0] == -1
+    assert query(L, cfg(flags=0, num_tokens=(1 << 15) + 1, top_k=8))[0] == 0
 
 
 def test_null_config_and_reserved_fields(L):
