@@ -63,6 +63,10 @@
 namespace epx {
 namespace {
 
+#ifndef EPX_DIRECT_QUADS
+#define EPX_DIRECT_QUADS 1
+#endif
+
 // A wait on another workgroup gives up (EP_FLAG_INTERNAL) once the
 // workgroup has run this many ticks of the 100 MHz wall clock (about 0.34 s);
 // every later wait of the workgroup then gives up at once, so a call whose
@@ -201,7 +205,62 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout_rank(LayoutArgs a) {
         for (int g = tid; g < NG; g += kLayoutThreads)
             s_cnt[g] = s_cnt[g] + s_pref[g] + (g == shared_group ? a.T : 0);
     }
-    if (DIRECT) {
+    if (DIRECT && EPX_DIRECT_QUADS && (NG & 3) == 0 && NG <= 128) {
+        // Group totals and this tile's in-group prefix from the [tile][group]
+        // table, four groups per 16-byte load (rows are 16-byte aligned when
+        // NG % 4 == 0).  tpq (a power of two, tpq * NG / 4 <= 256, at most a
+        // wave) lanes share a quad of groups: lane r sums tiles r, r + tpq,
+        // ...; with 16 loads in flight per lane that is one round trip for
+        // up to 16 * tpq tiles (the same as the one-group-per-load form below
+        // wherever that bounds the tile size; at least 256 otherwise), with
+        // a quarter of its load instructions.  Measured on MI355X against
+        // that form: skewed (128 groups) 14.4 -> 14.0 us, capacity (64)
+        // 20.0 -> 19.4 us; with 256 groups (4 lanes per quad, so a wave
+        // load spans 4 table rows) 10.5 -> 11.1 us, so only up to 128.
+        constexpr int kBatch4 = kDirectBatch / 4;
+        const int Q = NG / 4;
+        const int tpq = min(4 * direct_lanes_per_group(NG), kWave);  // a quad's lanes stay in one wave
+        const int r = tid & (tpq - 1);
+        const uint4* table = reinterpret_cast<const uint4*>(a.desc);
+        for (int q = tid / tpq; q < Q; q += kLayoutThreads / tpq) {
+            int32_t tot[4] = {0, 0, 0, 0}, pre[4] = {0, 0, 0, 0};
+            for (int j0 = r; j0 < a.tiles; j0 += kBatch4 * tpq) {
+                uint4 v[kBatch4];
+#pragma unroll
+                for (int i = 0; i < kBatch4; ++i) {
+                    const int j = j0 + i * tpq;
+                    v[i] = table[(uint32_t)min(j, a.tiles - 1) * (uint32_t)Q + (uint32_t)q];
+                }
+                __builtin_amdgcn_sched_barrier(0);  // the whole batch in flight first (see below)
+#pragma unroll
+                for (int i = 0; i < kBatch4; ++i) {
+                    const int j = j0 + i * tpq;
+                    const bool in = j < a.tiles, before = j < (int)tile;
+                    const int32_t n[4] = {(int32_t)v[i].x, (int32_t)v[i].y, (int32_t)v[i].z, (int32_t)v[i].w};
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) {
+                        tot[c] += in ? n[c] : 0;
+                        pre[c] += before ? n[c] : 0;
+                    }
+                }
+            }
+            for (int o = 1; o < tpq; o <<= 1) {
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    tot[c] += __shfl_xor(tot[c], o, kWave);
+                    pre[c] += __shfl_xor(pre[c], o, kWave);
+                }
+            }
+            if (r == 0) {
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const int g = 4 * q + c;
+                    s_cnt[g] = tot[c] + (g == shared_group ? a.T : 0);
+                    s_pref[g] = pre[c];
+                }
+            }
+        }
+    } else if (DIRECT) {
         // Group totals and this tile's in-group prefix from the [tile][group]
         // table.  tpg (a power of two, tpg * NG <= 256) lanes share a group:
         // lane r of the group sums tiles r, r + tpg, ...; with 64 loads in
