@@ -20,7 +20,8 @@
 // ranks the one tile to learn the group totals, workgroup 0 writes the
 // per-slot results and the others spread the groups' metadata runs.
 //
-// Count (default up to 8192 routed slots, any size with EP_LAYOUT_COUNT):
+// Count (default up to 8192 routed slots, forced with EP_LAYOUT_COUNT up to
+// 2^18):
 // k_layout_rank alone; every workgroup counts all routed slots into LDS
 // counters per group (those before its tile apart: its in-group prefix),
 // then ranks its own tile of 256 slots as the two-kernel path does.
@@ -36,7 +37,8 @@
 //  2. k_layout_rank   every workgroup reads, for each group, the group's
 //                     column of tile counts (lanes over groups, so wave loads
 //                     are contiguous; 64 loads in flight per lane, and several
-//                     lanes per group when groups are few) and sums it twice:
+//                     lanes per group when groups are few; four groups per
+//                     16-byte load up to 128 groups) and sums it twice:
 //                     over all tiles (the group total) and over the tiles
 //                     before its own (its in-group prefix).  No workgroup
 //                     waits on another, and there are no atomics on global
