@@ -7,26 +7,29 @@
 // 2688 = 448 * 6: the largest finite E4M3 block scale times the largest
 // E2M1 magnitude, so the block that holds rowmax gets scale 448.
 //
-// One wave64 per token (four for batches under kSmallBatchTokens).  Lane l
-// holds 16-element blocks l, l+64, ... of the row in registers (two 16-byte
-// loads per block), so a block's amax is lane-local and the row max is one
-// wave reduction (plus an LDS exchange when a token has several waves).
-// The token is quantized once (VALU only: there is no contraction here for
-// MFMA), then its bytes are written to each of the token's K' rows: 8 code
-// bytes per block per lane (512 contiguous bytes per wave store), one scale
-// byte per block.  The code stores are nontemporal, as the bf16 dispatch's:
-// with plain ones the 117 MB of codes at DeepSeek-V3 size waited dirty in
-// the MALL and the next kernels wrote them back.  Measured on MI355X
-// (graphs of the whole step, interleaved builds): DeepSeek-V3 step 413.4 ->
-// 410.2 us, skewed 465.0 -> 452.0, NVFP4 workload 454.9 -> 451.9, capacity
-// 204.8 -> 202.9 us, while the kernel alone got slower (29.6 -> 32.8 us
-// back to back, 34.0 -> 36.7 us after a cache flush).  A consumer that
-// read the codes right away would find them in the MALL with plain stores.
-// Nontemporal scale stores as well cost more than they gave (step 412.5).
-// Small batches of wide rows instead take one workgroup
-// of 8 waves per token (k_nvfp4_wg): the row is quantized into LDS once and
-// each wave stores whole slot rows with 16-byte code and 4-byte scale
-// stores.
+// Rows of H % 64 == 0 with at least 256 blocks (every named workload but
+// the narrow capacity one) take one workgroup of 8 waves per token
+// (k_nvfp4_wg): the row is quantized into LDS once and each wave stores
+// whole slot rows with 16-byte code and 4-byte scale stores.  Other rows
+// take one wave64 per token (four for batches under kSmallBatchTokens,
+// k_nvfp4): lane l holds 16-element blocks l, l+64, ... of the row in
+// registers (two 16-byte loads per block), so a block's amax is
+// lane-local and the row max is one wave reduction (plus an LDS exchange
+// when a token has several waves); its bytes then go to each of the
+// token's K' rows, 8 code bytes per block per lane (512 contiguous bytes
+// per wave store) and one scale byte per block.  The token is quantized
+// once (VALU only: there is no contraction here for MFMA).
+// The code stores are nontemporal, as the bf16 dispatch's: with plain ones
+// the 117 MB of codes at DeepSeek-V3 size waited dirty in the MALL and the
+// next kernels wrote them back.  Measured on MI355X with one wave per
+// token (graphs of the whole step, interleaved builds): DeepSeek-V3 step
+// 413.4 -> 410.2 us, skewed 465.0 -> 452.0, NVFP4 workload 454.9 ->
+// 451.9, capacity 204.8 -> 202.9 us, while that kernel alone got slower
+// (29.6 -> 32.8 us back to back, 34.0 -> 36.7 us after a cache flush); the
+// workgroup form with nontemporal codes then took the DeepSeek-V3 step to
+// 407.6 us and the kernel back to 29.8 us.  A consumer that read the codes
+// right away would find them in the MALL with plain stores.  Nontemporal
+// scale stores as well cost more than they gave (step 412.5).
 //
 // Arithmetic is IEEE binary32 with round-to-nearest-even everywhere; the
 // library is built with correctly rounded division and without FMA
@@ -222,6 +225,9 @@ __global__ __launch_bounds__(kQuantThreads) void k_nvfp4(Nvfp4Args a) {
 #ifndef EPX_NVFP4_WG
 #define EPX_NVFP4_WG 1
 #endif
+#ifndef EPX_NVFP4_WG_NT
+#define EPX_NVFP4_WG_NT 1
+#endif
 constexpr int kWgWaves = 8;
 constexpr int kWgMaxBlocks = 16 * kWave;  // H <= 16384: 1024 blocks
 
@@ -229,7 +235,8 @@ constexpr int kWgMaxBlocks = 16 * kWave;  // H <= 16384: 1024 blocks
 // 256 blocks): lane l of wave w holds blocks w*64 + l + i*512; the row max
 // meets in LDS, the codes and scales are quantized into LDS once, then wave
 // w stores the codes, scales and rowscale of slots w, w + 8, ... with
-// 16-byte code and 4-byte scale stores.
+// 16-byte code stores (nontemporal, as in k_nvfp4) and 4-byte scale
+// stores.
 template <int NB>
 __global__ __launch_bounds__(kWgWaves * kWave) void k_nvfp4_wg(Nvfp4Args a) {
     // Declared as 16- and 4-byte words so that the stores below can read
@@ -290,7 +297,15 @@ __global__ __launch_bounds__(kWgWaves * kWave) void k_nvfp4_wg(Nvfp4Args a) {
         if (row < 0 || row >= a.R) continue;
         uint4* crow = reinterpret_cast<uint4*>(a.codes + (int64_t)row * (a.H / 2));
         uint32_t* srow = reinterpret_cast<uint32_t*>(a.scales + (int64_t)row * nblk);
+#if EPX_NVFP4_WG_NT
+        typedef uint32_t v4u_t __attribute__((ext_vector_type(4)));
+        for (int32_t v = lane; v < cvec; v += kWave) {
+            const uint4 c = s_code4[v];
+            __builtin_nontemporal_store(v4u_t{c.x, c.y, c.z, c.w}, reinterpret_cast<v4u_t*>(crow + v));
+        }
+#else
         for (int32_t v = lane; v < cvec; v += kWave) crow[v] = s_code4[v];
+#endif
         for (int32_t v = lane; v < swords; v += kWave) srow[v] = s_sc4[v];
         if (lane == 0) a.rowscale[row] = rs;
     }
@@ -311,13 +326,17 @@ int nvfp4_max_hidden() { return 16 * kWave * kMaxBlocksPerLane; }
 hipError_t launch_nvfp4(const Nvfp4Args& a, hipStream_t stream) {
     if (a.T == 0) return hipSuccess;
     const int32_t nblk = a.H / 16;
-    // Batches under kSmallBatchTokens, rows of H % 64 == 0 with at least
-    // 256 blocks and 4-byte aligned scales: one workgroup of 8 waves per
-    // token.  At DeepSeek-V3 dims T = 128 went from 5.7 to 4.3 us and
-    // T = 1024 from 10.8 to 9.4 us; at T = 4096 one wave per token stays
-    // faster (29.6 against 30.8 us; skewed workload 33.1 against 34.8).
-    if (EPX_NVFP4_WG && a.T < kSmallBatchTokens && a.H % 64 == 0 && nblk >= 4 * kWave &&
-        (reinterpret_cast<uintptr_t>(a.scales) & 3) == 0) {
+    // Rows of H % 64 == 0 with at least 256 blocks and 4-byte aligned
+    // scales, batches within its grid (2^23 tokens): one workgroup of 8
+    // waves per token.  At DeepSeek-V3 dims T = 128 went from 5.7 to 4.3 us
+    // and T = 1024 from 10.8 to 9.4 us against one wave per token.  With
+    // plain code stores one wave per token stayed faster at T = 4096 (29.6
+    // against 30.8 us); with nontemporal code stores in both the workgroup
+    // form wins there too: 29.8 against 32.4 us, the whole step 407.6
+    // against 411.3 us (NVFP4 workload 448.1 against 449.9 us, skewed equal,
+    // T = 2048 15.1 against 16.7 us).
+    if (EPX_NVFP4_WG && a.H % 64 == 0 && nblk >= 4 * kWave && (reinterpret_cast<uintptr_t>(a.scales) & 3) == 0 &&
+        (int64_t)a.T * kWgWaves * kWave <= 0xFFFFFFFFll) {
         const int nb = (nblk + kWgWaves * kWave - 1) / (kWgWaves * kWave);  // blocks per lane
         if (nb == 1)
             hipLaunchKernelGGL(k_nvfp4_wg<1>, dim3((unsigned)a.T), dim3(kWgWaves * kWave), 0, stream, a);
