@@ -212,6 +212,20 @@ __device__ __forceinline__ uint32_t lanes_below(uint64_t m) {
                                      __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
 }
 
+// Inclusive sum over lanes 0..lane of the wave, by DPP row shifts (1, 2, 4,
+// 8 within each row of 16 lanes) and row broadcasts (lane 15 into the next
+// row, lane 31 into rows 2 and 3): six cross-lane adds with no LDS round
+// trip.  Every lane of the wave must be active.
+__device__ __forceinline__ int32_t wave_inclusive_sum(int32_t v) {
+    v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);  // row_shr:1
+    v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);  // row_shr:2
+    v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);  // row_shr:4
+    v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);  // row_shr:8
+    v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);  // row_bcast:15 into rows 1, 3
+    v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);  // row_bcast:31 into rows 2, 3
+    return v;
+}
+
 // Lanes of the wave holding the same key as this lane.  Every lane of the
 // wave must be active; keys are < 2^nbits.
 __device__ __forceinline__ uint64_t match_any(uint32_t key, int nbits) {

@@ -402,12 +402,7 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout_rank(LayoutArgs a) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) tsum += al[j];
     }
-    int32_t incl = tsum;
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-        const int32_t n = __shfl_up(incl, o, kWave);
-        if (lane >= o) incl += n;
-    }
+    const int32_t incl = wave_inclusive_sum(tsum);
     if (lane == kWave - 1) s_wsum[w] = incl;
     __syncthreads();
     int32_t wbase = 0, total = 0;
@@ -858,12 +853,7 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout_sp(LayoutArgs a) {
             tsum += run;
         }
         // exclusive scan of the per-thread sums: stage offsets of the groups
-        int32_t incl = tsum;
-#pragma unroll
-        for (int o = 1; o < kWave; o <<= 1) {
-            const int32_t n = __shfl_up(incl, o, kWave);
-            if (lane >= o) incl += n;
-        }
+        const int32_t incl = wave_inclusive_sum(tsum);
         if (lane == kWave - 1) s_wsum[w] = incl;
         __syncthreads();
         int32_t wb = 0, tot = 0;
@@ -960,12 +950,7 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout_sp(LayoutArgs a) {
         al[j] = g < NG ? align_up(s_cnt[g], a.A) : 0;
         asum += al[j];
     }
-    int32_t aincl = asum;
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-        const int32_t n = __shfl_up(aincl, o, kWave);
-        if (lane >= o) aincl += n;
-    }
+    const int32_t aincl = wave_inclusive_sum(asum);
     if (lane == kWave - 1) s_wsum[w] = aincl;
     __syncthreads();
     int32_t awb = 0, total = 0;
