@@ -9,9 +9,11 @@ segments, top-8, alignment 128), inputs resident in HBM:
     ep_dispatch_layout  -> ep_dispatch (bf16) -> ep_dispatch_nvfp4
     -> ep_combine -> ep_combine_bwd -> ep_dispatch_bwd
 
-The step is captured once into a HIP graph; K replays are timed between two
-device synchronizations (the same step launched op by op from Python is
-reported as eager_ms_per_step).  Each op is also captured as a graph of 8
+K steps are launched op by op through the Python binding and timed between
+two device synchronizations; the host enqueues a step in about a third of
+its GPU time, so the kernels run back to back.  The same step captured as
+one HIP graph and replayed K times is reported as graph_ms_per_step (each
+replay adds the graph launch's idle gap).  Each op is also captured as a graph of 8
 back-to-back launches and bracketed by HIP events on the stream it runs on,
 which gives each kernel's average duration.  Prints ONE JSON line on stdout:
 tokens/s of the whole step (`value`), the roofline of the dominant kernel
@@ -93,7 +95,7 @@ def traffic_for(op: str, workload: str):
 
 
 def in_step_for(workload: str):
-    """Per-op durations inside graph-replayed steps, from the rocprofv3
+    """Per-op durations inside the timed back-to-back steps, from the rocprofv3
     kernel trace of `workload` (see profiles/), or None when missing, taken
     on another workload or on different kernel sources."""
     path = os.path.join(ROOT, "profiles", f"kernel_trace_{workload}.json")
@@ -262,14 +264,9 @@ def main() -> int:
     torch.cuda.synchronize()
     eager_out = {k: v.clone() for k, v in (("recv", recv), ("codes", codes), ("y", y), ("gout", gout),
                                            ("gx", gx), ("token_row", lay.token_row))}
-    # eager step time (host launch overhead included)
-    t0 = time.perf_counter()
-    for _ in range(max(3, args.steps // 5)):
-        step()
-    torch.cuda.synchronize()
-    eager_ms = (time.perf_counter() - t0) * 1e3 / max(3, args.steps // 5)
 
-    # the whole step as one HIP graph
+    # the whole step as one HIP graph, checked against the eager result and
+    # timed beside the eager steps
     g_step = capture(torch, step)
     g_step.replay()
     torch.cuda.synchronize()
@@ -279,16 +276,24 @@ def main() -> int:
             raise RuntimeError(f"graph replay of the step changed {k}")
     log(f"[bench] warmup {args.warmup} done, graph checked; timing {args.steps} steps")
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    start.record(stream)
-    for _ in range(args.steps):
-        g_step.replay()
-    end.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_step = wall * 1e3 / args.steps
-    gpu_ms_step = start.elapsed_time(end) / args.steps
+
+    def time_steps(launch):
+        """(wall ms, event ms) per step of args.steps launches, between two syncs."""
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        start.record(stream)
+        for _ in range(args.steps):
+            launch()
+        end.record(stream)
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e3 / args.steps, start.elapsed_time(end) / args.steps
+
+    ms_step, gpu_ms_step = time_steps(step)          # the timed steps
+    graph_ms, _ = time_steps(g_step.replay)
+    for k, v in eager_out.items():
+        cur = {"recv": recv, "codes": codes, "y": y, "gout": gout, "gx": gx, "token_row": lay.token_row}[k]
+        if not torch.equal(cur.view(torch.uint8), v.view(torch.uint8)):
+            raise RuntimeError(f"the timed steps changed {k}")
 
     # per-op kernel durations: a graph of LAUNCHES back-to-back launches per op,
     # bracketed by HIP events on the stream the kernels run on
@@ -397,7 +402,7 @@ def main() -> int:
         if n in in_step_us:
             per_op[n]["in_step_eager"] = dict(rate(n, statistics.median(in_step_us[n])), reps=len(in_step_us[n]))
         if trace is not None and n in trace["in_step_us"]:
-            per_op[n]["in_step"] = dict(rate(n, trace["in_step_us"][n]), steps=trace["graph_steps"])
+            per_op[n]["in_step"] = dict(rate(n, trace["in_step_us"][n]), steps=trace.get("steps"))
         log(f"[bench] {n:18s} {med:8.2f} us  {nbytes[n] / 1e6:8.2f} MB  {gbps:7.1f} GB/s  "
             f"{100 * gbps / HBM_PEAK_GBPS:5.1f}% of 8 TB/s   cold {per_op[n]['cold']['us_median']:8.2f} us "
             f"{100 * per_op[n]['cold']['frac']:5.1f}%" +
@@ -415,7 +420,7 @@ def main() -> int:
             "in_step_eager_frac": per_op[dom]["in_step_eager"]["frac"],
             "cold_frac": per_op[dom]["cold"]["frac"], "cold_launch_us": per_op[dom]["cold"]["us_median"],
             "note": ("frac: median launch of graphs of 8 back-to-back launches (warm); in_step_frac: the kernel "
-                     "inside graph-replayed steps, from the rocprofv3 trace in profiles/kernel_trace_<workload>.json "
+                     "inside the timed back-to-back steps, from the rocprofv3 trace in profiles/kernel_trace_<workload>.json "
                      "(null when the kernel sources differ from the traced ones); in_step_eager_frac: the op inside "
                      "eager steps with an event between consecutive ops, the event packet's gap included; "
                      "cold_frac: one launch after a 1 GiB read that evicts L2 and MALL")}
@@ -429,8 +434,9 @@ def main() -> int:
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 4),
         "gpu_ms_per_step": round(gpu_ms_step, 4),
-        "eager_ms_per_step": round(eager_ms, 4),
-        "launch": "one HIP graph per step (eager_ms_per_step: the same step launched from Python)",
+        "graph_ms_per_step": round(graph_ms, 4),
+        "launch": ("each op launched from Python through the binding, host ahead of the GPU "
+                   "(graph_ms_per_step: the same step captured as one HIP graph and replayed)"),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -444,7 +450,7 @@ def main() -> int:
         "fwd_dispatch_combine_tokens_per_s": round(T / (fwd_us * 1e-6), 1),
         "ops": per_op,
         "ops_note": ("us (median), us_mean, us_p10, us_p90, GBps, frac: warm, graphs of 8 back-to-back launches, "
-                     f"{OP_WARMUP} untimed replays then {REPS} timed; in_step: the op's kernels inside graph-replayed "
+                     f"{OP_WARMUP} untimed replays then {REPS} timed; in_step: the op's kernels inside the timed "
                      "steps, from the rocprofv3 kernel trace committed under profiles/ (only while the kernel "
                      "sources match it); in_step_eager: the op inside eager steps enqueued back to back "
                      f"({IN_STEP_STEPS} steps, the first 2 dropped), an event between consecutive ops, whose packet "

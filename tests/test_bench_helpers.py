@@ -37,7 +37,7 @@ def test_digest_ignores_comments_and_whitespace(tree):
 
 def test_profile_readers_follow_the_digest(tree):
     d = bench.source_digest()
-    trace = {"workload": "dsv3", "source_digest": d, "graph_steps": 3,
+    trace = {"workload": "dsv3", "source_digest": d, "steps": 3,
              "in_step_us": {"dispatch": 90.0}, "step_span_us": 400.0}
     traffic = {"workload": "dsv3", "source_digest": d, "ops": {"dispatch": {"bytes_per_launch": 123}}}
     (tree / "profiles" / "kernel_trace_dsv3.json").write_text(json.dumps(trace))
