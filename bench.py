@@ -521,7 +521,8 @@ def capture(torch, fn):
 
 
 def latency_sweep(torch, epx, wl, dev, workload: str, token_counts) -> int:
-    """Per-op latency (µs, graphs of 8 back-to-back launches, median of 10)
+    """Per-op latency (µs, graphs of 8 back-to-back launches, 3 untimed
+    replays then the median of 10)
     of the workload's shape at each token count, plus the whole step (the
     ops of the benchmark step, FP8 dispatch excluded).  One JSON line per T."""
     for T in token_counts:
@@ -572,6 +573,8 @@ def latency_sweep(torch, epx, wl, dev, workload: str, token_counts) -> int:
                 for _ in range(8):
                     fn()
             g = capture(torch, many)
+            for _ in range(3):  # untimed: clocks up, the previous op's lines gone
+                g.replay()
             times = []
             for _ in range(10):
                 a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
