@@ -22,7 +22,7 @@ using namespace epx;
 
 struct Shape {
     int32_t T, H, E, S, K, Kp, A, C, shared, src, E_loc, G, NG;
-    int64_t R, min_rows, ws_bytes, tiles, sp_tiles;
+    int64_t R, min_rows, ws_bytes, tiles, chunks, sp_tiles;
     uint32_t flags;
 };
 
@@ -75,12 +75,14 @@ int derive(const ep_cfg_t* c, Shape* d) {
     if (packed >= (int64_t(1) << 31)) return EP_EINVAL;
     d->min_rows = d->C > 0 ? (int64_t)d->S * d->C : packed;
     if (d->min_rows >= (int64_t(1) << 31)) return EP_EINVAL;  // rows are int32
-    // Workspace: a header, then either path's per-tile tables (32-bit tile
-    // counts of the direct path; two arrays of 64-bit descriptors of the
-    // single pass).
+    // Workspace: a header, then either path's tables (the direct path's
+    // 32-bit tile counts and chunk sums; the single pass's two arrays of
+    // 64-bit descriptors).
     d->tiles = layout_tiles((int64_t)d->T * d->K, d->NG);
+    d->chunks = direct_chunks(d->tiles);
     d->sp_tiles = sp_tiles((int64_t)d->T * d->K);
-    d->ws_bytes = kWorkspaceHeader + std::max(d->tiles * (int64_t)d->NG * 4, d->sp_tiles * (int64_t)d->NG * 16);
+    d->ws_bytes = kWorkspaceHeader + std::max((d->tiles + d->chunks) * (int64_t)d->NG * 4,
+                                              d->sp_tiles * (int64_t)d->NG * 16);
     d->R = c->recv_rows;
     d->flags = c->flags;
     return EP_OK;
@@ -153,6 +155,7 @@ int zero_pad(const Shape& d, const ep_layout_t* L, void* base, int64_t row_bytes
 int layout_check(const Shape& d, const int32_t* topk_ids, const ep_layout_t* L) {
     int rc;
     if ((rc = check_rows(d)) != EP_OK) return rc;
+    if ((int64_t)d.T * d.K > kLayoutMaxSlots) return EP_EINVAL;
     if (L == nullptr) return EP_EINVAL;
     if (bad_buffer(topk_ids, (int64_t)d.T * d.K * 4, 4)) return EP_EINVAL;
     if (bad_buffer(L->counts, (int64_t)d.NG * 4, 4) || bad_buffer(L->seg_base, (int64_t)(d.S + 1) * 4, 4) ||
@@ -201,11 +204,11 @@ int layout_launch(const Shape& d, const int32_t* topk_ids, void* ws, const ep_la
         a.mode = kLayoutSmall;
     } else if (routed <= kCountMaxSlots) {
         a.mode = kLayoutCount;
-    } else if (layout_direct(d.tiles) || d.sp_tiles > kSpMaxTiles) {
-        a.mode = kLayoutDirect;  // measured fastest wherever its column sums fit one launch
     } else {
-        a.mode = kLayoutSinglePass;  // past 256 direct-path tiles the column sums grow with the tile count
+        a.mode = kLayoutDirect;  // measured faster than the single pass at every size
     }
+    a.chunks = 0;
+    a.chunk_sums = nullptr;
     if (a.mode == kLayoutSinglePass) {
         a.tiles = (int32_t)d.sp_tiles;
         a.rank_blocks = (int32_t)sp_blocks(d.sp_tiles, d.NG);
@@ -216,6 +219,8 @@ int layout_launch(const Shape& d, const int32_t* topk_ids, void* ws, const ep_la
         a.rank_blocks = (int32_t)std::max<int64_t>(a.tiles, std::min<int32_t>(d.NG, 256));
     } else if (a.mode == kLayoutDirect) {
         a.tiles = (int32_t)d.tiles;
+        a.chunks = (int32_t)d.chunks;
+        if (d.chunks > 0) a.chunk_sums = a.desc + d.tiles * (int64_t)d.NG;
         a.rank_blocks = (int32_t)std::max<int64_t>(d.tiles, std::min<int32_t>(d.NG, 256));
         a.slots_per_thread = layout_slots_per_thread(routed, d.NG);
     } else {  // one tile holds every slot

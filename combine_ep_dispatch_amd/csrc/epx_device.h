@@ -18,14 +18,19 @@ constexpr int kMaxSlots = EP_MAX_SLOTS;  // K + shared_expert: one slot per lane
 constexpr int kLayoutThreads = 256;                      // 4 waves
 constexpr int kLayoutWaves = kLayoutThreads / kWave;
 constexpr int kWorkspaceHeader = 256;                    // reserved header before the descriptors
-// Up to this many tiles the layout takes the direct path by default: the
-// histogram launch stores each tile's per-group counts as a row of a
-// [tile][group] table, and every rank workgroup sums each group's whole
-// column (its prefix over earlier tiles and the group total).  Above it the
-// single pass (one kernel) is the default, whose reads grow more slowly with
-// the tile count.
+// Direct path: the histogram launch stores each tile's per-group counts as a
+// row of a [tile][group] table.  Up to this many tiles every rank workgroup
+// sums each group's whole column (its prefix over earlier tiles and the
+// group total).  Past it the table is cut into chunks of this many rows, a
+// launch between the two sums each chunk's column into a [chunk][group]
+// table, and every rank workgroup sums that table's column and the rows of
+// its own chunk before its tile: a fixed number of loads per workgroup, so
+// the layout's cost stays linear in the slots (a whole column per workgroup
+// would grow with the square of the tile count).
 constexpr int kDirectMaxTiles = 256;
-inline bool layout_direct(int64_t tiles) { return tiles <= kDirectMaxTiles; }
+inline int64_t direct_chunks(int64_t tiles) {
+    return tiles <= kDirectMaxTiles ? 0 : (tiles + kDirectMaxTiles - 1) / kDirectMaxTiles;
+}
 
 // Direct-path column sums: lanes that share one group's column (a power of
 // two, lanes * NG <= 256 where NG allows), each summing every lanes-th tile
@@ -42,7 +47,7 @@ __host__ __device__ inline int direct_lanes_per_group(int NG) {
 // from 4 or 8 slots per thread down to 2 pays for that extra round trip
 // (fewer serial match-any rounds per wave), going from 2 to 1 does not.  So:
 // 1 when that fits one batch of loads, else the smallest of 2, 4, 8 that
-// keeps the direct path (at most kDirectMaxTiles tiles), else 8 (look-back).
+// keeps one chunk (at most kDirectMaxTiles tiles), else 8.
 inline int layout_slots_per_thread(int64_t routed_slots, int NG) {
     auto tiles_at = [&](int spt) {
         return (routed_slots + (int64_t)kLayoutThreads * spt - 1) / ((int64_t)kLayoutThreads * spt);
@@ -95,14 +100,22 @@ constexpr int kLayoutCount = 3;       // k_layout_rank alone: every workgroup co
 // that gives at most kSpTargetTiles tiles (16, 32 and 64 measured within 1
 // us of each other at 8k-32k routed slots).  A workgroup remembers at most
 // kSpMaxTilesPerBlock tiles it took, so the single pass needs
-// tiles <= 32 x the workgroups that can run at once; it is the default only
-// up to kSpMaxTiles tiles (8192 = 32 x one workgroup per CU).
+// tiles <= 32 x the workgroups that can run at once; a layout call never
+// gives it more than kSpMaxTiles tiles (8192 = 32 x one workgroup per CU).
 #ifndef EPX_SP_TILES
 #define EPX_SP_TILES 32
 #endif
 constexpr int kSpTargetTiles = EPX_SP_TILES;
 constexpr int kSpMaxTilesPerBlock = 32;
 constexpr int64_t kSpMaxTiles = 8192;
+
+// Routed slots (T*K) a layout call takes.  Up to here the chunk-sum column
+// a direct-path rank workgroup reads stays short (at most 32 chunks), and
+// the single pass, when a caller forces it, runs at most kSpMaxTiles tiles
+// of 256 x 8 slots, which the workgroups that are sure to be resident (one
+// per CU) can hold.
+constexpr int64_t kLayoutMaxSlots = int64_t(1) << 24;
+static_assert(kLayoutMaxSlots <= kSpMaxTiles * 256 * 8, "the single pass must take every layout");
 inline int sp_slots_per_thread(int64_t routed_slots) {
     for (int spt = 1; spt < 8; spt *= 2)
         if (routed_slots <= (int64_t)kLayoutThreads * spt * kSpTargetTiles) return spt;
@@ -250,12 +263,14 @@ __device__ __forceinline__ T uniform(T v) {
 struct LayoutArgs {
     const int32_t* topk_ids;
     uint32_t* desc;      // direct path: [tiles][NG] tile counts
+    uint32_t* chunk_sums;  // direct path past kDirectMaxTiles tiles: [chunks][NG] column sums of the chunks
     void* sp_header;     // single pass: workspace header (generation, ticket, ...)
     uint64_t* sp_desc;   // single pass: [tiles][NG] look-back descriptors
     ep_layout_t out;
     int32_t T, K, Kp, E, S, G, NG, E_loc, A, C, shared, src_seg;
     int64_t recv_rows;
     int32_t tiles;             // tiles of the path that runs
+    int32_t chunks;            // direct path: direct_chunks(tiles) (0: no chunk sums)
     int32_t mode;              // kLayoutSinglePass, kLayoutDirect, kLayoutSmall or kLayoutCount
     int32_t lookback;          // single pass: tile prefixes by decoupled look-back (else from all aggregates)
     int32_t rank_blocks;       // workgroups of the rank pass / single pass: max(tiles, min(NG, 256))

@@ -26,7 +26,8 @@
 // counters per group (those before its tile apart: its in-group prefix),
 // then ranks its own tile of 256 slots as the two-kernel path does.
 //
-// Two kernels (default up to 256 tiles, any size with EP_LAYOUT_DIRECT):
+// Two kernels (default past 8192 routed slots, any size with
+// EP_LAYOUT_DIRECT; a third launch between them past 256 tiles):
 //  1. k_layout_hist   per tile of 256 x {1,2,4,8} routed slots, a wave64
 //                     match-any over the group key (one ballot per key bit);
 //                     the lowest lane of each match set adds the set's
@@ -52,14 +53,23 @@
 //                     and expert_ids of whole groups (pad rows included) as
 //                     coalesced runs, are spread over at least
 //                     min(groups, 256) workgroups.
+//     Past 256 tiles, k_layout_chunks sums each chunk of 256 table rows per
+//     group between the two, and each rank workgroup sums those chunk sums
+//     and its own chunk's rows before its tile instead of a whole column:
+//     fixed work per workgroup, so the cost stays linear in the slots
+//     (MI355X, 256 groups: 50 us at 2^20 routed slots, 383 us at 2^24; with
+//     whole columns 4.8 ms there).
 //
-// Single pass (default past 256 tiles; any size with EP_LAYOUT_LOOKBACK or
-// EP_LAYOUT_BARRIER): k_layout_sp, one kernel with ticketed tiles, described
-// above it.  Measured on MI355X it is slower than the two kernels wherever
-// those apply (DeepSeek-V3 share: 14.8 against 12.0 us per launch; the
-// look-back flavour 19.9): a position needs the totals of all groups, so the
-// single pass waits for the slowest tile's counts through memory-side loads
-// across the XCDs, which costs more than the second launch.
+// Single pass (EP_LAYOUT_LOOKBACK or EP_LAYOUT_BARRIER): k_layout_sp, one
+// kernel with ticketed tiles, described above it.  Measured on MI355X it is
+// slower than the two kernels at every size (DeepSeek-V3 share: 14.8
+// against 12.0 us per launch; the look-back flavour 19.9; at 2^24 routed
+// slots the look-back takes 0.83 ms): a position needs the totals of all
+// groups, so the single pass waits for the slowest tile's counts through
+// memory-side loads across the XCDs, which costs more than the second
+// launch.  The barrier flavour reads every tile's counts in every
+// workgroup, so its cost grows with the square of the tile count (29 ms at
+// 2^24 slots).
 #include "epx_device.h"
 
 namespace epx {
@@ -116,6 +126,85 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout_hist(LayoutArgs a) {
     uint32_t* row = a.desc + (int64_t)blockIdx.x * a.NG;
     for (int g = tid; g < a.NG; g += kLayoutThreads) row[g] = (uint32_t)s_hist[g];
     if (blockIdx.x == 0 && tid == 0) a.out.flags[0] = 0;
+}
+
+// Direct-path column sums.  Lane r of the tpg lanes that share a column
+// sums its entries j = r, r + tpg, ... below n (col[j * stride]): all of
+// them into tot, those below `split` into pre.  Loads are unconditional, at
+// clamped 32-bit offsets (n * stride < 2^25), and masked afterwards: no
+// branch around a load and no 64-bit address temporaries, which let the
+// compiler reuse pending loads' registers and wait on each load in turn.
+// kDirectBatch loads per lane are in flight together: one round trip to
+// memory for up to kDirectBatch * tpg entries.
+__device__ __forceinline__ void column_sums(const uint32_t* col, uint32_t stride, int n, int split, int r, int tpg,
+                                            int32_t& tot, int32_t& pre) {
+    constexpr int kBatch = kDirectBatch;
+    for (int j0 = r; j0 < n; j0 += kBatch * tpg) {
+        uint32_t v[kBatch];
+#pragma unroll
+        for (int i = 0; i < kBatch; ++i) {
+            const int j = j0 + i * tpg;
+            v[i] = col[(uint32_t)min(j, n - 1) * stride];
+        }
+        // Every load of the batch is issued before the first is consumed:
+        // left to itself the scheduler may interleave the sums with the
+        // issue to save registers, which waits on the first loads with half
+        // the batch not yet sent (a second round trip to memory).
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < kBatch; ++i) {
+            const int j = j0 + i * tpg;
+            const int32_t c = j < n ? (int32_t)v[i] : 0;
+            tot += c;
+            pre += j < split ? c : 0;
+        }
+    }
+}
+
+// The same over four adjacent columns at once, one 16-byte load per entry
+// (col[j * stride] holds the four columns' entries j).
+__device__ __forceinline__ void quad_sums(const uint4* col, uint32_t stride, int n, int split, int r, int tpq,
+                                          int32_t (&tot)[4], int32_t (&pre)[4]) {
+    constexpr int kBatch4 = kDirectBatch / 4;
+    for (int j0 = r; j0 < n; j0 += kBatch4 * tpq) {
+        uint4 v[kBatch4];
+#pragma unroll
+        for (int i = 0; i < kBatch4; ++i) {
+            const int j = j0 + i * tpq;
+            v[i] = col[(uint32_t)min(j, n - 1) * stride];
+        }
+        __builtin_amdgcn_sched_barrier(0);  // the whole batch in flight first
+#pragma unroll
+        for (int i = 0; i < kBatch4; ++i) {
+            const int j = j0 + i * tpq;
+            const bool in = j < n, before = j < split;
+            const int32_t c[4] = {(int32_t)v[i].x, (int32_t)v[i].y, (int32_t)v[i].z, (int32_t)v[i].w};
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                tot[q] += in ? c[q] : 0;
+                pre[q] += before ? c[q] : 0;
+            }
+        }
+    }
+}
+
+// Direct path past kDirectMaxTiles tiles: chunk_sums[c][g] = the sum of
+// rows [c * kDirectMaxTiles, (c + 1) * kDirectMaxTiles) of the tile-count
+// table's column g.  Grid: (chunks, group blocks of kLayoutThreads / tpg
+// groups); tpg lanes share a group as in the rank kernel's column sums.
+__global__ __launch_bounds__(kLayoutThreads) void k_layout_chunks(LayoutArgs a) {
+    const int tid = threadIdx.x, NG = a.NG;
+    const int tpg = direct_lanes_per_group(NG);
+    const int r = tid & (tpg - 1);
+    const int g = (int)blockIdx.y * (kLayoutThreads / tpg) + tid / tpg;
+    const int t0 = (int)blockIdx.x * kDirectMaxTiles;
+    const int n = min(kDirectMaxTiles, a.tiles - t0);
+    // a group's tpg lanes sit in one wave and leave together
+    if (g >= NG) return;
+    int32_t tot = 0, pre = 0;
+    column_sums(a.desc + (uint32_t)t0 * (uint32_t)NG + g, (uint32_t)NG, n, 0, r, tpg, tot, pre);
+    for (int o = 1; o < tpg; o <<= 1) tot += __shfl_xor(tot, o, kWave);
+    if (r == 0) a.chunk_sums[(int64_t)blockIdx.x * NG + g] = (uint32_t)tot;
 }
 
 template <int SPT, int MODE>
@@ -207,43 +296,40 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout_rank(LayoutArgs a) {
         for (int g = tid; g < NG; g += kLayoutThreads)
             s_cnt[g] = s_cnt[g] + s_pref[g] + (g == shared_group ? a.T : 0);
     }
+    // Direct path: the group totals and this tile's in-group prefix from the
+    // [tile][group] table; past kDirectMaxTiles tiles from the chunk sums
+    // (totals, and the prefix over earlier chunks) plus the rows of this
+    // tile's own chunk before it.  Workgroups past the last tile need only
+    // the totals.
+    const int my_chunk = DIRECT ? min((int)(tile / kDirectMaxTiles), a.chunks) : 0;
+    const int c0 = my_chunk * kDirectMaxTiles;
+    const bool in_chunk = DIRECT && a.chunks > 0 && tile < (uint32_t)a.tiles;
     if (DIRECT && EPX_DIRECT_QUADS && (NG & 3) == 0 && NG <= 128) {
-        // Group totals and this tile's in-group prefix from the [tile][group]
-        // table, four groups per 16-byte load (rows are 16-byte aligned when
+        // Four groups per 16-byte load (rows are 16-byte aligned when
         // NG % 4 == 0).  tpq (a power of two, tpq * NG / 4 <= 256, at most a
-        // wave) lanes share a quad of groups: lane r sums tiles r, r + tpq,
+        // wave) lanes share a quad of groups: lane r sums entries r, r + tpq,
         // ...; with 16 loads in flight per lane that is one round trip for
-        // up to 16 * tpq tiles (the same as the one-group-per-load form below
-        // wherever that bounds the tile size; at least 256 otherwise), with
-        // a quarter of its load instructions.  Measured on MI355X against
-        // that form: skewed (128 groups) 14.4 -> 14.0 us, capacity (64)
-        // 20.0 -> 19.4 us; with 256 groups (4 lanes per quad, so a wave
+        // up to 16 * tpq entries (the same as the one-group-per-load form
+        // below wherever that bounds the tile size; at least 256 otherwise),
+        // with a quarter of its load instructions.  Measured on MI355X
+        // against that form: skewed (128 groups) 14.4 -> 14.0 us, capacity
+        // (64) 20.0 -> 19.4 us; with 256 groups (4 lanes per quad, so a wave
         // load spans 4 table rows) 10.5 -> 11.1 us, so only up to 128.
-        constexpr int kBatch4 = kDirectBatch / 4;
         const int Q = NG / 4;
         const int tpq = min(4 * direct_lanes_per_group(NG), kWave);  // a quad's lanes stay in one wave
         const int r = tid & (tpq - 1);
         const uint4* table = reinterpret_cast<const uint4*>(a.desc);
+        const uint4* chunks = reinterpret_cast<const uint4*>(a.chunk_sums);
         for (int q = tid / tpq; q < Q; q += kLayoutThreads / tpq) {
             int32_t tot[4] = {0, 0, 0, 0}, pre[4] = {0, 0, 0, 0};
-            for (int j0 = r; j0 < a.tiles; j0 += kBatch4 * tpq) {
-                uint4 v[kBatch4];
-#pragma unroll
-                for (int i = 0; i < kBatch4; ++i) {
-                    const int j = j0 + i * tpq;
-                    v[i] = table[(uint32_t)min(j, a.tiles - 1) * (uint32_t)Q + (uint32_t)q];
-                }
-                __builtin_amdgcn_sched_barrier(0);  // the whole batch in flight first (see below)
-#pragma unroll
-                for (int i = 0; i < kBatch4; ++i) {
-                    const int j = j0 + i * tpq;
-                    const bool in = j < a.tiles, before = j < (int)tile;
-                    const int32_t n[4] = {(int32_t)v[i].x, (int32_t)v[i].y, (int32_t)v[i].z, (int32_t)v[i].w};
-#pragma unroll
-                    for (int c = 0; c < 4; ++c) {
-                        tot[c] += in ? n[c] : 0;
-                        pre[c] += before ? n[c] : 0;
-                    }
+            if (a.chunks == 0) {
+                quad_sums(table + q, (uint32_t)Q, a.tiles, (int)tile, r, tpq, tot, pre);
+            } else {
+                quad_sums(chunks + q, (uint32_t)Q, a.chunks, my_chunk, r, tpq, tot, pre);
+                if (in_chunk) {
+                    int32_t t2[4] = {0, 0, 0, 0};
+                    quad_sums(table + (uint32_t)c0 * (uint32_t)Q + q, (uint32_t)Q, min(kDirectMaxTiles, a.tiles - c0),
+                              (int)tile - c0, r, tpq, t2, pre);
                 }
             }
             for (int o = 1; o < tpq; o <<= 1) {
@@ -263,41 +349,21 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout_rank(LayoutArgs a) {
             }
         }
     } else if (DIRECT) {
-        // Group totals and this tile's in-group prefix from the [tile][group]
-        // table.  tpg (a power of two, tpg * NG <= 256) lanes share a group:
-        // lane r of the group sums tiles r, r + tpg, ...; with 64 loads in
-        // flight per lane this is one round trip for up to 64 * tpg tiles.
-        // The partial sums meet by xor-shuffles inside the lane group (all
-        // lanes of a group are active or inactive together).
-        constexpr int kBatch = kDirectBatch;
+        // tpg (a power of two, tpg * NG <= 256) lanes share a group; their
+        // partial sums meet by xor-shuffles inside the lane group (all lanes
+        // of a group are active or inactive together).
         const int tpg = direct_lanes_per_group(NG);
         const int r = tid & (tpg - 1);
         for (int g = tid / tpg; g < NG; g += kLayoutThreads / tpg) {
-            const uint32_t* col = a.desc + g;
             int32_t tot = 0, pre = 0;
-            for (int j0 = r; j0 < a.tiles; j0 += kBatch * tpg) {
-                // Unconditional loads at clamped 32-bit offsets (tiles * NG
-                // < 2^20), masked afterwards: no branch around a load and no
-                // 64-bit address temporaries, which let the compiler reuse
-                // pending loads' registers and wait on each load in turn.
-                uint32_t v[kBatch];
-#pragma unroll
-                for (int i = 0; i < kBatch; ++i) {
-                    const int j = j0 + i * tpg;
-                    v[i] = col[(uint32_t)min(j, a.tiles - 1) * (uint32_t)NG];
-                }
-                // Every load of the batch is issued before the first is
-                // consumed: left to itself the scheduler may interleave the
-                // sums with the issue to save registers, which waits on the
-                // first loads with half the batch not yet sent (a second
-                // round trip to memory).
-                __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-                for (int i = 0; i < kBatch; ++i) {
-                    const int j = j0 + i * tpg;
-                    const int32_t n = j < a.tiles ? (int32_t)v[i] : 0;
-                    tot += n;
-                    pre += j < (int)tile ? n : 0;
+            if (a.chunks == 0) {
+                column_sums(a.desc + g, (uint32_t)NG, a.tiles, (int)tile, r, tpg, tot, pre);
+            } else {
+                column_sums(a.chunk_sums + g, (uint32_t)NG, a.chunks, my_chunk, r, tpg, tot, pre);
+                if (in_chunk) {
+                    int32_t t2 = 0;
+                    column_sums(a.desc + (uint32_t)c0 * (uint32_t)NG + g, (uint32_t)NG,
+                                min(kDirectMaxTiles, a.tiles - c0), (int)tile - c0, r, tpg, t2, pre);
                 }
             }
             for (int o = 1; o < tpg; o <<= 1) {
@@ -930,8 +996,13 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout_sp(LayoutArgs a) {
         const int g = tid * J + j;
         if (g >= NG) continue;
         int32_t tot;
-        if (LOOKBACK && live) {
-            tot = pref[j] + agg[j] + sp_sum<W>(aggs, NG, g, t + 1, NT, NT, nullptr, gen, t_begin, flag);
+        if (LOOKBACK) {
+            // The totals are the exclusive prefix of a tile past the last
+            // one: the look-back from the last tile folds aggregates back to
+            // the first inclusive prefix it meets, a few round trips however
+            // many tiles there are (summing every later tile's aggregate
+            // instead makes the pass quadratic in the tile count).
+            tot = sp_lookback<W>(desc, NG, g, NT, gen, t_begin, flag);
         } else {
             int32_t from_t = 0;  // tiles >= t
             tot = sp_sum<W>(aggs, NG, g, 0, NT, live ? t : NT, &from_t, gen, t_begin, flag);
@@ -1145,6 +1216,11 @@ void launch_spt(const LayoutArgs& a, hipStream_t stream) {
         hipLaunchKernelGGL((k_layout_rank<SPT, kLayoutCount>), dim3((unsigned)a.rank_blocks), block, 0, stream, a);
     } else if (a.mode == kLayoutDirect) {
         hipLaunchKernelGGL((k_layout_hist<SPT>), dim3((unsigned)a.tiles), block, 0, stream, a);
+        if (a.chunks > 0) {
+            const int per_block = kLayoutThreads / direct_lanes_per_group(a.NG);
+            hipLaunchKernelGGL(k_layout_chunks, dim3((unsigned)a.chunks, (unsigned)((a.NG + per_block - 1) / per_block)),
+                               block, 0, stream, a);
+        }
         hipLaunchKernelGGL((k_layout_rank<SPT, kLayoutDirect>), dim3((unsigned)a.rank_blocks), block, 0, stream, a);
     } else if (a.NG <= kLayoutThreads) {
         if (a.lookback)

@@ -190,12 +190,16 @@ int ep_query(const ep_cfg_t* cfg, int64_t* min_recv_rows, int64_t* workspace_byt
  *  - up to 8192 routed slots (by default; EP_LAYOUT_COUNT at any size): one
  *    kernel in which every workgroup counts all slots per group in LDS,
  *    then ranks its own tile;
- *  - otherwise up to 256 tiles (by default; EP_LAYOUT_DIRECT at any size):
- *    two kernels, a [tile][group] count table then the ranks;
- *  - beyond that (by default; EP_LAYOUT_LOOKBACK / EP_LAYOUT_BARRIER at any
- *    size): one kernel, tiles taken from an atomic ticket, each tile's
- *    prefix by decoupled look-back (or from one read of every tile's
- *    counts), the group totals from every tile's published counts.
+ *  - otherwise (by default; EP_LAYOUT_DIRECT at any size): two kernels, a
+ *    [tile][group] count table then the ranks, with a third launch between
+ *    them past 256 tiles that sums the table in chunks of 256 tiles;
+ *  - EP_LAYOUT_LOOKBACK / EP_LAYOUT_BARRIER: one kernel, tiles taken from
+ *    an atomic ticket, each tile's prefix by decoupled look-back (or from
+ *    one read of every tile's counts, whose cost grows with the square of
+ *    the tile count); slower than the two kernels at every size measured.
+ * At most 2^24 routed slots (T*K), else EP_EINVAL: up to there every path
+ * costs about linearly in the slots (the single pass runs at most 8192
+ * tiles).  The other calls take any T*K' < 2^30 with a valid token_row.
  * Data errors go to layout->flags; a single-pass wait that cannot end gives
  * up after about 0.3 s and sets EP_FLAG_INTERNAL.
  */

@@ -44,10 +44,12 @@ def sp_tiles(routed):
 
 
 def workspace_bytes(routed, ng):
-    """A 256-byte header, then the larger of the two paths' per-tile tables:
-    32-bit tile counts (two-kernel path) or two arrays of 64-bit descriptors
-    (single pass)."""
-    return 256 + max(layout_tiles(routed, ng) * ng * 4, sp_tiles(routed) * ng * 16)
+    """A 256-byte header, then the larger of the two paths' tables: 32-bit
+    tile counts plus, past 256 tiles, 32-bit sums of each chunk of 256 tiles
+    (two-kernel path), or two arrays of 64-bit descriptors (single pass)."""
+    tiles = layout_tiles(routed, ng)
+    chunks = 0 if tiles <= 256 else -(-tiles // 256)
+    return 256 + max((tiles + chunks) * ng * 4, sp_tiles(routed) * ng * 16)
 
 
 def test_layout_tiles_rule():
@@ -149,7 +151,10 @@ def test_query_sizes(L, orc):
 
     for kw in [dict(), dict(align=1), dict(shared_expert=1, src_segment=1),
                dict(seg_capacity=100), dict(num_tokens=0), dict(num_tokens=4096, hidden=7168,
-               num_experts=256, num_segments=8, top_k=8, align=128)]:
+               num_experts=256, num_segments=8, top_k=8, align=128),
+               # past 256 two-kernel tiles (chunk sums) and at the 2^24-slot layout limit
+               dict(num_tokens=70_000, num_experts=64, num_segments=4, top_k=8, align=16),
+               dict(num_tokens=1 << 21, num_experts=256, num_segments=8, top_k=8, align=128, shared_expert=1)]:
         c = cfg(**kw)
         st, rows, ws, g = query(L, c)
         assert st == 0
@@ -209,6 +214,24 @@ def test_forced_count_path_bound(L):
     assert query(L, cfg(flags=16, num_tokens=1 << 15, top_k=8))[0] == 0
     assert query(L, cfg(flags=16, num_tokens=(1 << 15) + 1, top_k=8))[0] == -1
     assert query(L, cfg(flags=0, num_tokens=(1 << 15) + 1, top_k=8))[0] == 0
+
+
+def test_layout_rejects_more_than_2_24_routed_slots(L):
+    """A layout call takes at most 2^24 routed slots (T*K); ep_query and the
+    movers take larger batches.  Only batches past the limit are passed: at
+    or below it these fake pointers would reach a launch."""
+    from combine_ep_dispatch_amd._lib import EpLayout
+
+    fake = 0x10000
+    lay = EpLayout(*([fake] * 8))
+    for T, K in (((1 << 21) + 1, 8), ((1 << 24) + 1, 1), (1 << 20, 17)):
+        c = cfg(num_tokens=T, top_k=K, num_experts=64, num_segments=8, hidden=256)
+        st, rows, ws, _ = query(L, c)
+        assert st == 0 and T * K > 1 << 24
+        c.recv_rows = rows
+        cc = c.to_c()
+        assert L.ep_dispatch_layout(ctypes.byref(cc), fake, fake, ws, ctypes.byref(lay), None) == -1
+        assert L.ep_dispatch_layout_noalloc(ctypes.byref(cc), fake, ctypes.byref(lay), None) == -1
 
 
 def test_null_config_and_reserved_fields(L):

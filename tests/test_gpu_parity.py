@@ -152,7 +152,12 @@ EDGE = {
     "spt4_157_tiles": dict(T=20011, S=4, E_loc=16, K=8, H=16, A=2),       # 4 slots/thread
     "direct_four_batches": dict(T=25000, S=8, E_loc=32, K=8, H=16, A=2),  # 256 groups, 196 tiles: 4 load batches
     "direct_254_tiles": dict(T=65000, S=4, E_loc=16, K=8, H=16, A=2, bad_p=0.01),  # direct path, near its tile limit
-    "lookback_274_tiles": dict(T=70001, S=4, E_loc=16, K=8, H=16, A=2, shared=1, src=3, bad_p=0.01),  # look-back path
+    # past 256 two-kernel tiles: 274 tiles, two chunks of tile-count sums (68 groups: 16-byte column loads)
+    "direct_274_tiles_chunked": dict(T=70001, S=4, E_loc=16, K=8, H=16, A=2, shared=1, src=3, bad_p=0.01),
+    # 293 tiles, a ragged second chunk, 21 groups (one group per load, 8 lanes per group)
+    "direct_293_tiles_ragged_chunk": dict(T=100001, S=3, E_loc=7, K=6, H=16, A=4, mask_p=0.05),
+    # 4096 tiles in 16 chunks, 16 groups (16-byte loads)
+    "direct_16_chunks": dict(T=1 << 20, S=2, E_loc=8, K=8, H=16, A=8, distinct=False),
     "single_pass_max_groups": dict(T=128, S=8, E_loc=255, K=8, shared=1, A=4, H=32),  # 2048 groups, one launch
     "single_pass_1024": dict(T=128, S=8, E_loc=32, K=8, H=64, A=128, shared=1, src=5),  # 1024 slots: count path
     "single_pass_1023": dict(T=1023, S=4, E_loc=8, K=1, H=16, A=4),                   # count path, ragged tile
@@ -164,6 +169,10 @@ EDGE = {
     "single_pass_513": dict(T=171, S=3, E_loc=5, K=3, H=32, A=2, mask_p=0.2),         # one past it: count path
     "count_8192": dict(T=1024, S=8, E_loc=32, K=8, H=64, A=128, mask_p=0.05),        # count path bound
     "direct_8193": dict(T=8193, S=4, E_loc=8, K=1, H=16, A=4, bad_p=0.01),            # one past it: two kernels
+    # the largest layout call: 2^24 routed slots, 264 groups; by default two
+    # kernels over 8192 tiles in 32 chunks, forced: 8192 single-pass tiles
+    "max_routed_slots": dict(T=1 << 21, S=8, E_loc=32, K=8, H=16, A=128, shared=1, src=3, mask_p=0.01,
+                             distinct=False),
     "slots_64": dict(T=300, S=1, E_loc=64, K=63, shared=1, src=0, H=64, A=4),  # K' = 64: 16 scatter slot blocks
     "hidden_8": dict(T=500, S=2, E_loc=4, K=3, H=8),                          # one ragged piece per row
     "hidden_16k": dict(T=300, S=2, E_loc=4, K=4, H=16384, A=8),               # 8 full pieces, 16 NVFP4 blocks per lane
