@@ -48,6 +48,7 @@ int derive(const ep_cfg_t* c, Shape* d) {
     if (c->flags & ~(EP_ZERO_PAD_ROWS | kPaths)) return EP_EINVAL;
     if (__builtin_popcount(c->flags & kPaths) > 1) return EP_EINVAL;  // at most one path
     if ((c->flags & EP_LAYOUT_COUNT) && (int64_t)c->num_tokens * c->top_k > kCountForcedMaxSlots) return EP_EINVAL;
+    if ((c->flags & EP_LAYOUT_BARRIER) && (int64_t)c->num_tokens * c->top_k > kBarrierForcedMaxSlots) return EP_EINVAL;
     d->T = c->num_tokens;
     d->H = c->hidden;
     d->E = c->num_experts;

@@ -89,6 +89,11 @@ constexpr int64_t kCountMaxSlots = 8192;
 // grows with the square of the batch (262 144 slots: 1024 workgroups of
 // 262 144 LDS additions each).
 constexpr int64_t kCountForcedMaxSlots = int64_t(1) << 18;
+// Forced with EP_LAYOUT_BARRIER the single pass takes at most this many
+// routed slots: every workgroup reads every tile's counts, so its cost grows
+// with the square of the tile count (MI355X, 256 groups: 147 us at 2^20
+// routed slots, 29 ms at 2^24, against 50 us and 0.38 ms for the default).
+constexpr int64_t kBarrierForcedMaxSlots = int64_t(1) << 20;
 
 // Layout kernel paths.
 constexpr int kLayoutSinglePass = 0;  // k_layout_sp: ticketed tiles, decoupled look-back

@@ -74,7 +74,10 @@ extern "C" {
                                   by decoupled look-back */
 #define EP_LAYOUT_DIRECT 4u    /* two kernels: tile-count table, then ranks */
 #define EP_LAYOUT_BARRIER 8u   /* one kernel: ticketed tiles, each tile's prefix
-                                  from one read of every tile's counts */
+                                  from one read of every tile's counts; at
+                                  most 2^20 routed slots (T*K), else
+                                  EP_EINVAL: its cost grows with the square
+                                  of the tile count */
 #define EP_LAYOUT_COUNT 16u    /* one kernel: every workgroup counts every
                                   routed slot (no workspace traffic); at
                                   most 2^18 routed slots (T*K), else

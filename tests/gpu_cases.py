@@ -55,6 +55,7 @@ LAYOUT_PATHS = {"single-pass": epx.EP_LAYOUT_LOOKBACK, "single-pass-barrier": ep
                 "two-kernel": epx.EP_LAYOUT_DIRECT, "count": epx.EP_LAYOUT_COUNT, "default": 0}
 PATH_FLAGS = epx.EP_LAYOUT_LOOKBACK | epx.EP_LAYOUT_DIRECT | epx.EP_LAYOUT_BARRIER | epx.EP_LAYOUT_COUNT
 COUNT_FORCED_MAX_SLOTS = 1 << 18  # routed slots EP_LAYOUT_COUNT accepts
+BARRIER_FORCED_MAX_SLOTS = 1 << 20  # routed slots EP_LAYOUT_BARRIER accepts
 
 
 def gpu_layout(cfg: epx.EpConfig, ids: np.ndarray, ws=None, path=None) -> epx.Layout:
@@ -205,9 +206,13 @@ def check_layout(c: Case, name: str) -> epx.Layout:
         f"R={c.cfg.recv_rows}")
     # Every layout path (single pass, two kernels, count, and whichever the
     # size selects by default) must give the oracle's layout; the default
-    # one is returned.  The count path takes at most 2^18 routed slots.
-    paths = ["single-pass", "single-pass-barrier", "two-kernel"]
-    if c.cfg.num_tokens * c.cfg.top_k <= COUNT_FORCED_MAX_SLOTS:
+    # one is returned.  The count path takes at most 2^18 routed slots, the
+    # single pass's barrier flavour 2^20.
+    routed = c.cfg.num_tokens * c.cfg.top_k
+    paths = ["single-pass", "two-kernel"]
+    if routed <= BARRIER_FORCED_MAX_SLOTS:
+        paths.append("single-pass-barrier")
+    if routed <= COUNT_FORCED_MAX_SLOTS:
         paths.append("count")
     for path in paths:
         assert_layout_equal(layout_np(gpu_layout(c.cfg, c.ids, path=path)), c.L, f"{name} ({path})")

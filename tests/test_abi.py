@@ -234,6 +234,17 @@ def test_layout_rejects_more_than_2_24_routed_slots(L):
         assert L.ep_dispatch_layout_noalloc(ctypes.byref(cc), fake, ctypes.byref(lay), None) == -1
 
 
+def test_forced_barrier_path_bound(L):
+    """EP_LAYOUT_BARRIER takes at most 2^20 routed slots (every workgroup
+    reads every tile's counts); the look-back and the default have no such
+    bound below the 2^24-slot layout limit."""
+    big = dict(num_tokens=(1 << 17) + 1, top_k=8, num_experts=64, num_segments=8)
+    assert query(L, cfg(flags=8, num_tokens=1 << 17, top_k=8, num_experts=64, num_segments=8))[0] == 0
+    assert query(L, cfg(flags=8, **big))[0] == -1
+    assert query(L, cfg(flags=2, **big))[0] == 0
+    assert query(L, cfg(flags=0, **big))[0] == 0
+
+
 def test_null_config_and_reserved_fields(L):
     assert L.ep_query(None, None, None, None) == -1
     c = cfg().to_c()
