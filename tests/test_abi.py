@@ -58,7 +58,7 @@ def test_layout_tiles_rule():
     assert layout_tiles(1024 * 8, 256) == 32          # 1 slot per thread
     assert layout_tiles(16384 * 6, 68) == 192         # 2 slots per thread, 2 batches of 2 lanes
     assert layout_tiles(4096 * 6, 68) == 96           # 1 slot per thread, 2 lanes per group
-    assert layout_tiles(70001 * 8, 64) == 274         # past the direct path
+    assert layout_tiles(70001 * 8, 64) == 274         # past one chunk of 256 tiles: two chunks
     assert layout_tiles(0, 8) == 1
 
 
