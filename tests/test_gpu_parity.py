@@ -67,6 +67,7 @@ def test_named_workload_full_size(G, name):
 SEED_BASE = int(os.environ.get("EPX_GPU_SEED_BASE", "0"))
 SEEDS = int(os.environ.get("EPX_GPU_SEEDS", "128"))
 LARGE_SEEDS = int(os.environ.get("EPX_GPU_LARGE_SEEDS", "4"))
+HUGE_SEEDS = int(os.environ.get("EPX_GPU_HUGE_SEEDS", "2"))
 
 
 @pytest.mark.parametrize("seed", range(SEED_BASE, SEED_BASE + SEEDS))
@@ -129,6 +130,33 @@ def test_large_random_shapes(G, seed):
     G.check_combine_bwd(c, lay, name, weighted=seed % 3 != 0)
     G.check_probs_grad(c, lay, name)
     G.check_combine_nvfp4(c, lay, name, weighted=seed % 2 == 0)
+
+
+@pytest.mark.parametrize("seed", range(SEED_BASE, SEED_BASE + HUGE_SEEDS))
+def test_huge_random_layouts(G, seed):
+    """Layouts past one chunk of 256 two-kernel tiles: T = 70 000..400 000
+    (up to 3.2 M routed slots, up to 7 chunks), random group counts up to
+    2048, repeated ids, masks, bad ids, capacity drops and the shared expert;
+    the bf16 movers at narrow rows."""
+    rng = np.random.default_rng(30_000 + seed)
+    S = int(rng.choice([1, 2, 4, 8]))
+    E_loc = int(rng.choice([3, 16, 21, 64, 255]))
+    K = int(rng.integers(1, min(S * E_loc, 8) + 1))
+    kw = dict(T=int(rng.integers(70_000, 400_001)), H=int(rng.choice([16, 48, 128])), S=S, E_loc=E_loc, K=K,
+              A=int(rng.choice([1, 4, 128])), shared=int(rng.integers(0, 2)), src=int(rng.integers(0, S)),
+              mask_p=float(rng.choice([0.0, 0.02])), bad_p=float(rng.choice([0.0, 0.001])), distinct=False)
+    c = G.random_case(40_000 + seed, **kw)
+    if seed % 3 == 1:
+        load = max(1, c.cfg.num_tokens * c.cfg.kp // c.cfg.num_segments)
+        c.cfg.seg_capacity = int(rng.integers(load // 2, load + 2))
+        c.cfg.recv_rows = G.epx.ep_query(c.cfg).min_recv_rows
+        c = G.Case(c.cfg, c.ids, c.probs, c.x, c.seed)
+    name = f"huge{seed}"
+    lay = G.check_layout(c, name)
+    G.check_dispatch(c, lay, name)
+    G.check_combine(c, lay, name, weighted=seed % 2 == 0)
+    G.check_dispatch_bwd(c, lay, name)
+    G.check_combine_bwd(c, lay, name, weighted=seed % 2 == 1)
 
 
 EDGE = {
