@@ -14,6 +14,7 @@ cases (no tokens, everything masked, the largest group count, tile
 boundaries, K = 1, one expert per segment, tiny capacities).
 """
 
+import dataclasses
 import os
 
 import numpy as np
@@ -354,6 +355,36 @@ def test_single_pass_workspace_reuse(G):
     c = G.workload_case("skewed", T=3000)
     G.gpu_layout(c.cfg, c.ids, ws=ws, path="two-kernel")
     G.assert_layout_equal(G.layout_np(G.gpu_layout(c.cfg, c.ids, ws=ws, path="single-pass")), c.L, "after 2k")
+
+
+def test_concurrent_streams(G):
+    """Calls on two streams at once, each with its own workspace and output
+    buffers, do not interfere: layouts (the single pass keeps a ticket and a
+    generation in its workspace) and bf16 dispatches of two different
+    shapes, enqueued alternately on two default-priority streams, match the
+    oracle on every round."""
+    cases = [G.workload_case("skewed", T=3000), G.random_case(11, T=2500, S=4, E_loc=16, K=6, A=16, H=256)]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    paths = [G.epx.EP_LAYOUT_LOOKBACK, 0, G.epx.EP_LAYOUT_BARRIER]
+    for rnd in range(3):
+        cfgs = [dataclasses.replace(c.cfg, flags=paths[(rnd + i) % 3]) for i, c in enumerate(cases)]
+        ids = [torch.from_numpy(np.ascontiguousarray(c.ids, np.int32).reshape(-1)).to(G.DEV) for c in cases]
+        xs = [G.u16_tensor(c.x) for c in cases]
+        lays = [G.sentinel_layout(cfg) for cfg in cfgs]
+        wss = [G.epx.workspace_for(cfg, G.DEV) for cfg in cfgs]
+        recvs = [G.bf16_filled(cfg.recv_rows, cfg.hidden, G.orc.SENTINEL_U16) for cfg in cfgs]
+        torch.cuda.synchronize()
+        for i in range(2):
+            with torch.cuda.stream(streams[i]):
+                G.epx.ep_dispatch_layout(cfgs[i], ids[i], wss[i], lays[i])
+        for i in range(2):
+            with torch.cuda.stream(streams[i]):
+                G.epx.ep_dispatch(cfgs[i], lays[i], xs[i], recvs[i])
+        torch.cuda.synchronize()
+        for i, c in enumerate(cases):
+            G.assert_layout_equal(G.layout_np(lays[i]), c.L, f"stream {i} round {rnd}")
+            G.assert_bits_equal(G.bits_of(recvs[i]), G.orc.dispatch(c.oc, c.L["token_row"], c.x),
+                                f"stream {i} round {rnd}: recv")
 
 
 def test_determinism(G):
