@@ -21,12 +21,13 @@ constexpr int kWorkspaceHeader = 256;                    // reserved header befo
 // Direct path: the histogram launch stores each tile's per-group counts as a
 // row of a [tile][group] table.  Up to this many tiles every rank workgroup
 // sums each group's whole column (its prefix over earlier tiles and the
-// group total).  Past it the table is cut into chunks of this many rows, a
-// launch between the two sums each chunk's column into a [chunk][group]
-// table, and every rank workgroup sums that table's column and the rows of
-// its own chunk before its tile: a fixed number of loads per workgroup, so
-// the layout's cost stays linear in the slots (a whole column per workgroup
-// would grow with the square of the tile count).
+// group total).  Past it the table is cut into chunks of this many rows: a
+// launch between the two turns each chunk's counts into prefixes within the
+// chunk and writes the chunk's sums to a [chunk][group] table, and every
+// rank workgroup sums that table's column and adds its own row: a fixed
+// number of loads per workgroup, so the layout's cost stays linear in the
+// slots (a whole column per workgroup would grow with the square of the
+// tile count).
 constexpr int kDirectMaxTiles = 256;
 inline int64_t direct_chunks(int64_t tiles) {
     return tiles <= kDirectMaxTiles ? 0 : (tiles + kDirectMaxTiles - 1) / kDirectMaxTiles;
@@ -92,7 +93,7 @@ constexpr int64_t kCountForcedMaxSlots = int64_t(1) << 18;
 // Forced with EP_LAYOUT_BARRIER the single pass takes at most this many
 // routed slots: every workgroup reads every tile's counts, so its cost grows
 // with the square of the tile count (MI355X, 256 groups: 147 us at 2^20
-// routed slots, 29 ms at 2^24, against 50 us and 0.38 ms for the default).
+// routed slots, 29 ms at 2^24, against 46 us and 0.22 ms for the default).
 constexpr int64_t kBarrierForcedMaxSlots = int64_t(1) << 20;
 
 // Layout kernel paths.

@@ -53,12 +53,12 @@
 //                     and expert_ids of whole groups (pad rows included) as
 //                     coalesced runs, are spread over at least
 //                     min(groups, 256) workgroups.
-//     Past 256 tiles, k_layout_chunks sums each chunk of 256 table rows per
-//     group between the two, and each rank workgroup sums those chunk sums
-//     and its own chunk's rows before its tile instead of a whole column:
-//     fixed work per workgroup, so the cost stays linear in the slots
-//     (MI355X, 256 groups: 50 us at 2^20 routed slots, 383 us at 2^24; with
-//     whole columns 4.8 ms there).
+//     Past 256 tiles, k_layout_chunks runs between the two: per chunk of 256
+//     table rows and group it turns the counts into prefixes within the
+//     chunk and sums them, and each rank workgroup reads the chunk sums and
+//     its own row instead of a whole column: fixed work per workgroup, so
+//     the cost stays linear in the slots (MI355X, 256 groups: 46 us at 2^20
+//     routed slots, 222 us at 2^24; with whole columns 4.8 ms there).
 //
 // Single pass (EP_LAYOUT_LOOKBACK or EP_LAYOUT_BARRIER): k_layout_sp, one
 // kernel with ticketed tiles, described above it.  Measured on MI355X it is
@@ -188,40 +188,56 @@ __device__ __forceinline__ void quad_sums(const uint4* col, uint32_t stride, int
     }
 }
 
-// Direct path past kDirectMaxTiles tiles: chunk_sums[c][g] = the sum of
-// rows [c * kDirectMaxTiles, (c + 1) * kDirectMaxTiles) of the tile-count
-// table's column g.  Grid: (chunks, group blocks of kLayoutThreads / tpg
-// groups); tpg lanes share a group as in the rank kernel's column sums.
+// Direct path past kDirectMaxTiles tiles: for chunk c of kDirectMaxTiles
+// rows of the tile-count table and group g, turns the chunk's counts into
+// exclusive prefixes within the chunk (in place) and writes their total to
+// chunk_sums[c][g].  One lane per group, kDirectBatch rows in flight; a
+// wave's loads and stores cover 64 adjacent groups of one row.  Grid:
+// (chunks, groups / kLayoutThreads).
 __global__ __launch_bounds__(kLayoutThreads) void k_layout_chunks(LayoutArgs a) {
-    const int tid = threadIdx.x, NG = a.NG;
-    const int tpg = direct_lanes_per_group(NG);
-    const int r = tid & (tpg - 1);
-    const int g = (int)blockIdx.y * (kLayoutThreads / tpg) + tid / tpg;
+    const int NG = a.NG;
+    const int g = (int)blockIdx.y * kLayoutThreads + (int)threadIdx.x;
     const int t0 = (int)blockIdx.x * kDirectMaxTiles;
     const int n = min(kDirectMaxTiles, a.tiles - t0);
-    // a group's tpg lanes sit in one wave and leave together
     if (g >= NG) return;
-    int32_t tot = 0, pre = 0;
-    column_sums(a.desc + (uint32_t)t0 * (uint32_t)NG + g, (uint32_t)NG, n, 0, r, tpg, tot, pre);
-    for (int o = 1; o < tpg; o <<= 1) tot += __shfl_xor(tot, o, kWave);
-    if (r == 0) a.chunk_sums[(int64_t)blockIdx.x * NG + g] = (uint32_t)tot;
+    uint32_t* col = a.desc + (uint32_t)t0 * (uint32_t)NG + g;
+    uint32_t run = 0;
+    for (int j0 = 0; j0 < n; j0 += kDirectBatch) {
+        uint32_t v[kDirectBatch];
+#pragma unroll
+        for (int i = 0; i < kDirectBatch; ++i) v[i] = col[(uint32_t)min(j0 + i, n - 1) * (uint32_t)NG];
+        __builtin_amdgcn_sched_barrier(0);  // the whole batch in flight first
+#pragma unroll
+        for (int i = 0; i < kDirectBatch; ++i) {
+            if (j0 + i < n) {
+                col[(uint32_t)(j0 + i) * (uint32_t)NG] = run;
+                run += v[i];
+            }
+        }
+    }
+    a.chunk_sums[(int64_t)blockIdx.x * NG + g] = run;
 }
 
 // CHUNKS (direct mode past kDirectMaxTiles tiles): the column sums come
 // from the chunk sums plus the tile's own chunk; a separate instantiation,
 // so that the common case keeps its own register allocation (it measured
-// 0.4 us slower with a run-time branch here).
-template <int SPT, int MODE, bool CHUNKS = false>
+// 0.4 us slower with a run-time branch here).  MAXG (256 or EP_MAX_GROUPS)
+// sizes the LDS arrays: up to 256 groups a workgroup takes 9 KiB of LDS
+// instead of 72 KiB, so that several fit on a CU when there are more
+// workgroups than CUs.
+template <int SPT, int MODE, bool CHUNKS = false, int MAXG = EP_MAX_GROUPS>
 __global__ __launch_bounds__(kLayoutThreads) void k_layout_rank(LayoutArgs a) {
     constexpr bool DIRECT = MODE == kLayoutDirect, SMALL = MODE == kLayoutSmall, COUNT = MODE == kLayoutCount;
     constexpr int kTileSlots = kLayoutThreads * SPT;
     constexpr int kSlotsPerWave = kWave * SPT;
-    __shared__ __align__(16) int32_t s_cnt[EP_MAX_GROUPS];    // group totals
-    __shared__ __align__(16) int32_t s_start[EP_MAX_GROUPS];  // first row of the group (clamped at capacity)
-    __shared__ __align__(16) int32_t s_lim[EP_MAX_GROUPS];    // first row past the segment's capacity
-    __shared__ int32_t s_pref[EP_MAX_GROUPS];   // slots of the group in earlier tiles
-    __shared__ int32_t s_gof[EP_MAX_GROUPS];    // group of each routed expert
-    __shared__ int32_t s_wcnt[kLayoutWaves][EP_MAX_GROUPS];  // per-wave counts / prefixes (a 4-byte word each)
+    constexpr int J = MAXG / kLayoutThreads;  // groups per thread in the per-group loops
+    static_assert(MAXG % 8 == 0 && MAXG <= EP_MAX_GROUPS, "group arrays");
+    __shared__ __align__(16) int32_t s_cnt[MAXG];    // group totals
+    __shared__ __align__(16) int32_t s_start[MAXG];  // first row of the group (clamped at capacity)
+    __shared__ __align__(16) int32_t s_lim[MAXG];    // first row past the segment's capacity
+    __shared__ int32_t s_pref[MAXG];   // slots of the group in earlier tiles
+    __shared__ int32_t s_gof[MAXG];    // group of each routed expert
+    __shared__ int32_t s_wcnt[kLayoutWaves][MAXG];  // per-wave counts / prefixes (a 4-byte word each)
     __shared__ int32_t s_wsum[kLayoutWaves];
     __shared__ int32_t s_flag;
 
@@ -302,11 +318,10 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout_rank(LayoutArgs a) {
     }
     // Direct path: the group totals and this tile's in-group prefix from the
     // [tile][group] table; past kDirectMaxTiles tiles from the chunk sums
-    // (totals, and the prefix over earlier chunks) plus the rows of this
-    // tile's own chunk before it.  Workgroups past the last tile need only
-    // the totals.
+    // (totals, and the prefix over earlier chunks) plus this tile's row,
+    // which k_layout_chunks turned into prefixes within its chunk.
+    // Workgroups past the last tile need only the totals.
     const int my_chunk = CHUNKS ? min((int)(tile / kDirectMaxTiles), a.chunks) : 0;
-    const int c0 = my_chunk * kDirectMaxTiles;
     const bool in_chunk = CHUNKS && tile < (uint32_t)a.tiles;
     if (DIRECT && EPX_DIRECT_QUADS && (NG & 3) == 0 && NG <= 128) {
         // Four groups per 16-byte load (rows are 16-byte aligned when
@@ -329,11 +344,15 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout_rank(LayoutArgs a) {
             if (!CHUNKS) {
                 quad_sums(table + q, (uint32_t)Q, a.tiles, (int)tile, r, tpq, tot, pre);
             } else {
+                // the tile's own row of in-chunk prefixes, in flight with
+                // the chunk-sum loads; one lane of the quad adds it
+                const uint4 own = table[(uint32_t)min((int)tile, a.tiles - 1) * (uint32_t)Q + (uint32_t)q];
                 quad_sums(chunks + q, (uint32_t)Q, a.chunks, my_chunk, r, tpq, tot, pre);
-                if (in_chunk) {
-                    int32_t t2[4] = {0, 0, 0, 0};
-                    quad_sums(table + (uint32_t)c0 * (uint32_t)Q + q, (uint32_t)Q, min(kDirectMaxTiles, a.tiles - c0),
-                              (int)tile - c0, r, tpq, t2, pre);
+                if (r == 0 && in_chunk) {
+                    pre[0] += (int32_t)own.x;
+                    pre[1] += (int32_t)own.y;
+                    pre[2] += (int32_t)own.z;
+                    pre[3] += (int32_t)own.w;
                 }
             }
             for (int o = 1; o < tpq; o <<= 1) {
@@ -363,12 +382,9 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout_rank(LayoutArgs a) {
             if (!CHUNKS) {
                 column_sums(a.desc + g, (uint32_t)NG, a.tiles, (int)tile, r, tpg, tot, pre);
             } else {
+                const uint32_t own = a.desc[(uint32_t)min((int)tile, a.tiles - 1) * (uint32_t)NG + (uint32_t)g];
                 column_sums(a.chunk_sums + g, (uint32_t)NG, a.chunks, my_chunk, r, tpg, tot, pre);
-                if (in_chunk) {
-                    int32_t t2 = 0;
-                    column_sums(a.desc + (uint32_t)c0 * (uint32_t)NG + g, (uint32_t)NG,
-                                min(kDirectMaxTiles, a.tiles - c0), (int)tile - c0, r, tpg, t2, pre);
-                }
+                if (r == 0 && in_chunk) pre += (int32_t)own;
             }
             for (int o = 1; o < tpg; o <<= 1) {
                 tot += __shfl_xor(tot, o, kWave);
@@ -391,7 +407,7 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout_rank(LayoutArgs a) {
     // In-tile ranks (per-wave running counters + match-any), then the
     // per-wave exclusive prefixes and the tile's aggregate per group.
     uint32_t key[SPT], rnk[SPT];
-    int32_t agg[EP_MAX_GROUPS / kLayoutThreads];
+    int32_t agg[J];
     auto rank_slots = [&]() {
         // ---- in-tile ranks (per-wave running counters + match-any) ----
         const int nbits = 32 - __clz(NG);
@@ -417,7 +433,7 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout_rank(LayoutArgs a) {
 
         // ---- per-wave exclusive prefixes and the tile aggregate per group ----
 #pragma unroll
-        for (int j = 0; j < EP_MAX_GROUPS / kLayoutThreads; ++j) {
+        for (int j = 0; j < J; ++j) {
             const int g = tid + j * kLayoutThreads;
             agg[j] = 0;
             if (g < NG) {
@@ -437,7 +453,7 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout_rank(LayoutArgs a) {
     if (SMALL) {
         rank_slots();
 #pragma unroll
-        for (int j = 0; j < EP_MAX_GROUPS / kLayoutThreads; ++j) {
+        for (int j = 0; j < J; ++j) {
             const int g = tid + j * kLayoutThreads;
             if (g < NG) {
                 s_cnt[g] = agg[j] + (g == shared_group ? a.T : 0);
@@ -448,16 +464,22 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout_rank(LayoutArgs a) {
     }
 
     // ---- aligned exclusive prefix P over all groups (segment-major) ----
-    // Thread i covers groups [8i, 8i + 8); NG <= 2048 = 256 * 8.  Counts,
+    // Thread i covers groups [8i, 8i + 8) (NG <= MAXG <= 2048 = 256 * 8;
+    // threads past MAXG / 8 hold none).  Counts,
     // starts and limits move between LDS and registers as 16-byte vectors
     // and no step branches per group, so each pass waits on LDS once rather
     // than once per group (measured on MI355X: this phase took 1.9 us of the
     // DeepSeek-V3 rank launch with a branch and a load per group).
+    const bool has8 = tid * 8 < MAXG;
     int32_t P[8], al[8];
     int32_t tsum = 0;
     {
         const int4* c4 = reinterpret_cast<const int4*>(s_cnt) + 2 * tid;
-        const int4 lo = c4[0], hi = c4[1];
+        int4 lo = make_int4(0, 0, 0, 0), hi = lo;
+        if (has8) {
+            lo = c4[0];
+            hi = c4[1];
+        }
         int32_t c[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
         const int32_t A = a.A;
 #pragma unroll
@@ -491,11 +513,13 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout_rank(LayoutArgs a) {
     }
     int4* st4 = reinterpret_cast<int4*>(s_start) + 2 * tid;
     int4* li4 = reinterpret_cast<int4*>(s_lim) + 2 * tid;
-    st4[0] = make_int4(P[0], P[1], P[2], P[3]);
-    st4[1] = make_int4(P[4], P[5], P[6], P[7]);
-    if (a.C == 0) {  // without a capacity a group starts at P and nothing is dropped
-        li4[0] = make_int4(0x7FFFFFFF, 0x7FFFFFFF, 0x7FFFFFFF, 0x7FFFFFFF);
-        li4[1] = li4[0];
+    if (has8) {
+        st4[0] = make_int4(P[0], P[1], P[2], P[3]);
+        st4[1] = make_int4(P[4], P[5], P[6], P[7]);
+        if (a.C == 0) {  // without a capacity a group starts at P and nothing is dropped
+            li4[0] = make_int4(0x7FFFFFFF, 0x7FFFFFFF, 0x7FFFFFFF, 0x7FFFFFFF);
+            li4[1] = li4[0];
+        }
     }
     __syncthreads();
 
@@ -540,10 +564,12 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout_rank(LayoutArgs a) {
             li[j] = (seg[j] + 1) * a.C;
         }
         __syncthreads();
-        st4[0] = make_int4(st[0], st[1], st[2], st[3]);
-        st4[1] = make_int4(st[4], st[5], st[6], st[7]);
-        li4[0] = make_int4(li[0], li[1], li[2], li[3]);
-        li4[1] = make_int4(li[4], li[5], li[6], li[7]);
+        if (has8) {
+            st4[0] = make_int4(st[0], st[1], st[2], st[3]);
+            st4[1] = make_int4(st[4], st[5], st[6], st[7]);
+            li4[0] = make_int4(li[0], li[1], li[2], li[3]);
+            li4[1] = make_int4(li[4], li[5], li[6], li[7]);
+        }
     }
 
     if (!SMALL) rank_slots();
@@ -1211,25 +1237,34 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout_sp(LayoutArgs a) {
 
 }  // namespace
 
+// The rank kernel with LDS arrays for at most 256 groups where they suffice.
+template <int SPT, int MODE, bool CHUNKS>
+void launch_rank(const LayoutArgs& a, hipStream_t stream) {
+    if (a.NG <= kLayoutThreads)
+        hipLaunchKernelGGL((k_layout_rank<SPT, MODE, CHUNKS, kLayoutThreads>), dim3((unsigned)a.rank_blocks),
+                           dim3(kLayoutThreads), 0, stream, a);
+    else
+        hipLaunchKernelGGL((k_layout_rank<SPT, MODE, CHUNKS, EP_MAX_GROUPS>), dim3((unsigned)a.rank_blocks),
+                           dim3(kLayoutThreads), 0, stream, a);
+}
+
 template <int SPT>
 void launch_spt(const LayoutArgs& a, hipStream_t stream) {
     const dim3 block(kLayoutThreads);
     if (a.mode == kLayoutSmall) {
-        hipLaunchKernelGGL((k_layout_rank<SPT, kLayoutSmall>), dim3((unsigned)a.rank_blocks), block, 0, stream, a);
+        launch_rank<SPT, kLayoutSmall, false>(a, stream);
     } else if (a.mode == kLayoutCount) {
-        hipLaunchKernelGGL((k_layout_rank<SPT, kLayoutCount>), dim3((unsigned)a.rank_blocks), block, 0, stream, a);
+        launch_rank<SPT, kLayoutCount, false>(a, stream);
     } else if (a.mode == kLayoutDirect) {
         hipLaunchKernelGGL((k_layout_hist<SPT>), dim3((unsigned)a.tiles), block, 0, stream, a);
-        if (a.chunks > 0) {
-            const int per_block = kLayoutThreads / direct_lanes_per_group(a.NG);
-            hipLaunchKernelGGL(k_layout_chunks, dim3((unsigned)a.chunks, (unsigned)((a.NG + per_block - 1) / per_block)),
-                               block, 0, stream, a);
-        }
         if (a.chunks > 0)
-            hipLaunchKernelGGL((k_layout_rank<SPT, kLayoutDirect, true>), dim3((unsigned)a.rank_blocks), block, 0,
-                               stream, a);
+            hipLaunchKernelGGL(k_layout_chunks,
+                               dim3((unsigned)a.chunks, (unsigned)((a.NG + kLayoutThreads - 1) / kLayoutThreads)), block,
+                               0, stream, a);
+        if (a.chunks > 0)
+            launch_rank<SPT, kLayoutDirect, true>(a, stream);
         else
-            hipLaunchKernelGGL((k_layout_rank<SPT, kLayoutDirect>), dim3((unsigned)a.rank_blocks), block, 0, stream, a);
+            launch_rank<SPT, kLayoutDirect, false>(a, stream);
     } else if (a.NG <= kLayoutThreads) {
         if (a.lookback)
             hipLaunchKernelGGL((k_layout_sp<SPT, kLayoutThreads, true>), dim3((unsigned)a.rank_blocks), block, 0,
