@@ -523,9 +523,14 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout_rank(LayoutArgs a) {
     }
     __syncthreads();
 
-    // Counts (direct and single-pass paths), offsets and segment bases: one
-    // tile writes them.
-    if (tile == 0) {
+    // Counts, offsets and segment bases: the last workgroup writes them.  It
+    // owns no tile when there are more workgroups than tiles, and otherwise
+    // the last, possibly ragged one; the tile-0 workgroup, which writes the
+    // flags word and (on the small path) every slot's results, stays off
+    // this chain of LDS reads (phase stamps at the DeepSeek-V3 share: the
+    // writer workgroup ran 1 us longer than the median one, and the rank
+    // launch ends with its slowest workgroup).
+    if (tile == gridDim.x - 1) {
         for (int g = tid; g < NG; g += kLayoutThreads) a.out.counts[g] = s_cnt[g];
         const int n = a.S * (G + 1);
         for (int idx = tid; idx < n; idx += kLayoutThreads) {
