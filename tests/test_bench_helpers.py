@@ -51,3 +51,22 @@ def test_profile_readers_follow_the_digest(tree):
     assert bench.in_step_for("dsv3") is None                       # kernels changed since the trace
     assert bench.traffic_for("dispatch", "dsv3") is None
 
+
+
+def test_profile_summarizer_maps_kernels_to_ops():
+    """bench_profiles.py attributes each traced kernel to the bench op it
+    serves (the rank kernel's second template argument is its path)."""
+    import bench_profiles as bp
+
+    assert bp.short("void epx::(anonymous namespace)::k_scatter<false, true>(epx::MoveArgs)") == "k_scatter<false, true>"
+    cases = {"k_scatter<false, true>": "dispatch", "k_scatter<true, true>": "combine_bwd",
+             "k_gather<true, true>": "combine", "k_gather<false, true>": "dispatch_bwd",
+             "k_layout_hist<2>": "layout_hist", "k_layout_rank<2, 1, false, 256>": "layout_rank",
+             "k_layout_rank<1, 3, false, 256>": "layout_count", "k_layout_rank<1, 2, false, 2048>": "layout_small",
+             "k_layout_sp<4, 256, true>": "layout_lookback", "k_layout_sp<4, 256, false>": "layout_barrier",
+             "k_nvfp4_wg<1>": "dispatch_nvfp4", "k_fp8_wg<8, false>": "dispatch_fp8",
+             "k_combine_nvfp4<true>": "combine_nvfp4", "k_probs_grad": "combine_bwd_probs",
+             "k_layout_chunks": None}
+    for k, op in cases.items():
+        assert bp.op_of(k) == op, k
+    assert bp.pattern_of("k_gather<true, true>") == "gather" and bp.pattern_of("k_scatter<false, true>") == "scatter"
