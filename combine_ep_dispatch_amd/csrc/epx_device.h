@@ -245,6 +245,18 @@ __device__ __forceinline__ int32_t wave_inclusive_sum(int32_t v) {
     return v;
 }
 
+// Workgroup barrier for LDS traffic only: the fences order LDS accesses
+// (a wait on the LDS counter) but not global memory, so global loads and
+// stores in flight stay in flight across it (__syncthreads also waits for
+// every outstanding global access of the wave, stores included).  Only for
+// code in which no thread reads global memory that another thread of its
+// workgroup wrote.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // Lanes of the wave holding the same key as this lane.  Every lane of the
 // wave must be active; keys are < 2^nbits.
 __device__ __forceinline__ uint64_t match_any(uint32_t key, int nbits) {

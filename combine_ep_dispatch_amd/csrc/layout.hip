@@ -111,7 +111,7 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout_hist(LayoutArgs a) {
     for (int g = tid; g < a.NG; g += kLayoutThreads) s_hist[g] = 0;
     for (int e = tid; e < a.E; e += kLayoutThreads)
         s_gof[e] = (e / a.E_loc) * a.G + a.shared + (e % a.E_loc);
-    __syncthreads();
+    lds_barrier();
 
 #pragma unroll
     for (int it = 0; it < SPT; ++it) {
@@ -122,7 +122,7 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout_hist(LayoutArgs a) {
         if (key != (uint32_t)a.NG && lanes_below(m) == 0)
             atomicAdd(&s_hist[key], (int32_t)__popcll(m));
     }
-    __syncthreads();
+    lds_barrier();
     uint32_t* row = a.desc + (int64_t)blockIdx.x * a.NG;
     for (int g = tid; g < a.NG; g += kLayoutThreads) row[g] = (uint32_t)s_hist[g];
     if (blockIdx.x == 0 && tid == 0) a.out.flags[0] = 0;
@@ -265,6 +265,52 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout_rank(LayoutArgs a) {
     const int32_t shared_group = a.shared ? a.src_seg * G : -1;
     if (tid == 0) s_flag = 0;
     int32_t flag = 0;
+
+    // In-tile ranks (per-wave running counters + match-any), then the
+    // per-wave exclusive prefixes and the tile's aggregate per group.
+    uint32_t key[SPT], rnk[SPT];
+    int32_t agg[J];
+    auto rank_slots = [&]() {
+        // ---- in-tile ranks (per-wave running counters + match-any) ----
+        const int nbits = 32 - __clz(NG);
+#pragma unroll
+        for (int it = 0; it < SPT; ++it) {
+            const int32_t e = eid[it];
+            const uint32_t k = (uint32_t)e < (uint32_t)a.E ? (uint32_t)s_gof[e] : (uint32_t)NG;
+            if (e != -1 && (uint32_t)e >= (uint32_t)a.E) flag |= EP_FLAG_BAD_ID;  // -1 = masked slot
+            const uint64_t m = match_any(k, nbits);
+            const uint32_t r = lanes_below(m);
+            // only the lowest lane of each key touches LDS; the others take
+            // its value by a cross-lane read
+            int32_t before = 0;
+            if (k != (uint32_t)NG && r == 0) {
+                before = s_wcnt[w][k];
+                s_wcnt[w][k] = before + (int32_t)__popcll(m);
+            }
+            before = __shfl(before, (int)__builtin_ctzll(m), kWave);
+            rnk[it] = k != (uint32_t)NG ? (uint32_t)before + r : 0u;
+            key[it] = k;
+        }
+        lds_barrier();
+
+        // ---- per-wave exclusive prefixes and the tile aggregate per group ----
+#pragma unroll
+        for (int j = 0; j < J; ++j) {
+            const int g = tid + j * kLayoutThreads;
+            agg[j] = 0;
+            if (g < NG) {
+                int32_t run = 0;
+#pragma unroll
+                for (int w2 = 0; w2 < kLayoutWaves; ++w2) {
+                    const int32_t c = s_wcnt[w2][g];
+                    s_wcnt[w2][g] = run;
+                    run += c;
+                }
+                agg[j] = run;
+            }
+        }
+    };
+
     if (COUNT) {
         // Group totals and this tile's in-group prefix by counting every
         // routed slot in LDS: slots before the tile into s_pref, the rest
@@ -275,7 +321,7 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout_rank(LayoutArgs a) {
         }
         for (int e = tid; e < a.E; e += kLayoutThreads)
             s_gof[e] = (e / a.E_loc) * G + a.shared + (e % a.E_loc);
-        __syncthreads();
+        lds_barrier();
         const int64_t mine0 = (int64_t)tile * kTileSlots;
         auto count = [&](int32_t e, int64_t f) {
             if ((uint32_t)e < (uint32_t)a.E)
@@ -312,9 +358,49 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout_rank(LayoutArgs a) {
         }
         for (int64_t f = tid; f < head; f += kLayoutThreads) count(a.topk_ids[f], f);
         for (int64_t f = head + 4 * nvec + tid; f < routed; f += kLayoutThreads) count(a.topk_ids[f], f);
-        __syncthreads();
+        lds_barrier();
         for (int g = tid; g < NG; g += kLayoutThreads)
             s_cnt[g] = s_cnt[g] + s_pref[g] + (g == shared_group ? a.T : 0);
+    }
+    // Direct path with one group per lane and one batch of column loads
+    // (129 to 256 groups and at most kDirectBatch tiles, as at the DeepSeek-V3
+    // share): the loads go out first, and the in-tile ranks, which need none
+    // of them, run while they are in flight (the workgroup barriers here
+    // wait on LDS only).
+    const bool early = DIRECT && !CHUNKS && MAXG == kLayoutThreads && NG > kLayoutThreads / 2 &&
+                       a.tiles <= kDirectBatch;
+    if (early) {
+        for (int e = tid; e < a.E; e += kLayoutThreads)
+            s_gof[e] = (e / a.E_loc) * G + a.shared + (e % a.E_loc);
+#pragma unroll
+        for (int w2 = 0; w2 < kLayoutWaves; ++w2)
+            if (tid < NG) s_wcnt[w2][tid] = 0;
+        lds_barrier();
+        // The ids must be in before the column loads go out: a wait on them
+        // with the column loads in flight would also wait on the first of
+        // those (the vector-memory counter a wait names holds at most 63).
+        int32_t ids = 0;
+#pragma unroll
+        for (int it = 0; it < SPT; ++it) ids |= eid[it];
+        __asm__ volatile("" : : "v"(ids));
+        const uint32_t* col = a.desc + min(tid, NG - 1);
+        uint32_t v[kDirectBatch];
+#pragma unroll
+        for (int i = 0; i < kDirectBatch; ++i) v[i] = col[(uint32_t)min(i, a.tiles - 1) * (uint32_t)NG];
+        __builtin_amdgcn_sched_barrier(0);
+        rank_slots();
+        int32_t tot = 0, pre = 0;
+#pragma unroll
+        for (int i = 0; i < kDirectBatch; ++i) {
+            const int32_t c = i < a.tiles ? (int32_t)v[i] : 0;
+            tot += c;
+            pre += i < (int)tile ? c : 0;
+        }
+        if (tid < NG) {
+            s_cnt[tid] = tot + (tid == shared_group ? a.T : 0);
+            s_pref[tid] = pre;
+        }
+        lds_barrier();
     }
     // Direct path: the group totals and this tile's in-group prefix from the
     // [tile][group] table; past kDirectMaxTiles tiles from the chunk sums
@@ -371,7 +457,7 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout_rank(LayoutArgs a) {
                 }
             }
         }
-    } else if (DIRECT) {
+    } else if (DIRECT && !early) {
         // tpg (a power of two, tpg * NG <= 256) lanes share a group; their
         // partial sums meet by xor-shuffles inside the lane group (all lanes
         // of a group are active or inactive together).
@@ -396,58 +482,15 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout_rank(LayoutArgs a) {
             }
         }
     }
-    if (!COUNT)
-        for (int e = tid; e < a.E; e += kLayoutThreads)
-            s_gof[e] = (e / a.E_loc) * G + a.shared + (e % a.E_loc);
+    if (!early) {
+        if (!COUNT)
+            for (int e = tid; e < a.E; e += kLayoutThreads)
+                s_gof[e] = (e / a.E_loc) * G + a.shared + (e % a.E_loc);
 #pragma unroll
-    for (int w2 = 0; w2 < kLayoutWaves; ++w2)
-        for (int g = tid; g < NG; g += kLayoutThreads) s_wcnt[w2][g] = 0;
-    __syncthreads();
-
-    // In-tile ranks (per-wave running counters + match-any), then the
-    // per-wave exclusive prefixes and the tile's aggregate per group.
-    uint32_t key[SPT], rnk[SPT];
-    int32_t agg[J];
-    auto rank_slots = [&]() {
-        // ---- in-tile ranks (per-wave running counters + match-any) ----
-        const int nbits = 32 - __clz(NG);
-#pragma unroll
-        for (int it = 0; it < SPT; ++it) {
-            const int32_t e = eid[it];
-            const uint32_t k = (uint32_t)e < (uint32_t)a.E ? (uint32_t)s_gof[e] : (uint32_t)NG;
-            if (e != -1 && (uint32_t)e >= (uint32_t)a.E) flag |= EP_FLAG_BAD_ID;  // -1 = masked slot
-            const uint64_t m = match_any(k, nbits);
-            const uint32_t r = lanes_below(m);
-            // only the lowest lane of each key touches LDS; the others take
-            // its value by a cross-lane read
-            int32_t before = 0;
-            if (k != (uint32_t)NG && r == 0) {
-                before = s_wcnt[w][k];
-                s_wcnt[w][k] = before + (int32_t)__popcll(m);
-            }
-            before = __shfl(before, (int)__builtin_ctzll(m), kWave);
-            rnk[it] = k != (uint32_t)NG ? (uint32_t)before + r : 0u;
-            key[it] = k;
-        }
-        __syncthreads();
-
-        // ---- per-wave exclusive prefixes and the tile aggregate per group ----
-#pragma unroll
-        for (int j = 0; j < J; ++j) {
-            const int g = tid + j * kLayoutThreads;
-            agg[j] = 0;
-            if (g < NG) {
-                int32_t run = 0;
-#pragma unroll
-                for (int w2 = 0; w2 < kLayoutWaves; ++w2) {
-                    const int32_t c = s_wcnt[w2][g];
-                    s_wcnt[w2][g] = run;
-                    run += c;
-                }
-                agg[j] = run;
-            }
-        }
-    };
+        for (int w2 = 0; w2 < kLayoutWaves; ++w2)
+            for (int g = tid; g < NG; g += kLayoutThreads) s_wcnt[w2][g] = 0;
+        lds_barrier();
+    }
 
     // Single pass: the group totals come from ranking the one tile.
     if (SMALL) {
@@ -460,7 +503,7 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout_rank(LayoutArgs a) {
                 s_pref[g] = 0;
             }
         }
-        __syncthreads();
+        lds_barrier();
     }
 
     // ---- aligned exclusive prefix P over all groups (segment-major) ----
@@ -496,7 +539,7 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout_rank(LayoutArgs a) {
     }
     const int32_t incl = wave_inclusive_sum(tsum);
     if (lane == kWave - 1) s_wsum[w] = incl;
-    __syncthreads();
+    lds_barrier();
     int32_t wbase = 0, total = 0;
 #pragma unroll
     for (int w2 = 0; w2 < kLayoutWaves; ++w2) {
@@ -521,7 +564,7 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout_rank(LayoutArgs a) {
             li4[1] = li4[0];
         }
     }
-    __syncthreads();
+    lds_barrier();
 
     // Counts, offsets and segment bases: the last workgroup writes them.  It
     // owns no tile when there are more workgroups than tiles, and otherwise
@@ -568,7 +611,7 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout_rank(LayoutArgs a) {
             st[j] = seg[j] * a.C + min(P[j] - segp[j], a.C);
             li[j] = (seg[j] + 1) * a.C;
         }
-        __syncthreads();
+        lds_barrier();
         if (has8) {
             st4[0] = make_int4(st[0], st[1], st[2], st[3]);
             st4[1] = make_int4(st[4], st[5], st[6], st[7]);
@@ -577,9 +620,9 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout_rank(LayoutArgs a) {
         }
     }
 
-    if (!SMALL) rank_slots();
+    if (!SMALL && !early) rank_slots();
 
-    __syncthreads();
+    lds_barrier();
 
     // ---- write the routed slots of this tile ----
     const uint32_t R = (uint32_t)a.recv_rows;
@@ -674,12 +717,12 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout_rank(LayoutArgs a) {
             if (end > st && end > R) flag |= EP_FLAG_INTERNAL;
         }
         if (flag) atomicOr(&s_flag, flag);
-        __syncthreads();
+        lds_barrier();
         if (tid == 0) a.out.flags[0] = s_flag;
         return;
     }
     if (flag) atomicOr(&s_flag, flag);
-    __syncthreads();
+    lds_barrier();
     if (tid == 0 && s_flag) atomicOr(a.out.flags, s_flag);
 }
 
