@@ -63,7 +63,7 @@ def test_named_workload_full_size(G, name):
 
 
 # Wider sweeps: EPX_GPU_SEEDS=2000 (about 3 minutes on the MI355X) and
-# EPX_GPU_LARGE_SEEDS=60 (6.5-7.6 s per large seed, about 8 minutes);
+# EPX_GPU_LARGE_SEEDS=50 (6.5-10.8 s per large seed, at most 9 minutes);
 # EPX_GPU_SEED_BASE shifts both seed ranges to explore new cases.
 SEED_BASE = int(os.environ.get("EPX_GPU_SEED_BASE", "0"))
 SEEDS = int(os.environ.get("EPX_GPU_SEEDS", "128"))
