@@ -48,8 +48,13 @@
 //                     inside their groups (per-wave running counters in LDS,
 //                     one 4-byte word per group so neighbouring groups share
 //                     no bank word, touched only by the lowest lane of each
-//                     match set), and writes counts (tile 0), offsets,
-//                     token_row and src_info.  The fused shared-expert rows,
+//                     match set), and writes token_row and src_info; the
+//                     last workgroup writes counts, offsets and segment
+//                     bases.  With one group per lane and one batch of
+//                     column loads the loads go out before the in-tile
+//                     ranks, which run while they are in flight (the
+//                     layout kernels' barriers wait on LDS only, see
+//                     lds_barrier).  The fused shared-expert rows,
 //                     and expert_ids of whole groups (pad rows included) as
 //                     coalesced runs, are spread over at least
 //                     min(groups, 256) workgroups.
@@ -69,7 +74,7 @@
 // memory-side loads across the XCDs, which costs more than the second
 // launch.  The barrier flavour reads every tile's counts in every
 // workgroup, so its cost grows with the square of the tile count (29 ms at
-// 2^24 slots).
+// 2^24 slots); it is refused past 2^20 routed slots.
 #include "epx_device.h"
 
 namespace epx {
