@@ -70,3 +70,56 @@ def test_profile_summarizer_maps_kernels_to_ops():
     for k, op in cases.items():
         assert bp.op_of(k) == op, k
     assert bp.pattern_of("k_gather<true, true>") == "gather" and bp.pattern_of("k_scatter<false, true>") == "scatter"
+
+
+def test_profile_summarizer_step_timeline(tmp_path, monkeypatch):
+    """bench_profiles.py takes the in-step durations from the steps whose
+    kernels run back to back (the timed eager steps and the graph replays),
+    leaves out the eager steps with an event between ops, and reports the
+    idle time between consecutive back-to-back steps."""
+    import csv
+
+    import bench_profiles as bp
+
+    names = ["void epx::(anonymous namespace)::k_layout_hist<2>(epx::LayoutArgs)",
+             "void epx::(anonymous namespace)::k_layout_rank<2, 1, false, 256>(epx::LayoutArgs)",
+             "void epx::(anonymous namespace)::k_scatter<false, true>(epx::MoveArgs)",
+             "void epx::(anonymous namespace)::k_nvfp4_wg<1>(epx::Nvfp4Args)",
+             "void epx::(anonymous namespace)::k_gather<true, true>(epx::MoveArgs)",
+             "void epx::(anonymous namespace)::k_scatter<true, true>(epx::MoveArgs)",
+             "void epx::(anonymous namespace)::k_gather<false, true>(epx::MoveArgs)"]
+    dur_ns = [4000, 7000, 90000, 29000, 91000, 90000, 89000]
+    rows, t = [], 1_000_000
+
+    def step(gap_between_ops, gap_after):
+        nonlocal t
+        for n, d in zip(names, dur_ns):
+            rows.append({"Kernel_Name": n, "Start_Timestamp": t, "End_Timestamp": t + d})
+            t += d + gap_between_ops
+        t += gap_after - gap_between_ops
+
+    for _ in range(3):
+        step(0, 0)            # eager timed steps: back to back
+    for _ in range(3):
+        step(0, 8000)         # graph replays: 8 us between steps
+    for _ in range(2):
+        step(5600, 20000)     # eager steps with an event before every op
+    d = tmp_path / "run" / "p_trace_dsv3"
+    d.mkdir(parents=True)
+    with open(d / "dsv3_kernel_trace.csv", "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Kernel_Name", "Start_Timestamp", "End_Timestamp"])
+        w.writeheader()
+        w.writerows(rows)
+    (tmp_path / "profiles").mkdir()
+    monkeypatch.setattr(bp, "OUT", str(tmp_path / "run"))
+    monkeypatch.setattr(bp, "RUN", "run")
+    monkeypatch.setattr(bp, "PROF", str(tmp_path / "profiles"))
+    avg, in_step, whole = bp.trace_summary("dsv3")
+    assert in_step["dispatch"] == 90.0 and in_step["combine"] == 91.0 and in_step["layout_rank"] == 7.0
+    assert whole == sum(dur_ns) / 1e3
+    doc = json.loads((tmp_path / "profiles" / "kernel_trace_dsv3.json").read_text())
+    assert doc["steps"] == 6 and doc["eager_event_gap_us"] == 5.6
+    assert doc["in_step_us"]["layout"] == 11.0
+    md = (tmp_path / "profiles" / "kernel_trace_dsv3.md").read_text()
+    assert "3 graph-replay boundaries" not in md  # boundaries are counted between consecutive steps
+    assert "2 graph-replay boundaries, median 8.00 us" in md and "eager step boundaries, median 0.00 us" in md
