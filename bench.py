@@ -524,7 +524,8 @@ def latency_sweep(torch, epx, wl, dev, workload: str, token_counts) -> int:
     """Per-op latency (µs, graphs of 8 back-to-back launches, 3 untimed
     replays then the median of 10)
     of the workload's shape at each token count, plus the whole step (the
-    ops of the benchmark step, FP8 dispatch excluded).  One JSON line per T."""
+    ops of the benchmark step, FP8 dispatch excluded) and the layout and
+    dispatch made in one call.  One JSON line per T."""
     for T in token_counts:
         w = wl.CONFIGS[workload].at_tokens(T)
         d = wl.make_workload(w)
@@ -564,6 +565,9 @@ def latency_sweep(torch, epx, wl, dev, workload: str, token_counts) -> int:
                           ("combine_nvfp4", lambda: epx.ep_combine_nvfp4(cfg, lay, codes, scales, rowscale, probs,
                                                                          cq_y))]
         ops += [(n, (lambda n=n: epx.ep_dispatch_layout(paths[n], ids, path_ws[n], path_lay[n]))) for n in paths]
+        fl_lay, fl_ws = epx.Layout.empty(cfg, dev), epx.workspace_for(cfg, dev)
+        fl_recv = torch.empty(R * H, dtype=torch.bfloat16, device=dev)
+        ops += [("dispatch_with_layout", lambda: epx.ep_dispatch_with_layout(cfg, ids, fl_ws, fl_lay, x, fl_recv))]
         ops += [("step", lambda: [fn() for _, fn in step_ops])]
         step_ops[0][1]()
         torch.cuda.synchronize()

@@ -169,9 +169,14 @@ int layout_check(const Shape& d, const int32_t* topk_ids, const ep_layout_t* L) 
 }
 
 // Launch of the layout kernels, after layout_check and check_device; `ws`
-// holds at least d.ws_bytes bytes.
-int layout_launch(const Shape& d, const int32_t* topk_ids, void* ws, const ep_layout_t* L, void* stream) {
+// holds at least d.ws_bytes bytes.  With x and recv given, the small path
+// also copies the payload rows (*fused is set when it did).
+int layout_launch(const Shape& d, const int32_t* topk_ids, void* ws, const ep_layout_t* L, void* stream,
+                  const uint16_t* x = nullptr, uint16_t* recv = nullptr, bool* fused = nullptr) {
     LayoutArgs a;
+    a.x = nullptr;
+    a.recv = nullptr;
+    a.H = d.H;
     a.topk_ids = topk_ids;
     a.desc = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(ws) + kWorkspaceHeader);
     a.out = *L;
@@ -228,7 +233,10 @@ int layout_launch(const Shape& d, const int32_t* topk_ids, void* ws, const ep_la
         a.tiles = 1;
         a.rank_blocks = std::min<int32_t>(d.NG, 256);
         a.slots_per_thread = routed <= 256 ? 1 : (routed <= 512 ? 2 : 4);
+        a.x = x;
+        a.recv = recv;
     }
+    if (fused) *fused = a.x != nullptr;
     return status_of(launch_layout(a, static_cast<hipStream_t>(stream)));
 }
 
@@ -315,6 +323,22 @@ int ep_dispatch(const ep_cfg_t* cfg, const ep_layout_t* layout, const uint16_t* 
     if ((rc = check_device()) != EP_OK) return rc;
     hipStream_t st = static_cast<hipStream_t>(stream);
     if ((rc = status_of(launch_scatter(move_args(d, layout, x, recv, nullptr), st))) != EP_OK) return rc;
+    return zero_pad(d, layout, recv, (int64_t)d.H * 2, st);
+}
+
+int ep_dispatch_with_layout(const ep_cfg_t* cfg, const int32_t* topk_ids, void* workspace, int64_t workspace_bytes,
+                            const ep_layout_t* layout, const uint16_t* x, uint16_t* recv, void* stream) {
+    Shape d;
+    int rc = derive(cfg, &d);
+    if (rc != EP_OK) return rc;
+    if ((rc = layout_check(d, topk_ids, layout)) != EP_OK) return rc;
+    if (workspace == nullptr || misaligned(workspace, 16) || workspace_bytes < d.ws_bytes) return EP_EINVAL;
+    if (bad_buffer(x, (int64_t)d.T * d.H * 2, 16) || bad_buffer(recv, d.R * d.H * 2, 16)) return EP_EINVAL;
+    if ((rc = check_device()) != EP_OK) return rc;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    bool fused = false;
+    if ((rc = layout_launch(d, topk_ids, workspace, layout, stream, x, recv, &fused)) != EP_OK) return rc;
+    if (!fused && (rc = status_of(launch_scatter(move_args(d, layout, x, recv, nullptr), st))) != EP_OK) return rc;
     return zero_pad(d, layout, recv, (int64_t)d.H * 2, st);
 }
 

@@ -245,6 +245,7 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout_rank(LayoutArgs a) {
     __shared__ int32_t s_wcnt[kLayoutWaves][MAXG];  // per-wave counts / prefixes (a 4-byte word each)
     __shared__ int32_t s_wsum[kLayoutWaves];
     __shared__ int32_t s_flag;
+    __shared__ int32_t s_rowof[SMALL ? kTileSlots : 1];  // small path with the dispatch fused: each slot's row
 
     const int tid = threadIdx.x, lane = tid & (kWave - 1), w = tid / kWave;
     const int NG = a.NG, G = a.G;
@@ -704,6 +705,43 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout_rank(LayoutArgs a) {
                 a.out.src_info[2 * (int64_t)row] = -1;
                 a.out.src_info[2 * (int64_t)row + 1] = -1;
             }
+        }
+    }
+
+    // ---- small path with the bf16 dispatch fused in: every workgroup
+    // ranked the whole tile, so each knows every slot's row; workgroup b
+    // copies the payload rows of slots (then shared-expert tokens) b,
+    // b + gridDim.x, ..., with the same rows and drops as token_row ----
+    if (SMALL && a.x != nullptr) {
+#pragma unroll
+        for (int it = 0; it < SPT; ++it) {
+            const int64_t f = wslot0 + it * kWave + lane;
+            if (f >= routed) continue;
+            const uint32_t g = key[it];
+            int32_t row = -1;
+            if (g != (uint32_t)NG) {
+                const uint32_t r = (uint32_t)s_start[g] + (uint32_t)s_pref[g] + (uint32_t)s_wcnt[w][g] + rnk[it];
+                if (r < (uint32_t)s_lim[g] && r < R) row = (int32_t)r;
+            }
+            s_rowof[f] = row;
+        }
+        lds_barrier();
+        const int32_t items = (int32_t)routed + (a.shared ? a.T : 0);
+        const int32_t nv = a.H / 8;  // 16-byte vectors per row
+        for (int32_t i = (int32_t)blockIdx.x; i < items; i += (int32_t)gridDim.x) {
+            int32_t row, t;
+            if (i < (int32_t)routed) {
+                row = s_rowof[i];
+                t = i / a.K;
+            } else {
+                t = i - (int32_t)routed;
+                const uint32_t r = (uint32_t)s_start[shared_group] + (uint32_t)t;
+                row = (r < (uint32_t)s_lim[shared_group] && r < R) ? (int32_t)r : -1;
+            }
+            if (row < 0) continue;
+            const uint4* src = reinterpret_cast<const uint4*>(a.x + (int64_t)t * a.H);
+            uint4* dst = reinterpret_cast<uint4*>(a.recv + (int64_t)row * a.H);
+            for (int32_t v = tid; v < nv; v += kLayoutThreads) dst[v] = src[v];
         }
     }
 

@@ -220,6 +220,21 @@ int ep_dispatch(const ep_cfg_t* cfg, const ep_layout_t* layout, const uint16_t* 
                 uint16_t* recv, void* stream);
 
 /*
+ * Layout and bf16 dispatch in one call ([FA] HybridEPDispatch.forward: the
+ * permutation and the dispatch of one batch in a single call).  Same
+ * arguments, outputs and errors as ep_dispatch_layout followed by
+ * ep_dispatch on the same stream, and the same results bit for bit.  Up to
+ * 512 routed slots (T*K; decode-sized batches) with no EP_LAYOUT_* path
+ * flag, one kernel computes the layout and copies the payload rows: every
+ * workgroup already ranks all slots there, so the copy needs no second
+ * launch.  Larger batches, or a forced path, run the layout launches and
+ * then the dispatch scatter.
+ */
+int ep_dispatch_with_layout(const ep_cfg_t* cfg, const int32_t* topk_ids, void* workspace,
+                            int64_t workspace_bytes, const ep_layout_t* layout, const uint16_t* x,
+                            uint16_t* recv, void* stream);
+
+/*
  * NVFP4 dispatch with a per-token dynamic global scale ([MX] execute):
  * every token is quantized once and its bytes written to each kept row.
  *   x         bf16 [T, H] (H % 16 == 0)

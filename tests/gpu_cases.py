@@ -231,6 +231,22 @@ def check_dispatch(c: Case, lay: epx.Layout, name: str):
     assert_bits_equal(bits_of(recv), want, f"{name}: recv")
 
 
+def check_dispatch_with_layout(c: Case, name: str):
+    """ep_dispatch_with_layout (one kernel for up to 512 routed slots, the
+    layout launches and the scatter above) against the oracle's layout and
+    dispatch, into sentinel-filled buffers."""
+    say(f"[gpu] dispatch_with_layout {name}: T={c.cfg.num_tokens} K={c.cfg.top_k} H={c.cfg.hidden}")
+    cfg = c.cfg
+    lay = sentinel_layout(cfg)
+    ws = epx.workspace_for(cfg, DEV)
+    ids_t = torch.from_numpy(np.ascontiguousarray(c.ids, np.int32).reshape(-1)).to(DEV)
+    recv = bf16_filled(cfg.recv_rows, cfg.hidden, orc.SENTINEL_U16)
+    epx.ep_dispatch_with_layout(cfg, ids_t, ws, lay, u16_tensor(c.x), recv)
+    torch.cuda.synchronize()
+    assert_layout_equal(layout_np(lay), c.L, f"{name} (with layout)")
+    assert_bits_equal(bits_of(recv), orc.dispatch(c.oc, c.L["token_row"], c.x), f"{name}: recv (with layout)")
+
+
 def check_nvfp4(c: Case, lay: epx.Layout, name: str, x=None):
     say(f"[gpu] nvfp4 {name}: H={c.cfg.hidden}")
     cfg = c.cfg

@@ -304,6 +304,27 @@ def test_calls_reject_bad_arguments_before_any_launch(L):
     assert L.ep_dispatch_nvfp4(ctypes.byref(cc), ctypes.byref(lay), fake, fake, fake, fake, None) == -1
 
 
+def test_dispatch_with_layout_rejects_bad_arguments_before_any_launch(L):
+    from combine_ep_dispatch_amd._lib import EpLayout
+
+    c = cfg()
+    st, rows, ws, g = query(L, c)
+    fake = 0x10000  # never dereferenced: every call below fails validation first
+    lay = EpLayout(*([fake] * 8))
+    c.recv_rows = rows - 1
+    cc = c.to_c()
+    assert L.ep_dispatch_with_layout(ctypes.byref(cc), fake, fake, ws, ctypes.byref(lay), fake, fake, None) == -1
+    c.recv_rows = rows
+    cc = c.to_c()
+    assert L.ep_dispatch_with_layout(ctypes.byref(cc), fake, fake, ws - 1, ctypes.byref(lay), fake, fake, None) == -1
+    assert L.ep_dispatch_with_layout(ctypes.byref(cc), fake, None, ws, ctypes.byref(lay), fake, fake, None) == -1
+    assert L.ep_dispatch_with_layout(ctypes.byref(cc), None, fake, ws, ctypes.byref(lay), fake, fake, None) == -1
+    assert L.ep_dispatch_with_layout(ctypes.byref(cc), fake, fake, ws, None, fake, fake, None) == -1
+    assert L.ep_dispatch_with_layout(ctypes.byref(cc), fake, fake, ws, ctypes.byref(lay), fake + 8, fake, None) == -1
+    assert L.ep_dispatch_with_layout(ctypes.byref(cc), fake, fake, ws, ctypes.byref(lay), fake, None, None) == -1
+    assert L.ep_dispatch_with_layout(None, fake, fake, ws, ctypes.byref(lay), fake, fake, None) == -1
+
+
 def test_binding_rejects_cpu_tensors():
     import torch
 

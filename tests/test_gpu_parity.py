@@ -88,6 +88,8 @@ def test_random_shapes(G, seed):
     name = f"random{seed}"
     lay = G.check_layout(c, name)
     G.check_dispatch(c, lay, name)
+    if seed % 2 == 0:
+        G.check_dispatch_with_layout(c, name)
     if c.cfg.hidden % 16 == 0:
         G.check_nvfp4(c, lay, name)
     if c.cfg.hidden % 128 == 0:
@@ -216,6 +218,7 @@ def test_edge_cases(G, edge):
     c = G.random_case(7, **dict(EDGE[edge]))
     lay = G.check_layout(c, edge)
     G.check_dispatch(c, lay, edge)
+    G.check_dispatch_with_layout(c, edge)
     if c.cfg.hidden % 16 == 0:
         G.check_nvfp4(c, lay, edge)
     if c.cfg.hidden % 128 == 0:
@@ -397,6 +400,34 @@ def test_determinism(G):
         G.assert_layout_equal(a, c.L, f"skewed3000 {path}")
 
 
+def test_dispatch_with_layout_matches_separate_calls(G):
+    """ep_dispatch_with_layout gives the bytes of ep_dispatch_layout then
+    ep_dispatch, pad rows zeroed or untouched, on the fused small path
+    (up to 512 routed slots: 1, 300 and 512 slots, shared expert, capacity
+    drops, masked and bad ids) and past it (513 slots)."""
+    cases = [dict(T=1, S=2, E_loc=4, K=1, H=16, A=8),
+             dict(T=100, S=3, E_loc=5, K=3, A=16, H=64, shared=1, src=1, mask_p=0.05, bad_p=0.02),
+             dict(T=64, S=8, E_loc=32, K=8, A=128, H=1040, shared=1, src=5),
+             dict(T=170, S=3, E_loc=5, K=3, A=2, H=48, C=40, shared=1),
+             dict(T=171, S=3, E_loc=5, K=3, A=2, H=48, C=40)]
+    for i, kw in enumerate(cases):
+        c = G.random_case(60 + i, **kw)
+        for flags in (0, G.epx.EP_ZERO_PAD_ROWS):
+            cfg = dataclasses.replace(c.cfg, flags=flags)
+            ids_t = torch.from_numpy(np.ascontiguousarray(c.ids, np.int32).reshape(-1)).to(G.DEV)
+            x = G.u16_tensor(c.x)
+            lay1, lay2 = G.sentinel_layout(cfg), G.sentinel_layout(cfg)
+            r1 = G.bf16_filled(cfg.recv_rows, cfg.hidden, 0x7FA5)
+            r2 = G.bf16_filled(cfg.recv_rows, cfg.hidden, 0x7FA5)
+            G.epx.ep_dispatch_layout(cfg, ids_t, G.epx.workspace_for(cfg, G.DEV), lay1)
+            G.epx.ep_dispatch(cfg, lay1, x, r1)
+            G.epx.ep_dispatch_with_layout(cfg, ids_t, G.epx.workspace_for(cfg, G.DEV), lay2, x, r2)
+            torch.cuda.synchronize()
+            G.assert_layout_equal(G.layout_np(lay2), G.layout_np(lay1), f"case {i} flags {flags}")
+            G.assert_bits_equal(G.bits_of(r2), G.bits_of(r1), f"case {i} flags {flags}: recv")
+            G.assert_layout_equal(G.layout_np(lay2), c.L, f"case {i} flags {flags} (oracle)")
+
+
 def test_zero_pad_rows_flag(G):
     c = G.random_case(21, T=333, S=3, E_loc=5, K=3, A=16, H=64, shared=1, src=1)
     c.cfg.flags = G.epx.EP_ZERO_PAD_ROWS
@@ -421,6 +452,14 @@ def test_zero_pad_rows_flag(G):
     torch.cuda.synchronize()
     r = G.bits_of(recv).reshape(cfg.recv_rows, cfg.hidden)
     assert np.all(r[pad] == 0) and np.all(r[~used] == 0x7FA5)
+    # the layout and dispatch in one call (layout launch then scatter at this size) zero the same pad rows
+    lay2 = G.sentinel_layout(cfg)
+    recv2 = G.bf16_filled(cfg.recv_rows, cfg.hidden, 0x7FA5)
+    ids_t = torch.from_numpy(np.ascontiguousarray(c.ids, np.int32).reshape(-1)).to(G.DEV)
+    G.epx.ep_dispatch_with_layout(cfg, ids_t, G.epx.workspace_for(cfg, G.DEV), lay2, G.u16_tensor(c.x), recv2)
+    torch.cuda.synchronize()
+    assert np.array_equal(G.bits_of(recv2), G.bits_of(recv))
+    G.assert_layout_equal(G.layout_np(lay2), c.L, "zero_pad (with layout)")
     assert np.array_equal(r[tr[tr >= 0]], G.orc.dispatch(c.oc, tr, c.x)[tr[tr >= 0]])
     cd = codes.cpu().numpy().reshape(cfg.recv_rows, -1)
     sc = scales.cpu().numpy().reshape(cfg.recv_rows, -1)
