@@ -526,6 +526,14 @@ def latency_sweep(torch, epx, wl, dev, workload: str, token_counts) -> int:
     of the workload's shape at each token count, plus the whole step (the
     ops of the benchmark step, FP8 dispatch excluded) and the layout and
     dispatch made in one call.  One JSON line per T."""
+    # Untimed device copies first (about 50 ms), so the first token count
+    # is not timed while the clocks are still coming up from idle.
+    a = torch.empty(64 << 20, dtype=torch.float32, device=dev)
+    b = torch.empty_like(a)
+    for _ in range(200):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    del a, b
     for T in token_counts:
         w = wl.CONFIGS[workload].at_tokens(T)
         d = wl.make_workload(w)
