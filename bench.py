@@ -526,15 +526,10 @@ def latency_sweep(torch, epx, wl, dev, workload: str, token_counts) -> int:
     of the workload's shape at each token count, plus the whole step (the
     ops of the benchmark step, FP8 dispatch excluded) and the layout and
     dispatch made in one call.  One JSON line per T."""
-    # Untimed device copies first (about 50 ms), so the first token count
-    # is not timed while the clocks are still coming up from idle.
-    a = torch.empty(64 << 20, dtype=torch.float32, device=dev)
-    b = torch.empty_like(a)
-    for _ in range(200):
-        b.copy_(a)
-    torch.cuda.synchronize()
-    del a, b
-    for T in token_counts:
+    # The first token count runs once more, unreported, before the others:
+    # its figures came out 1-2 us high when it ran first (idle clocks, fresh
+    # allocations), which 50 ms of device copies beforehand did not change.
+    for i, T in enumerate([token_counts[0]] + list(token_counts)):
         w = wl.CONFIGS[workload].at_tokens(T)
         d = wl.make_workload(w)
         cfg = epx.EpConfig(num_tokens=T, hidden=w.H, num_experts=w.E, num_segments=w.S, top_k=w.K,
@@ -597,7 +592,8 @@ def latency_sweep(torch, epx, wl, dev, workload: str, token_counts) -> int:
             torch.cuda.synchronize()
             res[n] = round(statistics.median(a.elapsed_time(b) * 1e3 / 8 for a, b in times), 2)
             del g
-        print(json.dumps({"latency_us": res, "workload": wl.describe(w), "tokens": T}), flush=True)
+        if i > 0:
+            print(json.dumps({"latency_us": res, "workload": wl.describe(w), "tokens": T}), flush=True)
     return 0
 
 

@@ -564,6 +564,74 @@ def test_graph_replays_match_eager(G):
             assert torch.equal(a, b), (i, k)
 
 
+def test_graph_replays_of_decode_step_with_fused_dispatch(G):
+    """A decode-sized step (T=16 at DeepSeek-V3 dims: the layout and the
+    dispatch in one kernel, then combine) captured into a HIP graph: every
+    replay, with its outputs cleared and unrelated eager work in between,
+    gives the eager results, and those equal the oracle's."""
+    c = G.workload_case("dsv3", T=16)
+    cfg = dataclasses.replace(c.cfg, flags=G.epx.EP_ZERO_PAD_ROWS)
+    epx, DEV = G.epx, G.DEV
+    R, T, H = cfg.recv_rows, cfg.num_tokens, cfg.hidden
+    ids = torch.from_numpy(np.ascontiguousarray(c.ids, np.int32).reshape(-1)).to(DEV)
+    x = G.u16_tensor(c.x)
+    probs = torch.from_numpy(c.probs.reshape(-1)).to(DEV)
+    out = G.u16_tensor(c.rows(2))
+    lay = epx.Layout.empty(cfg, DEV)
+    ws = epx.workspace_for(cfg, DEV)
+    recv = torch.empty(R * H, dtype=torch.bfloat16, device=DEV)
+    y = torch.empty(T * H, dtype=torch.bfloat16, device=DEV)
+
+    def step():
+        epx.ep_dispatch_with_layout(cfg, ids, ws, lay, x, recv)
+        epx.ep_combine(cfg, lay, out, probs, y)
+
+    def clear():
+        # the oracle's sentinel bytes: rows past the used ones stay unwritten
+        for t in (recv, y, lay.token_row, lay.expert_ids, lay.src_info, lay.counts, lay.row_offsets, lay.flags):
+            t.view(torch.uint8).fill_(int(G.orc.SENTINEL_U8))
+
+    clear()
+    step()
+    torch.cuda.synchronize()
+    G.assert_layout_equal(G.layout_np(lay), c.L, "decode step (eager)")
+    want_recv = G.orc.dispatch(c.oc, c.L["token_row"], c.x)
+    used = np.zeros(R, bool)
+    for sg in range(cfg.num_segments):
+        used[c.L["seg_base"][sg]: c.L["seg_base"][sg] + c.L["row_offsets"][sg, -1]] = True
+    tr = c.L["token_row"]
+    kept = np.zeros(R, bool)
+    kept[tr[tr >= 0]] = True
+    got = G.bits_of(recv).reshape(R, H)
+    assert (used & ~kept).any()
+    assert np.array_equal(got[kept], want_recv.reshape(R, H)[kept])
+    assert np.all(got[used & ~kept] == 0)  # pad rows zeroed
+    G.assert_bits_equal(G.bits_of(y), G.orc.combine(c.oc, c.L["token_row"], c.rows(2), c.probs), "decode y")
+    ref_recv, ref_y, ref_tr = recv.clone(), y.clone(), lay.token_row.clone()
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    other = G.random_case(5, T=40, H=64)
+    u = torch.from_numpy(np.nonzero(used)[0]).to(DEV).long()
+    for i in range(4):
+        clear()
+        torch.cuda.synchronize()
+        G.check_dispatch_with_layout(other, f"eager between replays {i}")  # unrelated eager work
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(lay.token_row, ref_tr), i
+        assert torch.equal(recv.view(R, H)[u], ref_recv.view(R, H)[u]), i
+        assert torch.equal(y, ref_y), i
+
+
 def test_autograd_dispatcher_matches_fp64_reference(G):
     """EpDispatcher: dispatch -> (x2) -> combine with autograd, against torch
     fp64 autograd of an index_select / index_add formulation on the oracle's
