@@ -151,6 +151,29 @@ int zero_pad(const Shape& d, const ep_layout_t* L, void* base, int64_t row_bytes
     return status_of(launch_zero_pad_rows(base, row_bytes, *L, d.S, d.G, d.A, d.C, d.R, st));
 }
 
+Nvfp4Args nvfp4_args(const Shape& d, const ep_layout_t* L, const uint16_t* x, uint8_t* codes, uint8_t* scales,
+                     uint16_t* rowscale) {
+    Nvfp4Args a;
+    a.x = x;
+    a.codes = codes;
+    a.scales = scales;
+    a.rowscale = rowscale;
+    a.token_row = L->token_row;
+    a.T = d.T;
+    a.Kp = d.Kp;
+    a.H = d.H;
+    a.R = d.R;
+    return a;
+}
+
+int zero_pad_nvfp4(const Shape& d, const ep_layout_t* L, uint8_t* codes, uint8_t* scales, uint16_t* rowscale,
+                   hipStream_t st) {
+    int rc;
+    if ((rc = zero_pad(d, L, codes, d.H / 2, st)) != EP_OK) return rc;
+    if ((rc = zero_pad(d, L, scales, d.H / 16, st)) != EP_OK) return rc;
+    return zero_pad(d, L, rowscale, 2, st);
+}
+
 // Host-side checks shared by both layout entry points (everything but the
 // workspace).
 int layout_check(const Shape& d, const int32_t* topk_ids, const ep_layout_t* L) {
@@ -169,13 +192,18 @@ int layout_check(const Shape& d, const int32_t* topk_ids, const ep_layout_t* L) 
 }
 
 // Launch of the layout kernels, after layout_check and check_device; `ws`
-// holds at least d.ws_bytes bytes.  With x and recv given, the small path
-// also copies the payload rows (*fused is set when it did).
+// holds at least d.ws_bytes bytes.  With x and recv (or codes, scales and
+// rowscale) given, the small path also makes the bf16 (or NVFP4) dispatch
+// (*fused is set when it did).
 int layout_launch(const Shape& d, const int32_t* topk_ids, void* ws, const ep_layout_t* L, void* stream,
-                  const uint16_t* x = nullptr, uint16_t* recv = nullptr, bool* fused = nullptr) {
+                  const uint16_t* x = nullptr, uint16_t* recv = nullptr, uint8_t* codes = nullptr,
+                  uint8_t* scales = nullptr, uint16_t* rowscale = nullptr, bool* fused = nullptr) {
     LayoutArgs a;
     a.x = nullptr;
     a.recv = nullptr;
+    a.codes = nullptr;
+    a.scales = nullptr;
+    a.rowscale = nullptr;
     a.H = d.H;
     a.topk_ids = topk_ids;
     a.desc = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(ws) + kWorkspaceHeader);
@@ -235,6 +263,9 @@ int layout_launch(const Shape& d, const int32_t* topk_ids, void* ws, const ep_la
         a.slots_per_thread = routed <= 256 ? 1 : (routed <= 512 ? 2 : 4);
         a.x = x;
         a.recv = recv;
+        a.codes = codes;
+        a.scales = scales;
+        a.rowscale = rowscale;
     }
     if (fused) *fused = a.x != nullptr;
     return status_of(launch_layout(a, static_cast<hipStream_t>(stream)));
@@ -337,7 +368,9 @@ int ep_dispatch_with_layout(const ep_cfg_t* cfg, const int32_t* topk_ids, void* 
     if ((rc = check_device()) != EP_OK) return rc;
     hipStream_t st = static_cast<hipStream_t>(stream);
     bool fused = false;
-    if ((rc = layout_launch(d, topk_ids, workspace, layout, stream, x, recv, &fused)) != EP_OK) return rc;
+    if ((rc = layout_launch(d, topk_ids, workspace, layout, stream, x, recv, nullptr, nullptr, nullptr, &fused)) !=
+        EP_OK)
+        return rc;
     if (!fused && (rc = status_of(launch_scatter(move_args(d, layout, x, recv, nullptr), st))) != EP_OK) return rc;
     return zero_pad(d, layout, recv, (int64_t)d.H * 2, st);
 }
@@ -355,20 +388,31 @@ int ep_dispatch_nvfp4(const ep_cfg_t* cfg, const ep_layout_t* layout, const uint
         return EP_EINVAL;
     if ((rc = check_device()) != EP_OK) return rc;
     hipStream_t st = static_cast<hipStream_t>(stream);
-    Nvfp4Args a;
-    a.x = x;
-    a.codes = codes;
-    a.scales = scales;
-    a.rowscale = rowscale;
-    a.token_row = layout->token_row;
-    a.T = d.T;
-    a.Kp = d.Kp;
-    a.H = d.H;
-    a.R = d.R;
-    if ((rc = status_of(launch_nvfp4(a, st))) != EP_OK) return rc;
-    if ((rc = zero_pad(d, layout, codes, d.H / 2, st)) != EP_OK) return rc;
-    if ((rc = zero_pad(d, layout, scales, d.H / 16, st)) != EP_OK) return rc;
-    return zero_pad(d, layout, rowscale, 2, st);
+    if ((rc = status_of(launch_nvfp4(nvfp4_args(d, layout, x, codes, scales, rowscale), st))) != EP_OK) return rc;
+    return zero_pad_nvfp4(d, layout, codes, scales, rowscale, st);
+}
+
+int ep_dispatch_nvfp4_with_layout(const ep_cfg_t* cfg, const int32_t* topk_ids, void* workspace,
+                                  int64_t workspace_bytes, const ep_layout_t* layout, const uint16_t* x,
+                                  uint8_t* codes, uint8_t* scales, uint16_t* rowscale, void* stream) {
+    Shape d;
+    int rc = derive(cfg, &d);
+    if (rc != EP_OK) return rc;
+    if ((rc = layout_check(d, topk_ids, layout)) != EP_OK) return rc;
+    if (workspace == nullptr || misaligned(workspace, 16) || workspace_bytes < d.ws_bytes) return EP_EINVAL;
+    if (d.H % 16 != 0 || d.H > nvfp4_max_hidden() || grid_too_big(d, 64)) return EP_EINVAL;
+    if (bad_buffer(x, (int64_t)d.T * d.H * 2, 16) || bad_buffer(codes, d.R * (d.H / 2), 16) ||
+        bad_buffer(scales, d.R * (d.H / 16), 1) || bad_buffer(rowscale, d.R * 2, 2))
+        return EP_EINVAL;
+    if ((rc = check_device()) != EP_OK) return rc;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    bool fused = false;
+    if ((rc = layout_launch(d, topk_ids, workspace, layout, stream, x, nullptr, codes, scales, rowscale, &fused)) !=
+        EP_OK)
+        return rc;
+    if (!fused && (rc = status_of(launch_nvfp4(nvfp4_args(d, layout, x, codes, scales, rowscale), st))) != EP_OK)
+        return rc;
+    return zero_pad_nvfp4(d, layout, codes, scales, rowscale, st);
 }
 
 int ep_dispatch_fp8(const ep_cfg_t* cfg, const ep_layout_t* layout, const uint16_t* x, uint8_t* codes,

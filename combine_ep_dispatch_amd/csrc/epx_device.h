@@ -293,9 +293,13 @@ struct LayoutArgs {
     int32_t lookback;          // single pass: tile prefixes by decoupled look-back (else from all aggregates)
     int32_t rank_blocks;       // workgroups of the rank pass / single pass: max(tiles, min(NG, 256))
     int32_t slots_per_thread;  // 1, 2, 4 or 8 (layout_slots_per_thread)
-    // Small path only: the bf16 dispatch fused in (nullptr: layout only).
+    // Small path only: a dispatch fused in (x nullptr: layout only), the
+    // bf16 one into recv, or the NVFP4 one into codes, scales and rowscale.
     const uint16_t* x;   // [T, H]
-    uint16_t* recv;      // [R, H]
+    uint16_t* recv;      // [R, H] (nullptr: no bf16 dispatch)
+    uint8_t* codes;      // [R, H/2] (nullptr: no NVFP4 dispatch)
+    uint8_t* scales;     // [R, H/16]
+    uint16_t* rowscale;  // [R]
     int32_t H;
 };
 hipError_t launch_layout(const LayoutArgs& a, hipStream_t stream);

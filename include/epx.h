@@ -255,6 +255,21 @@ int ep_dispatch_nvfp4(const ep_cfg_t* cfg, const ep_layout_t* layout, const uint
                       uint8_t* codes, uint8_t* scales, uint16_t* rowscale, void* stream);
 
 /*
+ * Layout and NVFP4 dispatch in one call ([MX] execute: the expert layout,
+ * the per-token global scales and the NVFP4 payload of one batch in a
+ * single call).  Same arguments, outputs and errors as ep_dispatch_layout
+ * followed by ep_dispatch_nvfp4 on the same stream, and the same results
+ * bit for bit.  Up to 512 routed slots (T*K) with no EP_LAYOUT_* path flag,
+ * one kernel computes the layout and quantizes each token once into LDS,
+ * then stores its codes, block scales and rowscale to each of its rows;
+ * larger batches, or a forced path, run the layout launches and then the
+ * NVFP4 dispatch.
+ */
+int ep_dispatch_nvfp4_with_layout(const ep_cfg_t* cfg, const int32_t* topk_ids, void* workspace,
+                                  int64_t workspace_bytes, const ep_layout_t* layout, const uint16_t* x,
+                                  uint8_t* codes, uint8_t* scales, uint16_t* rowscale, void* stream);
+
+/*
  * FP8 dispatch ([FA] init_hybrid_ep_buffer: FP8 communication in the
  * dispatch phase; HybridEPDispatch.forward returns a scaling factor beside
  * the hidden states).  The pages give no format; this library reads it as

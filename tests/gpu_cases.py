@@ -247,6 +247,28 @@ def check_dispatch_with_layout(c: Case, name: str):
     assert_bits_equal(bits_of(recv), orc.dispatch(c.oc, c.L["token_row"], c.x), f"{name}: recv (with layout)")
 
 
+def check_dispatch_nvfp4_with_layout(c: Case, name: str):
+    """ep_dispatch_nvfp4_with_layout (one kernel for up to 512 routed slots,
+    the layout launches and the NVFP4 dispatch above) against the oracle's
+    layout and NVFP4 dispatch, into sentinel-filled buffers."""
+    say(f"[gpu] dispatch_nvfp4_with_layout {name}: T={c.cfg.num_tokens} K={c.cfg.top_k} H={c.cfg.hidden}")
+    cfg = c.cfg
+    R, H = cfg.recv_rows, cfg.hidden
+    lay = sentinel_layout(cfg)
+    ws = epx.workspace_for(cfg, DEV)
+    ids_t = torch.from_numpy(np.ascontiguousarray(c.ids, np.int32).reshape(-1)).to(DEV)
+    codes = torch.full((R * H // 2,), int(orc.SENTINEL_U8), dtype=torch.uint8, device=DEV)
+    scales = torch.full((R * H // 16,), int(orc.SENTINEL_U8), dtype=torch.uint8, device=DEV)
+    rowscale = bf16_filled(R, 1, orc.SENTINEL_U16)
+    epx.ep_dispatch_nvfp4_with_layout(cfg, ids_t, ws, lay, u16_tensor(c.x), codes, scales, rowscale)
+    torch.cuda.synchronize()
+    assert_layout_equal(layout_np(lay), c.L, f"{name} (nvfp4 with layout)")
+    wc, wsc, wr = orc.dispatch_nvfp4(c.oc, c.L["token_row"], c.x)
+    assert_bits_equal(codes.cpu().numpy(), wc, f"{name}: codes (with layout)")
+    assert_bits_equal(scales.cpu().numpy(), wsc, f"{name}: scales (with layout)")
+    assert_bits_equal(bits_of(rowscale), wr, f"{name}: rowscale (with layout)")
+
+
 def check_nvfp4(c: Case, lay: epx.Layout, name: str, x=None):
     say(f"[gpu] nvfp4 {name}: H={c.cfg.hidden}")
     cfg = c.cfg

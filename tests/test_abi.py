@@ -325,6 +325,29 @@ def test_dispatch_with_layout_rejects_bad_arguments_before_any_launch(L):
     assert L.ep_dispatch_with_layout(None, fake, fake, ws, ctypes.byref(lay), fake, fake, None) == -1
 
 
+def test_dispatch_nvfp4_with_layout_rejects_bad_arguments_before_any_launch(L):
+    from combine_ep_dispatch_amd._lib import EpLayout
+
+    c = cfg()
+    st, rows, ws, g = query(L, c)
+    fake = 0x10000  # never dereferenced: every call below fails validation first
+    lay = EpLayout(*([fake] * 8))
+    cc = c.to_c()
+    f = L.ep_dispatch_nvfp4_with_layout
+    assert f(ctypes.byref(cc), fake, fake, ws - 1, ctypes.byref(lay), fake, fake, fake, fake, None) == -1
+    assert f(ctypes.byref(cc), fake, fake, ws, None, fake, fake, fake, fake, None) == -1
+    assert f(ctypes.byref(cc), fake, fake, ws, ctypes.byref(lay), fake + 8, fake, fake, fake, None) == -1  # x
+    assert f(ctypes.byref(cc), fake, fake, ws, ctypes.byref(lay), fake, fake + 8, fake, fake, None) == -1  # codes
+    assert f(ctypes.byref(cc), fake, fake, ws, ctypes.byref(lay), fake, fake, None, fake, None) == -1
+    assert f(ctypes.byref(cc), fake, fake, ws, ctypes.byref(lay), fake, fake, fake, fake + 1, None) == -1
+    for H in (24, 16384 + 16):  # not a whole number of 16-element blocks; past the NVFP4 row limit
+        c2 = cfg()
+        c2.hidden = H
+        c2.recv_rows = rows
+        cc2 = c2.to_c()
+        assert f(ctypes.byref(cc2), fake, fake, ws, ctypes.byref(lay), fake, fake, fake, fake, None) == -1
+
+
 def test_binding_rejects_cpu_tensors():
     import torch
 

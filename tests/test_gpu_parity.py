@@ -90,6 +90,8 @@ def test_random_shapes(G, seed):
     G.check_dispatch(c, lay, name)
     if seed % 2 == 0:
         G.check_dispatch_with_layout(c, name)
+    elif c.cfg.hidden % 16 == 0:
+        G.check_dispatch_nvfp4_with_layout(c, name)
     if c.cfg.hidden % 16 == 0:
         G.check_nvfp4(c, lay, name)
     if c.cfg.hidden % 128 == 0:
@@ -221,6 +223,7 @@ def test_edge_cases(G, edge):
     G.check_dispatch_with_layout(c, edge)
     if c.cfg.hidden % 16 == 0:
         G.check_nvfp4(c, lay, edge)
+        G.check_dispatch_nvfp4_with_layout(c, edge)
     if c.cfg.hidden % 128 == 0:
         G.check_fp8(c, lay, edge)
     G.check_combine(c, lay, edge)
@@ -402,7 +405,9 @@ def test_determinism(G):
 
 def test_dispatch_with_layout_matches_separate_calls(G):
     """ep_dispatch_with_layout gives the bytes of ep_dispatch_layout then
-    ep_dispatch, pad rows zeroed or untouched, on the fused small path
+    ep_dispatch, and ep_dispatch_nvfp4_with_layout those of
+    ep_dispatch_layout then ep_dispatch_nvfp4, pad rows zeroed or untouched,
+    on the fused small path
     (up to 512 routed slots: 1, 300 and 512 slots, shared expert, capacity
     drops, masked and bad ids) and past it (513 slots)."""
     cases = [dict(T=1, S=2, E_loc=4, K=1, H=16, A=8),
@@ -426,6 +431,19 @@ def test_dispatch_with_layout_matches_separate_calls(G):
             G.assert_layout_equal(G.layout_np(lay2), G.layout_np(lay1), f"case {i} flags {flags}")
             G.assert_bits_equal(G.bits_of(r2), G.bits_of(r1), f"case {i} flags {flags}: recv")
             G.assert_layout_equal(G.layout_np(lay2), c.L, f"case {i} flags {flags} (oracle)")
+            # the NVFP4 form against ep_dispatch_nvfp4 on the separate layout
+            R, H = cfg.recv_rows, cfg.hidden
+            q1 = [torch.full((R * H // 2,), 0xA5, dtype=torch.uint8, device=G.DEV),
+                  torch.full((R * H // 16,), 0xA5, dtype=torch.uint8, device=G.DEV), G.bf16_filled(R, 1, 0x7FA5)]
+            q2 = [t.clone() for t in q1]
+            lay3 = G.sentinel_layout(cfg)
+            G.epx.ep_dispatch_nvfp4(cfg, lay1, x, *q1)
+            G.epx.ep_dispatch_nvfp4_with_layout(cfg, ids_t, G.epx.workspace_for(cfg, G.DEV), lay3, x, *q2)
+            torch.cuda.synchronize()
+            G.assert_layout_equal(G.layout_np(lay3), G.layout_np(lay1), f"case {i} flags {flags} (nvfp4)")
+            for n, a_, b_ in zip(("codes", "scales", "rowscale"), q2, q1):
+                G.assert_bits_equal(a_.view(torch.uint8).cpu().numpy(), b_.view(torch.uint8).cpu().numpy(),
+                                    f"case {i} flags {flags}: {n}")
 
 
 def test_zero_pad_rows_flag(G):
