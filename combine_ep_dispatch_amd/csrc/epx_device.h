@@ -301,6 +301,7 @@ struct LayoutArgs {
     uint8_t* scales;     // [R, H/16]
     uint16_t* rowscale;  // [R]
     int32_t H;
+    int32_t fused_rpu;   // rows per unit of the fused dispatch (>= 1)
 };
 hipError_t launch_layout(const LayoutArgs& a, hipStream_t stream);
 

@@ -21,13 +21,13 @@
 // per-slot results and the others spread the groups' metadata runs.  As
 // every workgroup then knows every slot's row, a dispatch can be fused in
 // (ep_dispatch_with_layout, ep_dispatch_nvfp4_with_layout): workgroup b
-// takes items b, b + gridDim.x, ... (a routed slot's or shared-expert
-// token's row), copying the token's bf16 row or quantizing it to NVFP4 and
-// storing that row; when the NVFP4 items outnumber the workgroups, a unit
-// is a whole token, quantized once and stored to all of its rows.  At
-// DeepSeek-V3 dims and T = 16 that is 5.4 us against 4.3 + 3.0 us for the
-// two calls, and 6.6 against 4.3 + 3.9 us for NVFP4 (one process,
-// interleaved).
+// takes units b, b + gridDim.x, ..., a unit being a token and a run of its
+// K' rows (as few rows per unit as let the units fit one round of
+// workgroups); it loads the token's bf16 row, or quantizes it to NVFP4,
+// once and stores it to each of the unit's rows.  At DeepSeek-V3 dims
+// (one process, interleaved) that is 5.4 us against 4.3 + 3.0 us for the
+// two calls at T = 16 and 7.4 against 5.0 + 3.5 us at T = 64; for NVFP4
+// 6.6 against 4.3 + 3.9 us and 7.9 against 5.0 + 4.0 us.
 //
 // Count (default up to 8192 routed slots, forced with EP_LAYOUT_COUNT up to
 // 2^18):
@@ -333,14 +333,16 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout_rank(LayoutArgs a) {
         const int64_t f = wslot0 + it * kWave + lane;
         eid[it] = f < routed ? a.topk_ids[f] : -1;
     }
-    // Small path with a dispatch fused: the work is split in units, one item
-    // (a slot's or shared-expert token's row) per unit, or for the NVFP4
-    // dispatch, when the items outnumber the workgroups, one token (quantized
-    // once, stored to all its rows) per unit.  (Loading each workgroup's
-    // first x row here, ahead of the ranks, measured 0.1-0.3 us slower.)
-    const int32_t fused_items = SMALL && a.x != nullptr ? (int32_t)routed + (a.shared ? a.T : 0) : 0;
-    const bool unit_is_token = a.codes != nullptr && fused_items > (int32_t)gridDim.x;
-    const int32_t fused_units = unit_is_token ? a.T : fused_items;
+    // Small path with a dispatch fused: a unit is one token and a run of up
+    // to `rpu` (LayoutArgs::fused_rpu) of its K' rows; the token is loaded
+    // (and for NVFP4 quantized) once per unit and stored to each of the
+    // unit's rows.
+    // (Loading each workgroup's first x row here, ahead of the ranks,
+    // measured 0.1-0.3 us slower.)
+    const bool fused = SMALL && a.x != nullptr;
+    const int32_t fused_rpu = a.fused_rpu;
+    const int32_t fused_chunks = fused ? (a.Kp + fused_rpu - 1) / fused_rpu : 1;  // units per token
+    const int32_t fused_units = fused ? a.T * fused_chunks : 0;
     const int32_t shared_group = a.shared ? a.src_seg * G : -1;
     if (tid == 0) s_flag = 0;
     int32_t flag = 0;
@@ -798,42 +800,43 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout_rank(LayoutArgs a) {
             s_rowof[f] = row;
         }
         lds_barrier();
-        // Workgroup b takes units b, b + gridDim.x, ...  Item i is routed
-        // slot i (token i / K, row s_rowof[i]) for i below T*K, then
-        // shared-expert token i - T*K.  Rows are workgroup-uniform, so a
-        // dropped or masked item skips the whole workgroup past its barriers.
+        // Workgroup b takes units b, b + gridDim.x, ...: unit u is token
+        // t = u / chunks and its slots k in [c rpu, (c + 1) rpu), c = u - t
+        // chunks.  Slot k < K has row s_rowof[t K + k], the shared-expert slot
+        // rank t of its group; -1 (masked, dropped) is skipped.  Every branch
+        // on t and on a row is workgroup-uniform.
         const int32_t nv = a.H / 8;  // 16-byte vectors per row
         const int32_t nblk = a.H / 16;
-        for (int32_t i = (int32_t)blockIdx.x; i < fused_units; i += (int32_t)gridDim.x) {
-            int32_t row = -1, t = i;
-            if (!unit_is_token) {
-                if (i < (int32_t)routed) {
-                    row = s_rowof[i];
-                    t = i / a.K;
-                } else {
-                    t = i - (int32_t)routed;
-                    row = shared_row_of(s_start, s_lim, shared_group, t, R);
-                }
-                row = uniform(row);
-                if (row < 0) continue;
-            }
+        auto row_of = [&](int32_t t, int32_t k) -> int32_t {
+            return uniform(k < a.K ? s_rowof[t * a.K + k] : shared_row_of(s_start, s_lim, shared_group, t, R));
+        };
+        for (int32_t u = (int32_t)blockIdx.x; u < fused_units; u += (int32_t)gridDim.x) {
+            const int32_t t = u / fused_chunks;
+            const int32_t k0 = (u - t * fused_chunks) * fused_rpu, k1 = min(a.Kp, k0 + fused_rpu);
             if (a.recv != nullptr) {
-                // bf16: the row's bits, every load of the row out before the
-                // first store
+                // bf16: the token's bits, every load of the row out before
+                // the first store
                 if (a.H <= kQuantMaxBlocks * 16) {
                     uint4 q[kQuantBlocksPerThread][2];
                     load_token_blocks(row_rsrc(a.x + (int64_t)t * a.H, a.H * 2), tid, q);
-                    store_token_blocks(row_rsrc(a.recv + (int64_t)row * a.H, a.H * 2), tid, q);
+                    for (int32_t k = k0; k < k1; ++k) {
+                        const int32_t row = row_of(t, k);
+                        if (row >= 0) store_token_blocks(row_rsrc(a.recv + (int64_t)row * a.H, a.H * 2), tid, q);
+                    }
                 } else {
                     const uint4* src = reinterpret_cast<const uint4*>(a.x + (int64_t)t * a.H);
-                    uint4* dst = reinterpret_cast<uint4*>(a.recv + (int64_t)row * a.H);
-                    for (int32_t v = tid; v < nv; v += kLayoutThreads) dst[v] = src[v];
+                    for (int32_t k = k0; k < k1; ++k) {
+                        const int32_t row = row_of(t, k);
+                        if (row < 0) continue;
+                        uint4* dst = reinterpret_cast<uint4*>(a.recv + (int64_t)row * a.H);
+                        for (int32_t v = tid; v < nv; v += kLayoutThreads) dst[v] = src[v];
+                    }
                 }
                 continue;
             }
             // NVFP4: the token is quantized (the row max meets in LDS, codes
             // and block scales are staged in LDS) with the NVFP4 dispatch's
-            // block arithmetic, then stored to this item's row.
+            // block arithmetic, then stored to each of the unit's rows.
             uint4 q[kQuantBlocksPerThread][2];
             load_token_blocks(row_rsrc(a.x + (int64_t)t * a.H, a.H * 2), tid, q);
             uint32_t bmax[kQuantBlocksPerThread];
@@ -864,9 +867,8 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout_rank(LayoutArgs a) {
             }
             lds_barrier();
             const uint16_t rs = rowmax == 0.0f ? (uint16_t)0 : (uint16_t)f32_to_bf16(1.0f / gs);
-            for (int32_t k = 0; k < (unit_is_token ? a.Kp : 1); ++k) {
-                if (unit_is_token)
-                    row = k < a.K ? s_rowof[t * a.K + k] : shared_row_of(s_start, s_lim, shared_group, t, R);
+            for (int32_t k = k0; k < k1; ++k) {
+                const int32_t row = row_of(t, k);
                 if (row < 0) continue;
                 uint2* crow = reinterpret_cast<uint2*>(a.codes + (int64_t)row * (a.H / 2));
                 uint8_t* srow = a.scales + (int64_t)row * nblk;
