@@ -50,7 +50,8 @@ METRIC = "dispatch+combine tokens/s and effective HBM GB/s (% of peak), 1 MI355X
 KERNEL_SOURCES = ("combine_ep_dispatch_amd/csrc/move.hip", "combine_ep_dispatch_amd/csrc/nvfp4.hip",
                   "combine_ep_dispatch_amd/csrc/layout.hip", "combine_ep_dispatch_amd/csrc/fp8.hip",
                   "combine_ep_dispatch_amd/csrc/nvfp4_combine.hip", "combine_ep_dispatch_amd/csrc/api.hip",
-                  "combine_ep_dispatch_amd/csrc/epx_device.h", "combine_ep_dispatch_amd/csrc/nvfp4_device.h")
+                  "combine_ep_dispatch_amd/csrc/epx_device.h", "combine_ep_dispatch_amd/csrc/nvfp4_device.h",
+                  "combine_ep_dispatch_amd/csrc/fp8_device.h")
 
 
 # Each layout path forced (timed beside the default choice; results must agree).
@@ -525,7 +526,7 @@ def latency_sweep(torch, epx, wl, dev, workload: str, token_counts) -> int:
     replays then the median of 10)
     of the workload's shape at each token count, plus the whole step (the
     ops of the benchmark step, FP8 dispatch excluded), the layout with the
-    bf16 or the NVFP4 dispatch made in one call, and the step with the bf16
+    bf16, NVFP4 or FP8 dispatch made in one call, and the step with the bf16
     one in place of its two calls.  One JSON line per T."""
     # The first token count runs once more, unreported, before the others:
     # its figures came out 1-2 us high when it ran first (idle clocks, fresh
@@ -575,6 +576,8 @@ def latency_sweep(torch, epx, wl, dev, workload: str, token_counts) -> int:
         fq = [torch.empty_like(codes), torch.empty_like(scales), torch.empty_like(rowscale)]
         ops += [("dispatch_nvfp4_with_layout",
                  lambda: epx.ep_dispatch_nvfp4_with_layout(cfg, ids, fl_ws, fl_lay, x, *fq))]
+        f8q = [torch.empty_like(f8c), torch.empty_like(f8s)]
+        ops += [("dispatch_fp8_with_layout", lambda: epx.ep_dispatch_fp8_with_layout(cfg, ids, fl_ws, fl_lay, x, *f8q))]
         fused_step = [("dispatch_with_layout", lambda: epx.ep_dispatch_with_layout(cfg, ids, ws, lay, x, recv))]
         fused_step += step_ops[2:]
         ops += [("step", lambda: [fn() for _, fn in step_ops])]

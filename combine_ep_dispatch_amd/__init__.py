@@ -34,7 +34,7 @@ from ._lib import (EP_FLAG_BAD_ID, EP_FLAG_DROPPED, EP_FLAG_INTERNAL, EP_FLAG_MA
 __all__ = [
     "EpConfig", "Layout", "QueryResult", "ep_query", "workspace_for", "ep_dispatch_layout",
     "ep_dispatch_layout_noalloc", "EP_NOALLOC_SCRATCH_BYTES", "ep_combine_nvfp4", "ep_dispatch_with_layout",
-    "ep_dispatch_nvfp4_with_layout",
+    "ep_dispatch_nvfp4_with_layout", "ep_dispatch_fp8_with_layout",
     "ep_dispatch", "ep_dispatch_nvfp4", "ep_dispatch_fp8", "ep_combine", "ep_dispatch_bwd", "ep_combine_bwd",
     "ep_combine_bwd_probs", "ep_indices_to_multihot", "ep_multihot_to_indices", "assert_no_overflow", "EpError", "abi_version", "EP_ZERO_PAD_ROWS", "EP_LAYOUT_LOOKBACK", "EP_LAYOUT_DIRECT", "EP_LAYOUT_BARRIER", "EP_LAYOUT_COUNT", "EP_FLAG_DROPPED",
     "EP_FLAG_BAD_ID", "EP_FLAG_INTERNAL",
@@ -235,6 +235,25 @@ def ep_dispatch_nvfp4_with_layout(cfg: EpConfig, topk_ids: torch.Tensor, workspa
                                                     workspace.numel(), ctypes.byref(L), x.data_ptr(),
                                                     codes.data_ptr(), scales.data_ptr(), rowscale.data_ptr(),
                                                     _stream(stream, dev)), "ep_dispatch_nvfp4_with_layout")
+
+
+def ep_dispatch_fp8_with_layout(cfg: EpConfig, topk_ids: torch.Tensor, workspace: torch.Tensor, layout: Layout,
+                                x: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor, stream=None) -> None:
+    """ep_dispatch_layout then ep_dispatch_fp8 in one call (one kernel for
+    decode-sized batches of up to 512 routed slots)."""
+    dev = x.device
+    T, H, R = cfg.num_tokens, cfg.hidden, cfg.recv_rows
+    _tensor(topk_ids, "topk_ids", torch.int32, T * cfg.top_k, dev)
+    _tensor(workspace, "workspace", torch.uint8, workspace.numel(), dev)
+    _tensor(x, "x", torch.bfloat16, T * H)
+    _tensor(codes, "codes", torch.uint8, R * H, dev)
+    _tensor(scales, "scales", torch.float32, R * (H // 128), dev)
+    layout.check(cfg, dev)
+    c, L = cfg.to_c(), layout.to_c()
+    _check(_lib.lib().ep_dispatch_fp8_with_layout(ctypes.byref(c), topk_ids.data_ptr(), workspace.data_ptr(),
+                                                  workspace.numel(), ctypes.byref(L), x.data_ptr(), codes.data_ptr(),
+                                                  scales.data_ptr(), _stream(stream, dev)),
+           "ep_dispatch_fp8_with_layout")
 
 
 def ep_dispatch_nvfp4(cfg: EpConfig, layout: Layout, x: torch.Tensor, codes: torch.Tensor,

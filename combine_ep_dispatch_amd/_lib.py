@@ -32,8 +32,8 @@ EP_MAX_GROUPS = 2048
 SYMBOLS = ("ep_query", "ep_dispatch_layout", "ep_dispatch", "ep_dispatch_nvfp4", "ep_dispatch_fp8",
            "ep_combine", "ep_dispatch_bwd", "ep_combine_bwd", "ep_combine_bwd_probs",
            "ep_indices_to_multihot", "ep_multihot_to_indices", "ep_dispatch_layout_noalloc",
-           "ep_combine_nvfp4", "ep_dispatch_with_layout", "ep_dispatch_nvfp4_with_layout", "ep_strerror",
-           "ep_abi_version")
+           "ep_combine_nvfp4", "ep_dispatch_with_layout", "ep_dispatch_nvfp4_with_layout",
+           "ep_dispatch_fp8_with_layout", "ep_strerror", "ep_abi_version")
 
 
 class EpCfg(ctypes.Structure):
@@ -84,7 +84,8 @@ def lib():
         L.ep_combine_nvfp4.argtypes = [cfg_p, lay_p, P, P, P, P, P, P]
         L.ep_dispatch_with_layout.argtypes = [cfg_p, P, P, I64, lay_p, P, P, P]
         L.ep_dispatch_nvfp4_with_layout.argtypes = [cfg_p, P, P, I64, lay_p, P, P, P, P, P]
-        for name in SYMBOLS[:15]:
+        L.ep_dispatch_fp8_with_layout.argtypes = [cfg_p, P, P, I64, lay_p, P, P, P, P]
+        for name in SYMBOLS[:16]:
             getattr(L, name).restype = I
         L.ep_strerror.argtypes = [I]
         L.ep_strerror.restype = ctypes.c_char_p

@@ -166,6 +166,25 @@ Nvfp4Args nvfp4_args(const Shape& d, const ep_layout_t* L, const uint16_t* x, ui
     return a;
 }
 
+Fp8Args fp8_args(const Shape& d, const ep_layout_t* L, const uint16_t* x, uint8_t* codes, float* scales) {
+    Fp8Args a;
+    a.x = x;
+    a.codes = codes;
+    a.scales = scales;
+    a.token_row = L->token_row;
+    a.T = d.T;
+    a.Kp = d.Kp;
+    a.H = d.H;
+    a.R = d.R;
+    return a;
+}
+
+int zero_pad_fp8(const Shape& d, const ep_layout_t* L, uint8_t* codes, float* scales, hipStream_t st) {
+    int rc;
+    if ((rc = zero_pad(d, L, codes, d.H, st)) != EP_OK) return rc;
+    return zero_pad(d, L, scales, (int64_t)(d.H / 128) * 4, st);
+}
+
 int zero_pad_nvfp4(const Shape& d, const ep_layout_t* L, uint8_t* codes, uint8_t* scales, uint16_t* rowscale,
                    hipStream_t st) {
     int rc;
@@ -192,18 +211,28 @@ int layout_check(const Shape& d, const int32_t* topk_ids, const ep_layout_t* L) 
 }
 
 // Launch of the layout kernels, after layout_check and check_device; `ws`
-// holds at least d.ws_bytes bytes.  With x and recv (or codes, scales and
-// rowscale) given, the small path also makes the bf16 (or NVFP4) dispatch
+// holds at least d.ws_bytes bytes.  With x and one dispatch's outputs given
+// (out), the small path also makes that bf16, NVFP4 or FP8 dispatch
 // (*fused is set when it did).
+struct FusedOut {  // the dispatch a small-path layout launch makes beside the layout
+    uint16_t* recv = nullptr;
+    uint8_t* codes = nullptr;
+    uint8_t* scales = nullptr;
+    uint16_t* rowscale = nullptr;
+    uint8_t* f8_codes = nullptr;
+    float* f8_scales = nullptr;
+};
+
 int layout_launch(const Shape& d, const int32_t* topk_ids, void* ws, const ep_layout_t* L, void* stream,
-                  const uint16_t* x = nullptr, uint16_t* recv = nullptr, uint8_t* codes = nullptr,
-                  uint8_t* scales = nullptr, uint16_t* rowscale = nullptr, bool* fused = nullptr) {
+                  const uint16_t* x = nullptr, const FusedOut& out = FusedOut(), bool* fused = nullptr) {
     LayoutArgs a;
     a.x = nullptr;
     a.recv = nullptr;
     a.codes = nullptr;
     a.scales = nullptr;
     a.rowscale = nullptr;
+    a.f8_codes = nullptr;
+    a.f8_scales = nullptr;
     a.fused_rpu = 1;
     a.H = d.H;
     a.topk_ids = topk_ids;
@@ -263,10 +292,12 @@ int layout_launch(const Shape& d, const int32_t* topk_ids, void* ws, const ep_la
         a.rank_blocks = std::min<int32_t>(d.NG, 256);
         a.slots_per_thread = routed <= 256 ? 1 : (routed <= 512 ? 2 : 4);
         a.x = x;
-        a.recv = recv;
-        a.codes = codes;
-        a.scales = scales;
-        a.rowscale = rowscale;
+        a.recv = out.recv;
+        a.codes = out.codes;
+        a.scales = out.scales;
+        a.rowscale = out.rowscale;
+        a.f8_codes = out.f8_codes;
+        a.f8_scales = out.f8_scales;
         if (x != nullptr) {
             // A fused dispatch unit is a token and up to rpu of its K' rows:
             // the fewest rows per unit whose units fit one round of
@@ -381,9 +412,9 @@ int ep_dispatch_with_layout(const ep_cfg_t* cfg, const int32_t* topk_ids, void* 
     if ((rc = check_device()) != EP_OK) return rc;
     hipStream_t st = static_cast<hipStream_t>(stream);
     bool fused = false;
-    if ((rc = layout_launch(d, topk_ids, workspace, layout, stream, x, recv, nullptr, nullptr, nullptr, &fused)) !=
-        EP_OK)
-        return rc;
+    FusedOut out;
+    out.recv = recv;
+    if ((rc = layout_launch(d, topk_ids, workspace, layout, stream, x, out, &fused)) != EP_OK) return rc;
     if (!fused && (rc = status_of(launch_scatter(move_args(d, layout, x, recv, nullptr), st))) != EP_OK) return rc;
     return zero_pad(d, layout, recv, (int64_t)d.H * 2, st);
 }
@@ -420,9 +451,11 @@ int ep_dispatch_nvfp4_with_layout(const ep_cfg_t* cfg, const int32_t* topk_ids, 
     if ((rc = check_device()) != EP_OK) return rc;
     hipStream_t st = static_cast<hipStream_t>(stream);
     bool fused = false;
-    if ((rc = layout_launch(d, topk_ids, workspace, layout, stream, x, nullptr, codes, scales, rowscale, &fused)) !=
-        EP_OK)
-        return rc;
+    FusedOut out;
+    out.codes = codes;
+    out.scales = scales;
+    out.rowscale = rowscale;
+    if ((rc = layout_launch(d, topk_ids, workspace, layout, stream, x, out, &fused)) != EP_OK) return rc;
     if (!fused && (rc = status_of(launch_nvfp4(nvfp4_args(d, layout, x, codes, scales, rowscale), st))) != EP_OK)
         return rc;
     return zero_pad_nvfp4(d, layout, codes, scales, rowscale, st);
@@ -441,18 +474,31 @@ int ep_dispatch_fp8(const ep_cfg_t* cfg, const ep_layout_t* layout, const uint16
         return EP_EINVAL;
     if ((rc = check_device()) != EP_OK) return rc;
     hipStream_t st = static_cast<hipStream_t>(stream);
-    Fp8Args a;
-    a.x = x;
-    a.codes = codes;
-    a.scales = scales;
-    a.token_row = layout->token_row;
-    a.T = d.T;
-    a.Kp = d.Kp;
-    a.H = d.H;
-    a.R = d.R;
-    if ((rc = status_of(launch_fp8(a, st))) != EP_OK) return rc;
-    if ((rc = zero_pad(d, layout, codes, d.H, st)) != EP_OK) return rc;
-    return zero_pad(d, layout, scales, (int64_t)(d.H / 128) * 4, st);
+    if ((rc = status_of(launch_fp8(fp8_args(d, layout, x, codes, scales), st))) != EP_OK) return rc;
+    return zero_pad_fp8(d, layout, codes, scales, st);
+}
+
+int ep_dispatch_fp8_with_layout(const ep_cfg_t* cfg, const int32_t* topk_ids, void* workspace,
+                                int64_t workspace_bytes, const ep_layout_t* layout, const uint16_t* x,
+                                uint8_t* codes, float* scales, void* stream) {
+    Shape d;
+    int rc = derive(cfg, &d);
+    if (rc != EP_OK) return rc;
+    if ((rc = layout_check(d, topk_ids, layout)) != EP_OK) return rc;
+    if (workspace == nullptr || misaligned(workspace, 16) || workspace_bytes < d.ws_bytes) return EP_EINVAL;
+    if (d.H % 128 != 0 || d.H > fp8_max_hidden() || grid_too_big(d, 64)) return EP_EINVAL;
+    if (bad_buffer(x, (int64_t)d.T * d.H * 2, 16) || bad_buffer(codes, d.R * d.H, 16) ||
+        bad_buffer(scales, d.R * (d.H / 128) * 4, 4))
+        return EP_EINVAL;
+    if ((rc = check_device()) != EP_OK) return rc;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    bool fused = false;
+    FusedOut out;
+    out.f8_codes = codes;
+    out.f8_scales = scales;
+    if ((rc = layout_launch(d, topk_ids, workspace, layout, stream, x, out, &fused)) != EP_OK) return rc;
+    if (!fused && (rc = status_of(launch_fp8(fp8_args(d, layout, x, codes, scales), st))) != EP_OK) return rc;
+    return zero_pad_fp8(d, layout, codes, scales, st);
 }
 
 int ep_combine(const ep_cfg_t* cfg, const ep_layout_t* layout, const uint16_t* expert_out, const float* probs,

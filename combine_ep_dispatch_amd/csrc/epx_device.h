@@ -294,12 +294,15 @@ struct LayoutArgs {
     int32_t rank_blocks;       // workgroups of the rank pass / single pass: max(tiles, min(NG, 256))
     int32_t slots_per_thread;  // 1, 2, 4 or 8 (layout_slots_per_thread)
     // Small path only: a dispatch fused in (x nullptr: layout only), the
-    // bf16 one into recv, or the NVFP4 one into codes, scales and rowscale.
+    // bf16 one into recv, the NVFP4 one into codes, scales and rowscale, or
+    // the FP8 one into f8_codes and f8_scales.
     const uint16_t* x;   // [T, H]
     uint16_t* recv;      // [R, H] (nullptr: no bf16 dispatch)
     uint8_t* codes;      // [R, H/2] (nullptr: no NVFP4 dispatch)
     uint8_t* scales;     // [R, H/16]
     uint16_t* rowscale;  // [R]
+    uint8_t* f8_codes;   // [R, H] (nullptr: no FP8 dispatch)
+    float* f8_scales;    // [R, H/128]
     int32_t H;
     int32_t fused_rpu;   // rows per unit of the fused dispatch (>= 1)
 };

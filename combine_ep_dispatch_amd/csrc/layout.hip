@@ -20,11 +20,12 @@
 // ranks the one tile to learn the group totals, workgroup 0 writes the
 // per-slot results and the others spread the groups' metadata runs.  As
 // every workgroup then knows every slot's row, a dispatch can be fused in
-// (ep_dispatch_with_layout, ep_dispatch_nvfp4_with_layout): workgroup b
-// takes units b, b + gridDim.x, ..., a unit being a token and a run of its
-// K' rows (as few rows per unit as let the units fit one round of
-// workgroups); it loads the token's bf16 row, or quantizes it to NVFP4,
-// once and stores it to each of the unit's rows.  At DeepSeek-V3 dims
+// (ep_dispatch_with_layout, ep_dispatch_nvfp4_with_layout,
+// ep_dispatch_fp8_with_layout): workgroup b takes units b, b + gridDim.x,
+// ..., a unit being a token and a run of its K' rows (as few rows per unit
+// as let the units fit one round of workgroups); it loads the token's bf16
+// row, or quantizes it to NVFP4 or FP8, once and stores it to each of the
+// unit's rows.  At DeepSeek-V3 dims
 // (one process, interleaved) that is 5.4 us against 4.3 + 3.0 us for the
 // two calls at T = 16 and 7.4 against 5.0 + 3.5 us at T = 64; for NVFP4
 // 6.6 against 4.3 + 3.9 us and 7.9 against 5.0 + 4.0 us.
@@ -84,6 +85,7 @@
 // launch.  The barrier flavour reads every tile's counts in every
 // workgroup, so its cost grows with the square of the tile count (29 ms at
 // 2^24 slots); it is refused past 2^20 routed slots.
+#include "fp8_device.h"
 #include "nvfp4_device.h"
 
 namespace epx {
@@ -101,6 +103,9 @@ constexpr uint64_t kWaitTicks = 1ull << 25;
 // Fused NVFP4 dispatch: 16-element blocks per row (H <= 16384) and per thread.
 constexpr int kQuantMaxBlocks = 1024;
 constexpr int kQuantBlocksPerThread = kQuantMaxBlocks / kLayoutThreads;
+// Fused FP8 dispatch: iterations of 8 128-element blocks per row (H <= 16384)
+// and per wave.
+constexpr int kF8ItersPerWave = 16 / kLayoutWaves;
 
 // Receive row of the fused shared-expert slot of token t: rank t of its
 // group, or -1 past the segment's capacity or the buffer.
@@ -830,6 +835,47 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout_rank(LayoutArgs a) {
                         if (row < 0) continue;
                         uint4* dst = reinterpret_cast<uint4*>(a.recv + (int64_t)row * a.H);
                         for (int32_t v = tid; v < nv; v += kLayoutThreads) dst[v] = src[v];
+                    }
+                }
+                continue;
+            }
+            if (a.f8_codes != nullptr) {
+                // FP8: wave w quantizes iterations w, w + 4, ... of the row
+                // (8 blocks of 128 elements each, in the FP8 dispatch's lane
+                // layout and block arithmetic) and stores its codes and block
+                // scales to each of the unit's rows; the waves share nothing.
+                const int32_t nb8 = a.H / 128, nit = (nb8 + 7) / 8;
+                const __amdgpu_buffer_rsrc_t xs = row_rsrc(a.x + (int64_t)t * a.H, a.H * 2);
+                uint4 p8[kF8ItersPerWave], q8[kF8ItersPerWave];
+#pragma unroll
+                for (int j = 0; j < kF8ItersPerWave; ++j) {
+                    const int32_t it = w + j * kLayoutWaves;  // zeros past the row, like load_iteration
+                    const v4u_t v0 = __builtin_amdgcn_raw_buffer_load_b128(xs, (128 * it + 2 * lane) * 16, 0, 0);
+                    const v4u_t v1 = __builtin_amdgcn_raw_buffer_load_b128(xs, (128 * it + 2 * lane + 1) * 16, 0, 0);
+                    p8[j] = make_uint4(v0.x, v0.y, v0.z, v0.w);
+                    q8[j] = make_uint4(v1.x, v1.y, v1.z, v1.w);
+                }
+                uint4 c8[kF8ItersPerWave];
+                float s8[kF8ItersPerWave];
+#pragma unroll
+                for (int j = 0; j < kF8ItersPerWave; ++j) {
+                    c8[j] = make_uint4(0, 0, 0, 0);
+                    s8[j] = 0.0f;
+                    if (w + j * kLayoutWaves < nit) quantize_loaded(p8[j], q8[j], c8[j], s8[j]);
+                }
+                for (int32_t k = k0; k < k1; ++k) {
+                    const int32_t row = row_of(t, k);
+                    if (row < 0) continue;
+                    const __amdgpu_buffer_rsrc_t cs = row_rsrc(a.f8_codes + (int64_t)row * a.H, a.H);
+                    float* srow = a.f8_scales + (int64_t)row * nb8;
+#pragma unroll
+                    for (int j = 0; j < kF8ItersPerWave; ++j) {
+                        const int32_t it = w + j * kLayoutWaves;
+                        if (it >= nit) break;
+                        __builtin_amdgcn_raw_buffer_store_b128(v4u_t{c8[j].x, c8[j].y, c8[j].z, c8[j].w}, cs,
+                                                               (64 * it + lane) * 16, 0, 0);
+                        const int32_t b = it * 8 + lane / 8;
+                        if ((lane & 7) == 0 && b < nb8) srow[b] = s8[j];
                     }
                 }
                 continue;

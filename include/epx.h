@@ -288,6 +288,20 @@ int ep_dispatch_fp8(const ep_cfg_t* cfg, const ep_layout_t* layout, const uint16
                     uint8_t* codes, float* scales, void* stream);
 
 /*
+ * Layout and FP8 dispatch in one call ([FA] HybridEPDispatch.forward: the
+ * permutation and the FP8 payload with its scaling factor from one call).
+ * Same arguments, outputs and errors as ep_dispatch_layout followed by
+ * ep_dispatch_fp8 on the same stream, and the same results bit for bit.  Up
+ * to 512 routed slots (T*K) with no EP_LAYOUT_* path flag, one kernel
+ * computes the layout and quantizes each token once per run of its rows,
+ * storing codes and block scales to each; larger batches, or a forced path,
+ * run the layout launches and then the FP8 dispatch.
+ */
+int ep_dispatch_fp8_with_layout(const ep_cfg_t* cfg, const int32_t* topk_ids, void* workspace,
+                                int64_t workspace_bytes, const ep_layout_t* layout, const uint16_t* x,
+                                uint8_t* codes, float* scales, void* stream);
+
+/*
  * Combine ([FA] HybridEPCombine.forward; [TD] moe_router_dtype fp32):
  *   y[t, :] = bf16_rne( sum_{k=0..K'-1, token_row[t,k] >= 0}
  *                       w_k * float(expert_out[token_row[t,k], :]) )

@@ -377,6 +377,27 @@ def check_fp8(c: Case, lay: epx.Layout, name: str, x=None):
     assert_bits_equal(scales.view(torch.int32).cpu().numpy(), wsc.view(np.int32), f"{name}: fp8 scales")
 
 
+def check_dispatch_fp8_with_layout(c: Case, name: str):
+    """ep_dispatch_fp8_with_layout (one kernel for up to 512 routed slots, the
+    layout launches and the FP8 dispatch above) against the oracle's layout
+    and FP8 dispatch, into sentinel-filled buffers."""
+    say(f"[gpu] dispatch_fp8_with_layout {name}: T={c.cfg.num_tokens} K={c.cfg.top_k} H={c.cfg.hidden}")
+    cfg = c.cfg
+    R, H = cfg.recv_rows, cfg.hidden
+    lay = sentinel_layout(cfg)
+    ws = epx.workspace_for(cfg, DEV)
+    ids_t = torch.from_numpy(np.ascontiguousarray(c.ids, np.int32).reshape(-1)).to(DEV)
+    codes = torch.full((R * H,), int(orc.SENTINEL_U8), dtype=torch.uint8, device=DEV)
+    scales = torch.full((R * (H // 128),), int(np.int32(orc.SENTINEL_F32_BITS.view(np.int32))),
+                        dtype=torch.int32, device=DEV).view(torch.float32)
+    epx.ep_dispatch_fp8_with_layout(cfg, ids_t, ws, lay, u16_tensor(c.x), codes, scales)
+    torch.cuda.synchronize()
+    assert_layout_equal(layout_np(lay), c.L, f"{name} (fp8 with layout)")
+    wc, wsc = orc.dispatch_fp8(c.oc, c.L["token_row"], c.x)
+    assert_bits_equal(codes.cpu().numpy(), wc, f"{name}: fp8 codes (with layout)")
+    assert_bits_equal(scales.view(torch.int32).cpu().numpy(), wsc.view(np.int32), f"{name}: fp8 scales (with layout)")
+
+
 def nvfp4_rows(c: Case, seed_offset: int):
     """Stand-in NVFP4 expert outputs for every receive row: random codes,
     E4M3 scales (some negative) and bf16 rowscales over 2^-40..2^40.  Rows no

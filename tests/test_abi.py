@@ -348,6 +348,31 @@ def test_dispatch_nvfp4_with_layout_rejects_bad_arguments_before_any_launch(L):
         assert f(ctypes.byref(cc2), fake, fake, ws, ctypes.byref(lay), fake, fake, fake, fake, None) == -1
 
 
+def test_dispatch_fp8_with_layout_rejects_bad_arguments_before_any_launch(L):
+    from combine_ep_dispatch_amd._lib import EpLayout
+
+    fake = 0x10000  # never dereferenced: every call below fails validation first
+    lay = EpLayout(*([fake] * 8))
+    f = L.ep_dispatch_fp8_with_layout
+    c = cfg()
+    c.hidden = 256
+    st, rows, ws, g = query(L, c)
+    c.recv_rows = rows
+    cc = c.to_c()
+    assert f(ctypes.byref(cc), fake, fake, ws - 1, ctypes.byref(lay), fake, fake, fake, None) == -1
+    assert f(ctypes.byref(cc), fake, fake, ws, None, fake, fake, fake, None) == -1
+    assert f(ctypes.byref(cc), fake, fake, ws, ctypes.byref(lay), fake + 8, fake, fake, None) == -1  # x
+    assert f(ctypes.byref(cc), fake, fake, ws, ctypes.byref(lay), fake, fake + 8, fake, None) == -1  # codes
+    assert f(ctypes.byref(cc), fake, fake, ws, ctypes.byref(lay), fake, fake, fake + 2, None) == -1  # scales
+    assert f(ctypes.byref(cc), fake, fake, ws, ctypes.byref(lay), fake, fake, None, None) == -1
+    for H in (192, 16384 + 128):  # not whole 128-element blocks; past the FP8 row limit
+        c2 = cfg()
+        c2.hidden = H
+        c2.recv_rows = rows
+        cc2 = c2.to_c()
+        assert f(ctypes.byref(cc2), fake, fake, ws, ctypes.byref(lay), fake, fake, fake, None) == -1
+
+
 def test_binding_rejects_cpu_tensors():
     import torch
 

@@ -92,6 +92,8 @@ def test_random_shapes(G, seed):
         G.check_dispatch_with_layout(c, name)
     elif c.cfg.hidden % 16 == 0:
         G.check_dispatch_nvfp4_with_layout(c, name)
+    if seed % 3 == 0 and c.cfg.hidden % 128 == 0:
+        G.check_dispatch_fp8_with_layout(c, name)
     if c.cfg.hidden % 16 == 0:
         G.check_nvfp4(c, lay, name)
     if c.cfg.hidden % 128 == 0:
@@ -224,6 +226,8 @@ def test_edge_cases(G, edge):
     if c.cfg.hidden % 16 == 0:
         G.check_nvfp4(c, lay, edge)
         G.check_dispatch_nvfp4_with_layout(c, edge)
+    if c.cfg.hidden % 128 == 0:
+        G.check_dispatch_fp8_with_layout(c, edge)
     if c.cfg.hidden % 128 == 0:
         G.check_fp8(c, lay, edge)
     G.check_combine(c, lay, edge)
@@ -444,6 +448,39 @@ def test_dispatch_with_layout_matches_separate_calls(G):
             for n, a_, b_ in zip(("codes", "scales", "rowscale"), q2, q1):
                 G.assert_bits_equal(a_.view(torch.uint8).cpu().numpy(), b_.view(torch.uint8).cpu().numpy(),
                                     f"case {i} flags {flags}: {n}")
+
+
+def test_dispatch_fp8_with_layout_matches_separate_calls(G):
+    """ep_dispatch_fp8_with_layout gives the bytes of ep_dispatch_layout then
+    ep_dispatch_fp8, pad rows zeroed or untouched: one kernel at 1, 300, 510
+    and 512 routed slots (shared expert, capacity drops, masked and bad ids;
+    rows of 1, 2 and 7 iterations of 8 128-element blocks, the last two
+    ragged) and the layout launches then the FP8 dispatch at 513."""
+    cases = [dict(T=1, S=2, E_loc=4, K=1, H=128, A=8),
+             dict(T=100, S=3, E_loc=5, K=3, A=16, H=7168, shared=1, src=1, mask_p=0.05, bad_p=0.02),
+             dict(T=64, S=8, E_loc=32, K=8, A=128, H=1152, shared=1, src=5),
+             dict(T=170, S=3, E_loc=5, K=3, A=2, H=256, C=40, shared=1),
+             dict(T=171, S=3, E_loc=5, K=3, A=2, H=256, C=40)]
+    for i, kw in enumerate(cases):
+        c = G.random_case(80 + i, **kw)
+        for flags in (0, G.epx.EP_ZERO_PAD_ROWS):
+            cfg = dataclasses.replace(c.cfg, flags=flags)
+            R, H = cfg.recv_rows, cfg.hidden
+            ids_t = torch.from_numpy(np.ascontiguousarray(c.ids, np.int32).reshape(-1)).to(G.DEV)
+            x = G.u16_tensor(c.x)
+            lay1, lay2 = G.sentinel_layout(cfg), G.sentinel_layout(cfg)
+            q1 = [torch.full((R * H,), 0xA5, dtype=torch.uint8, device=G.DEV),
+                  torch.full((R * (H // 128),), 0x7FA5A5A5, dtype=torch.int32, device=G.DEV).view(torch.float32)]
+            q2 = [t.clone() for t in q1]
+            G.epx.ep_dispatch_layout(cfg, ids_t, G.epx.workspace_for(cfg, G.DEV), lay1)
+            G.epx.ep_dispatch_fp8(cfg, lay1, x, *q1)
+            G.epx.ep_dispatch_fp8_with_layout(cfg, ids_t, G.epx.workspace_for(cfg, G.DEV), lay2, x, *q2)
+            torch.cuda.synchronize()
+            G.assert_layout_equal(G.layout_np(lay2), G.layout_np(lay1), f"case {i} flags {flags} (fp8)")
+            G.assert_layout_equal(G.layout_np(lay2), c.L, f"case {i} flags {flags} (fp8, oracle)")
+            for n, a_, b_ in zip(("codes", "scales"), q2, q1):
+                G.assert_bits_equal(a_.view(torch.uint8).cpu().numpy(), b_.view(torch.uint8).cpu().numpy(),
+                                    f"case {i} flags {flags}: fp8 {n}")
 
 
 def test_zero_pad_rows_flag(G):
