@@ -11,8 +11,8 @@ Marshalling only: every step runs in libepx's HIP kernels.
                                              # expert_out and probs
     y.backward(grad)                         # -> x.grad, expert_out.grad, probs.grad
 
-dispatch() builds the layout (the "handle") and keeps it for the combine
-and both backward passes; rows past a segment's used rows are left as the
+dispatch() builds the layout (the "handle") in the same call as the
+dispatch and keeps it for the combine and both backward passes; rows past a segment's used rows are left as the
 buffers held them (zero for the buffers allocated here).  Every routing
 gets a layout of its own, and each forward node keeps the layout it ran
 with, so routing the next batch before this one's backward is safe.  The
@@ -27,16 +27,21 @@ from typing import Optional
 import torch
 
 from . import (EpConfig, Layout, ep_combine, ep_combine_bwd, ep_combine_bwd_probs, ep_dispatch,
-               ep_dispatch_bwd, ep_dispatch_layout, ep_query, workspace_for)
+               ep_dispatch_bwd, ep_dispatch_layout, ep_dispatch_with_layout, ep_query, workspace_for)
 
 __all__ = ["EpDispatcher"]
 
 
 class _Dispatch(torch.autograd.Function):
     @staticmethod
-    def forward(ctx, x, cfg, layout):
+    def forward(ctx, x, cfg, layout, topk_ids=None, workspace=None):
+        # with topk_ids, the layout is built in the same call (one kernel for
+        # decode-sized batches)
         recv = torch.zeros(cfg.recv_rows, cfg.hidden, dtype=torch.bfloat16, device=x.device)
-        ep_dispatch(cfg, layout, x.contiguous().view(-1), recv.view(-1))
+        if topk_ids is None:
+            ep_dispatch(cfg, layout, x.contiguous().view(-1), recv.view(-1))
+        else:
+            ep_dispatch_with_layout(cfg, topk_ids, workspace, layout, x.contiguous().view(-1), recv.view(-1))
         ctx.cfg, ctx.layout = cfg, layout
         return recv
 
@@ -45,7 +50,7 @@ class _Dispatch(torch.autograd.Function):
         cfg = ctx.cfg
         gx = torch.empty(cfg.num_tokens, cfg.hidden, dtype=torch.bfloat16, device=grad_recv.device)
         ep_dispatch_bwd(cfg, ctx.layout, grad_recv.to(torch.bfloat16).contiguous().view(-1), gx.view(-1))
-        return gx, None, None
+        return gx, None, None, None, None
 
 
 class _Combine(torch.autograd.Function):
@@ -95,10 +100,16 @@ class EpDispatcher:
         return layout
 
     def dispatch(self, x: torch.Tensor, topk_ids: Optional[torch.Tensor] = None) -> torch.Tensor:
-        """[T, H] bf16 -> [R, H] bf16 receive rows; routes first when topk_ids is given."""
-        if topk_ids is not None:
-            self.route(topk_ids)
-        return _Dispatch.apply(x, self.cfg, self.layout)
+        """[T, H] bf16 -> [R, H] bf16 receive rows.  With topk_ids, routes in
+        the same call (ep_dispatch_with_layout) into a new layout that later
+        calls use, as route() would."""
+        if topk_ids is None:
+            return _Dispatch.apply(x, self.cfg, self.layout)
+        layout = Layout.empty(self.cfg, self.device)
+        ids = topk_ids.to(torch.int32).contiguous().view(-1)
+        recv = _Dispatch.apply(x, self.cfg, layout, ids, self.workspace)
+        self.layout = layout
+        return recv
 
     def combine(self, expert_out: torch.Tensor, probs: Optional[torch.Tensor]) -> torch.Tensor:
         """[R, H] bf16 expert outputs -> [T, H] bf16, weighted by probs [T, K] (or 1)."""

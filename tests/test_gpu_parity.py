@@ -687,6 +687,41 @@ def test_graph_replays_of_decode_step_with_fused_dispatch(G):
         assert torch.equal(y, ref_y), i
 
 
+def test_autograd_dispatch_with_ids_matches_route_then_dispatch(G):
+    """EpDispatcher.dispatch(x, topk_ids) (layout and dispatch in one call,
+    one kernel at 64 routed slots) gives the receive rows and the input
+    gradient of route(topk_ids) then dispatch(x), bit for bit, and the
+    oracle's receive rows."""
+    from combine_ep_dispatch_amd.autograd import EpDispatcher
+
+    c = G.random_case(45, T=16, S=4, E_loc=8, K=4, H=256, A=8, shared=1, src=1, mask_p=0.1)
+    T, H = c.cfg.num_tokens, c.cfg.hidden
+    ids = torch.from_numpy(c.ids).to(G.DEV)
+    gr = G.u16_tensor(G.wl.make_tensor_like_rows(c.cfg.recv_rows, H, 6)).view(-1, H)
+    out = []
+    for one_call in (True, False):
+        cfg = G.epx.EpConfig(num_tokens=T, hidden=H, num_experts=c.cfg.num_experts, num_segments=c.cfg.num_segments,
+                             top_k=c.cfg.top_k, align=c.cfg.align, shared_expert=1, src_segment=1)
+        d = EpDispatcher(cfg, G.DEV)
+        x = G.u16_tensor(c.x).view(T, H).clone().requires_grad_(True)
+        if one_call:
+            recv = d.dispatch(x, ids)
+        else:
+            d.route(ids)
+            recv = d.dispatch(x)
+        (recv.float() * gr.float()).sum().backward()
+        torch.cuda.synchronize()
+        out.append((G.bits_of(recv.detach()), G.bits_of(x.grad), G.layout_np(d.layout)))
+    assert np.array_equal(out[0][0], out[1][0]) and np.array_equal(out[0][1], out[1][1])
+    for k in ("counts", "row_offsets", "seg_base", "token_row", "flags"):  # written whole (rows past the used
+        assert np.array_equal(out[0][2][k], c.L[k]), k                    # ones stay as Layout.empty left them)
+    tr = c.L["token_row"]
+    kept = np.zeros(c.cfg.recv_rows, bool)
+    kept[tr[tr >= 0]] = True
+    want = G.orc.dispatch(c.oc, tr, c.x).reshape(c.cfg.recv_rows, H)
+    assert np.array_equal(out[0][0].reshape(-1, H)[kept], want[kept])
+
+
 def test_autograd_dispatcher_matches_fp64_reference(G):
     """EpDispatcher: dispatch -> (x2) -> combine with autograd, against torch
     fp64 autograd of an index_select / index_add formulation on the oracle's
