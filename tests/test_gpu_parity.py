@@ -211,6 +211,7 @@ EDGE = {
     "slots_64": dict(T=300, S=1, E_loc=64, K=63, shared=1, src=0, H=64, A=4),  # K' = 64: 16 scatter slot blocks
     "hidden_8": dict(T=500, S=2, E_loc=4, K=3, H=8),                          # one ragged piece per row
     "hidden_16k": dict(T=300, S=2, E_loc=4, K=4, H=16384, A=8),               # 8 full pieces, 16 NVFP4 blocks per lane
+    "fused_wide_row": dict(T=5, S=2, E_loc=4, K=2, H=16392, A=4, shared=1),   # one-call bf16 copy past 16384 elements
     # quantizing dispatch, one workgroup per token: K' = 9 (a wave stores two slot rows), masks, bad ids
     "quant_wg_k9": dict(T=700, S=4, E_loc=8, K=8, shared=1, src=1, H=7168, A=4, mask_p=0.1, bad_p=0.01),
     "quant_wg_capacity": dict(T=900, S=2, E_loc=16, K=6, H=4096, A=2, C=1500),       # capacity drops
